@@ -1,0 +1,104 @@
+"""Pins for the oracle's per-query top-k.
+
+Pinned to: brute-force enumeration of subsets on tiny rows (the unique subset
+whose every member beats every non-member), library sort on distinct scores,
+all-equal rows (the first positions), signed zero handling and causality.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+
+def _canon(v):
+    v = np.array(v, dtype=np.float32, copy=True)
+    v[v == 0] = 0.0
+    return v
+
+
+def brute_force_topk_set(row, n_cand, k):
+    vals = _canon(row[:n_cand])
+
+    def beats(a, b):
+        return vals[a] > vals[b] or (vals[a] == vals[b] and a < b)
+
+    m = min(k, n_cand)
+    found = []
+    for sub in itertools.combinations(range(n_cand), m):
+        inside = set(sub)
+        if all(beats(a, b) for a in inside for b in range(n_cand) if b not in inside):
+            found.append(inside)
+    assert len(found) == 1
+    return found[0]
+
+
+def test_topk_brute_force_tiny_rows():
+    rng = np.random.default_rng(11)
+    for trial in range(60):
+        n = int(rng.integers(1, 9))
+        row = rng.integers(-2, 3, n).astype(np.float32)  # heavy ties
+        if trial % 3 == 0:
+            row = np.where(row == 0, -0.0, row).astype(np.float32)
+        for k in range(1, 10):
+            for n_cand in range(1, n + 1):
+                got = oracle.topk_row(row, n_cand, k)
+                m = min(k, n_cand)
+                assert (got[m:] == -1).all()
+                assert set(got[:m].tolist()) == brute_force_topk_set(row, n_cand, k)
+                # sorted under the total order
+                v = _canon(row)
+                for a, b in zip(got[: m - 1], got[1:m]):
+                    assert v[a] > v[b] or (v[a] == v[b] and a < b)
+
+
+def test_topk_distinct_matches_library_sort():
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(64, 300, generator=g)
+    for k in (1, 7, 64, 299, 300):
+        ref = torch.topk(x, k, dim=-1, sorted=True).indices.numpy()
+        got = np.stack([oracle.topk_row(r, 300, k) for r in x.numpy()])
+        assert np.array_equal(got, ref)
+
+
+def test_all_equal_rows_pick_first_positions():
+    L, k = 20, 7
+    for w_sign in (1.0, -1.0):
+        scores = np.full((1, L, L), 0.0, np.float32) * w_sign
+        idx = oracle.topk(scores, k, 0)
+        for t in range(L):
+            m = min(k, t + 1)
+            assert idx[0, t, :m].tolist() == list(range(m))
+            assert (idx[0, t, m:] == -1).all()
+
+
+def test_signed_zero_counts_as_zero():
+    row = np.array([-0.0, 0.0, -0.0, 0.0], np.float32)
+    assert oracle.topk_row(row, 4, 3).tolist() == [0, 1, 2]
+    row = np.array([0.0, -0.0, 1.0, -1.0], np.float32)
+    assert oracle.topk_row(row, 4, 4).tolist() == [2, 0, 1, 3]
+
+
+def test_topk_reads_only_causal_prefix():
+    rng = np.random.default_rng(2)
+    s = rng.standard_normal((2, 6, 10)).astype(np.float32)
+    a = oracle.topk(s, 4, q_pos0=3)
+    s2 = s.copy()
+    for i in range(6):
+        s2[:, i, 3 + i + 1:] = 1e30  # anything beyond t must be ignored
+    b = oracle.topk(s2, 4, q_pos0=3)
+    assert np.array_equal(a, b)
+    assert (a >= -1).all()
+    for i in range(6):
+        assert (a[:, i] <= 3 + i).all()
+
+
+def test_short_rows_return_all_positions():
+    rng = np.random.default_rng(4)
+    s = rng.standard_normal((1, 5, 5)).astype(np.float32)
+    idx = oracle.topk(s, 16, 0)
+    for t in range(5):
+        assert sorted(idx[0, t, : t + 1].tolist()) == list(range(t + 1))
+        assert (idx[0, t, t + 1:] == -1).all()
