@@ -1,0 +1,179 @@
+"""IndexCache hot path on AMD MI355X: Python binding of libidxc.so.
+
+Each function marshals torch tensors (device memory and the current stream)
+into one call of the C ABI of the same name (include/idxc.h); every step of
+the computation runs in the library's HIP kernels. Nothing here computes.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import IdxcDims, IdxcError, IdxcLayer
+
+__all__ = ["idxc_version", "idxc_validate_pattern", "idxc_schedule", "idxc_indexer_scores",
+           "idxc_topk", "idxc_workspace_bytes", "idxc_indexer_topk", "idxc_sparse_attn",
+           "idxc_layer_stack_forward", "make_dims", "IdxcError"]
+
+
+def _stream(stream=None) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None) -> ctypes.c_void_p:
+    if t is None:
+        return ctypes.c_void_p(0)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def make_dims(B, Lq, Lk, q_pos0=0, H_I=0, d_I=0, H=0, D=0, k=0) -> IdxcDims:
+    return IdxcDims(int(B), int(Lq), int(Lk), int(q_pos0), int(H_I), int(d_I), int(H),
+                    int(D), int(k))
+
+
+def _idx_dims(q_idx, k_idx, q_pos0, k=0) -> IdxcDims:
+    B, Lq, H_I, d_I = q_idx.shape
+    return make_dims(B, Lq, k_idx.shape[1], q_pos0, H_I, d_I, 0, 0, k)
+
+
+def idxc_version() -> str:
+    return _lib.load().idxc_version().decode()
+
+
+def idxc_validate_pattern(pattern: str) -> int:
+    """Returns the number of F layers; raises IdxcError for a bad pattern."""
+    lib = _lib.load()
+    nf = ctypes.c_int32(0)
+    _lib.check(lib.idxc_validate_pattern(pattern.encode(), len(pattern), ctypes.byref(nf)))
+    return nf.value
+
+
+def idxc_schedule(pattern: str) -> List[int]:
+    """source[l] = l for F layers, f(l) for S layers (host only)."""
+    lib = _lib.load()
+    arr = (ctypes.c_int32 * max(1, len(pattern)))()
+    _lib.check(lib.idxc_schedule(pattern.encode(), len(pattern), arr))
+    return list(arr[: len(pattern)])
+
+
+def idxc_indexer_scores(q_idx, k_idx, w, q_pos0: int = 0, out=None, stream=None):
+    lib = _lib.load()
+    d = _idx_dims(q_idx, k_idx, q_pos0)
+    if out is None:
+        out = torch.empty((d.B, d.Lq, d.Lk), dtype=torch.float32, device=q_idx.device)
+    _lib.check(lib.idxc_indexer_scores(_ptr(q_idx, "q_idx", torch.bfloat16),
+                                       _ptr(k_idx, "k_idx", torch.bfloat16),
+                                       _ptr(w, "w", torch.bfloat16), ctypes.byref(d),
+                                       _ptr(out, "scores", torch.float32), _stream(stream)))
+    return out
+
+
+def idxc_topk(scores, k: int, q_pos0: int = 0, out=None, stream=None):
+    lib = _lib.load()
+    B, Lq, Lk = scores.shape
+    d = make_dims(B, Lq, Lk, q_pos0, k=k)
+    if out is None:
+        out = torch.empty((B, Lq, k), dtype=torch.int32, device=scores.device)
+    _lib.check(lib.idxc_topk(_ptr(scores, "scores", torch.float32), ctypes.byref(d),
+                             _ptr(out, "indices", torch.int32), _stream(stream)))
+    return out
+
+
+def idxc_workspace_bytes(B, Lq, Lk, q_pos0, H_I, d_I, k) -> int:
+    lib = _lib.load()
+    d = make_dims(B, Lq, Lk, q_pos0, H_I, d_I, 0, 0, k)
+    n = ctypes.c_size_t(0)
+    _lib.check(lib.idxc_workspace_bytes(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=device)
+
+
+def idxc_indexer_topk(q_idx, k_idx, w, k: int, q_pos0: int = 0, workspace=None, out=None,
+                      stream=None):
+    lib = _lib.load()
+    d = _idx_dims(q_idx, k_idx, q_pos0, k)
+    if workspace is None:
+        workspace = _workspace(idxc_workspace_bytes(d.B, d.Lq, d.Lk, q_pos0, d.H_I, d.d_I, k),
+                               q_idx.device)
+    if out is None:
+        out = torch.empty((d.B, d.Lq, k), dtype=torch.int32, device=q_idx.device)
+    _lib.check(lib.idxc_indexer_topk(_ptr(q_idx, "q_idx", torch.bfloat16),
+                                     _ptr(k_idx, "k_idx", torch.bfloat16),
+                                     _ptr(w, "w", torch.bfloat16), ctypes.byref(d),
+                                     _ptr(workspace, "workspace"),
+                                     workspace.numel() * workspace.element_size(),
+                                     _ptr(out, "indices", torch.int32), _stream(stream)))
+    return out
+
+
+def idxc_sparse_attn(q, k, v, indices, scale: float, out=None, stream=None):
+    lib = _lib.load()
+    B, Lq, H, D = q.shape
+    d = make_dims(B, Lq, k.shape[1], 0, 0, 0, H, D, indices.shape[-1])
+    if out is None:
+        out = torch.empty_like(q)
+    _lib.check(lib.idxc_sparse_attn(_ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
+                                    _ptr(v, "v", torch.bfloat16),
+                                    _ptr(indices, "indices", torch.int32), ctypes.byref(d),
+                                    float(scale), _ptr(out, "out", torch.bfloat16),
+                                    _stream(stream)))
+    return out
+
+
+def idxc_layer_stack_forward(pattern: str, layers: Sequence[Dict[str, torch.Tensor]], k: int,
+                             scale: float, q_pos0: int = 0, index_cache=None, workspace=None,
+                             debug_indices: bool = False, stream=None):
+    """Run the stack. layers[l] holds q_idx, k_idx, w (F layers), q, k, v and
+    optionally out. Returns dict(out=[...], indexer_calls=int,
+    index_cache=tensor, debug_indices=tensor or None)."""
+    lib = _lib.load()
+    n = len(layers)
+    ref = next(L for L in layers if L.get("q") is not None)
+    B, Lq, H, D = ref["q"].shape
+    Lk = ref["k"].shape[1]
+    f0 = next((L for L in layers if L.get("q_idx") is not None), None)
+    H_I, d_I = (f0["q_idx"].shape[2], f0["q_idx"].shape[3]) if f0 is not None else (0, 0)
+    d = make_dims(B, Lq, Lk, q_pos0, H_I, d_I, H, D, k)
+    dev = ref["q"].device
+    if index_cache is None:
+        index_cache = torch.empty((B, Lq, k), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = _workspace(idxc_workspace_bytes(B, Lq, Lk, q_pos0, H_I, d_I, k), dev)
+    dbg = torch.empty((n, B, Lq, k), dtype=torch.int32, device=dev) if debug_indices else None
+    arr = (IdxcLayer * n)()
+    outs = []
+    for l, L in enumerate(layers):
+        o = L.get("out")
+        if o is None:
+            o = torch.empty_like(L["q"])
+        outs.append(o)
+        arr[l] = IdxcLayer(_ptr(L.get("q_idx"), "q_idx", torch.bfloat16).value,
+                           _ptr(L.get("k_idx"), "k_idx", torch.bfloat16).value,
+                           _ptr(L.get("w"), "w", torch.bfloat16).value,
+                           _ptr(L["q"], "q", torch.bfloat16).value,
+                           _ptr(L["k"], "k", torch.bfloat16).value,
+                           _ptr(L["v"], "v", torch.bfloat16).value,
+                           _ptr(o, "out", torch.bfloat16).value)
+    calls = ctypes.c_int32(-1)
+    _lib.check(lib.idxc_layer_stack_forward(pattern.encode(), n, arr, ctypes.byref(d),
+                                            float(scale), _ptr(index_cache, "index_cache"),
+                                            _ptr(workspace, "workspace"),
+                                            workspace.numel() * workspace.element_size(),
+                                            ctypes.byref(calls), _ptr(dbg, "debug_indices"),
+                                            _stream(stream)))
+    return dict(out=outs, indexer_calls=calls.value, index_cache=index_cache,
+                debug_indices=dbg)

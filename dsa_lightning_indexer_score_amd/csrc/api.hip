@@ -1,0 +1,392 @@
+// C ABI of libidxc: argument checks, workspace sizing and the F/S layer loop.
+//
+// Every check runs on the host before any launch: a call that returns an
+// error has launched nothing and has not touched device memory or initialised
+// a HIP device.
+//
+// The F/S scheduler follows the state machine of "IndexCache：跨层复用稀疏注意力
+// 的索引" (wineandchord.com), section "从 DSA 的成本分解开始" (an F layer
+// recomputes the top-k and overwrites the single cached index tensor, an S
+// layer reuses it, the first layer must be F, roles outside {F, S} are errors)
+// and the loop of the "NLP——IndexCache" notes, section "IndexCache 方法"
+// (compute and cache on F, read the cache on S; f(l) = max{j < l : c_j = F}).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/idxc.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace idxc;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return IDXC_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(IDXC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE_PTR(p, name)                                                          \
+  do {                                                                                \
+    if ((p) == nullptr) return fail(IDXC_ERR_INVALID_ARG, "%s is NULL", name);         \
+    if (!aligned16(p)) return fail(IDXC_ERR_INVALID_ARG, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+constexpr int kMaxRows = 1 << 24;
+constexpr int kMaxLk = 1 << 24;
+
+// Common size checks. need: bit 0 = indexer fields, bit 1 = attention fields,
+// bit 2 = k.
+int check_dims(const idxc_dims* d, int need) {
+  if (d == nullptr) return fail(IDXC_ERR_INVALID_ARG, "dims is NULL");
+  if (d->B < 1 || d->Lq < 1 || d->Lk < 1)
+    return fail(IDXC_ERR_INVALID_ARG, "B, Lq and Lk must be >= 1 (got %d, %d, %d)", d->B, d->Lq,
+                d->Lk);
+  if (d->q_pos0 < 0) return fail(IDXC_ERR_INVALID_ARG, "q_pos0 must be >= 0");
+  if ((long long)d->q_pos0 + d->Lq > d->Lk)
+    return fail(IDXC_ERR_INVALID_ARG, "q_pos0 + Lq (%lld) exceeds Lk (%d)",
+                (long long)d->q_pos0 + d->Lq, d->Lk);
+  if ((long long)d->B * d->Lq > kMaxRows || d->Lk > kMaxLk)
+    return fail(IDXC_ERR_UNSUPPORTED, "B*Lq or Lk too large");
+  if (need & 1) {
+    if (d->H_I < 1 || d->d_I < 1) return fail(IDXC_ERR_INVALID_ARG, "H_I and d_I must be >= 1");
+    if (d->H_I > 64) return fail(IDXC_ERR_UNSUPPORTED, "H_I = %d > 64", d->H_I);
+    if (d->d_I != 32 && d->d_I != 64 && d->d_I != 128)
+      return fail(IDXC_ERR_UNSUPPORTED, "d_I = %d not in {32, 64, 128}", d->d_I);
+  }
+  if (need & 2) {
+    if (d->H < 1 || d->D < 1) return fail(IDXC_ERR_INVALID_ARG, "H and D must be >= 1");
+    if (d->H > 64) return fail(IDXC_ERR_UNSUPPORTED, "H = %d > 64", d->H);
+    if (d->D != 64 && d->D != 128) return fail(IDXC_ERR_UNSUPPORTED, "D = %d not in {64, 128}", d->D);
+  }
+  if (need & 4) {
+    if (d->k < 1) return fail(IDXC_ERR_INVALID_ARG, "k must be >= 1");
+    if (d->k > kMaxK) return fail(IDXC_ERR_UNSUPPORTED, "k = %d > %d", d->k, kMaxK);
+  }
+  return IDXC_OK;
+}
+
+int check_pattern(const char* pattern, int32_t n_layers, int32_t* n_full) {
+  if (pattern == nullptr) return fail(IDXC_ERR_INVALID_ARG, "pattern is NULL");
+  if (n_layers < 1) return fail(IDXC_ERR_INVALID_ARG, "n_layers must be >= 1");
+  const size_t len = strnlen(pattern, (size_t)n_layers + 1);
+  if (len != (size_t)n_layers)
+    return fail(IDXC_ERR_PATTERN, "pattern length %zu != n_layers %d", len, n_layers);
+  int nf = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    const char c = pattern[l];
+    if (c == 'F') ++nf;
+    else if (c != 'S') return fail(IDXC_ERR_PATTERN, "role '%c' at layer %d is not F or S", c, l);
+  }
+  if (pattern[0] != 'F') return fail(IDXC_ERR_PATTERN, "the first layer must be F");
+  if (n_full) *n_full = nf;
+  return IDXC_OK;
+}
+
+// ---- workspace plan -------------------------------------------------------
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Smallest candidate capacity: after a compaction a row holds k entries and
+// must still take one more 64-key tile.
+int min_cap(int k) { return (k + 64 + 63) / 64 * 64; }
+
+int default_cap(int k) {
+  int cap = 2 * k;
+  if (cap < k + 64) cap = k + 64;
+  if (cap < 4096) cap = 4096;
+  return (cap + 63) / 64 * 64;
+}
+
+struct Plan {
+  bool split;      // materialised scores + top-k (few rows)
+  size_t bytes;    // workspace needed at full speed
+  size_t min_bytes;
+};
+
+Plan plan_for(const idxc_dims* d) {
+  Plan p;
+  const size_t rows = (size_t)d->B * d->Lq;
+  p.split = indexer_prefers_split(d->B, d->Lq, d->Lk);
+  if (p.split) {
+    p.bytes = align_up(rows * (size_t)d->Lk * 4);
+    p.min_bytes = p.bytes;
+  } else {
+    p.bytes = align_up(rows * 4) + rows * (size_t)default_cap(d->k) * 8;
+    p.min_bytes = align_up(rows * 4) + rows * (size_t)min_cap(d->k) * 8;
+  }
+  return p;
+}
+
+// Largest candidate capacity (multiple of 64, <= default) that fits.
+int cap_for(const idxc_dims* d, size_t ws_bytes) {
+  const size_t rows = (size_t)d->B * d->Lq;
+  const size_t head = align_up(rows * 4);
+  if (ws_bytes < head) return 0;
+  size_t cap = (ws_bytes - head) / (rows * 8);
+  cap = cap / 64 * 64;
+  const size_t dc = (size_t)default_cap(d->k);
+  if (cap > dc) cap = dc;
+  return (int)cap;
+}
+
+// Indexer + top-k for one layer into `indices`, using the workspace.
+hipError_t run_indexer_topk(const void* q_idx, const void* k_idx, const void* w,
+                            const idxc_dims* d, void* ws, size_t ws_bytes, int32_t* indices,
+                            hipStream_t st) {
+  IndexerArgs ia{};
+  ia.q_idx = static_cast<const uint16_t*>(q_idx);
+  ia.k_idx = static_cast<const uint16_t*>(k_idx);
+  ia.w = static_cast<const uint16_t*>(w);
+  ia.B = d->B;
+  ia.Lq = d->Lq;
+  ia.Lk = d->Lk;
+  ia.q_pos0 = d->q_pos0;
+  ia.H_I = d->H_I;
+  ia.d_I = d->d_I;
+  ia.k = d->k;
+  const int rows = d->B * d->Lq;
+  TopkArgs ta{};
+  ta.Lq = d->Lq;
+  ta.Lk = d->Lk;
+  ta.q_pos0 = d->q_pos0;
+  ta.rows = rows;
+  ta.k = d->k;
+  ta.out = indices;
+  if (plan_for(d).split) {
+    ia.scores = static_cast<float*>(ws);
+    hipError_t e = launch_indexer_scores(ia, st);
+    if (e != hipSuccess) return e;
+    ta.scores = ia.scores;
+    return launch_topk(ta, st);
+  }
+  const int cap = cap_for(d, ws_bytes);
+  ia.cand_count = static_cast<int*>(ws);
+  ia.cand = reinterpret_cast<decltype(ia.cand)>(static_cast<uint8_t*>(ws) + align_up((size_t)rows * 4));
+  ia.cap = cap;
+  hipError_t e = launch_indexer_candidates(ia, st);
+  if (e != hipSuccess) return e;
+  ta.cand = ia.cand;
+  ta.cand_count = ia.cand_count;
+  ta.cap = cap;
+  return launch_topk(ta, st);
+}
+
+AttnArgs attn_args(const void* q, const void* k, const void* v, const int32_t* indices,
+                   const idxc_dims* d, float scale, void* out) {
+  AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.key = static_cast<const uint16_t*>(k);
+  a.val = static_cast<const uint16_t*>(v);
+  a.indices = indices;
+  a.B = d->B;
+  a.Lq = d->Lq;
+  a.Lk = d->Lk;
+  a.H = d->H;
+  a.D = d->D;
+  a.topk = d->k;
+  a.scale = scale;
+  a.out = static_cast<uint16_t*>(out);
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* idxc_last_error(void) { return g_err; }
+
+const char* idxc_version(void) { return "idxc 0.1.0 gfx950"; }
+
+int idxc_validate_pattern(const char* pattern, int32_t n_layers, int32_t* n_full) {
+  const int r = check_pattern(pattern, n_layers, n_full);
+  return r == IDXC_OK ? ok() : r;
+}
+
+int idxc_schedule(const char* pattern, int32_t n_layers, int32_t* source) {
+  const int r = check_pattern(pattern, n_layers, nullptr);
+  if (r != IDXC_OK) return r;
+  if (source == nullptr) return fail(IDXC_ERR_INVALID_ARG, "source is NULL");
+  int last_f = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    if (pattern[l] == 'F') last_f = l;
+    source[l] = last_f;
+  }
+  return ok();
+}
+
+int idxc_workspace_bytes(const idxc_dims* dims, size_t* bytes) {
+  int r = check_dims(dims, 1 | 4);
+  if (r != IDXC_OK) return r;
+  if (bytes == nullptr) return fail(IDXC_ERR_INVALID_ARG, "bytes is NULL");
+  const Plan p = plan_for(dims);
+  // the stack also needs nothing else: attention runs without workspace
+  *bytes = p.bytes;
+  return ok();
+}
+
+int idxc_indexer_scores(const void* q_idx, const void* k_idx, const void* w,
+                        const idxc_dims* dims, float* scores, void* hip_stream) {
+  int r = check_dims(dims, 1);
+  if (r != IDXC_OK) return r;
+  REQUIRE_PTR(q_idx, "q_idx");
+  REQUIRE_PTR(k_idx, "k_idx");
+  REQUIRE_PTR(w, "w");
+  REQUIRE_PTR(scores, "scores");
+  IndexerArgs ia{};
+  ia.q_idx = static_cast<const uint16_t*>(q_idx);
+  ia.k_idx = static_cast<const uint16_t*>(k_idx);
+  ia.w = static_cast<const uint16_t*>(w);
+  ia.B = dims->B;
+  ia.Lq = dims->Lq;
+  ia.Lk = dims->Lk;
+  ia.q_pos0 = dims->q_pos0;
+  ia.H_I = dims->H_I;
+  ia.d_I = dims->d_I;
+  ia.k = dims->k;
+  ia.scores = scores;
+  return hip_status(launch_indexer_scores(ia, static_cast<hipStream_t>(hip_stream)),
+                    "indexer_scores launch");
+}
+
+int idxc_topk(const float* scores, const idxc_dims* dims, int32_t* indices, void* hip_stream) {
+  int r = check_dims(dims, 4);
+  if (r != IDXC_OK) return r;
+  REQUIRE_PTR(scores, "scores");
+  REQUIRE_PTR(indices, "indices");
+  TopkArgs ta{};
+  ta.scores = scores;
+  ta.Lq = dims->Lq;
+  ta.Lk = dims->Lk;
+  ta.q_pos0 = dims->q_pos0;
+  ta.rows = dims->B * dims->Lq;
+  ta.k = dims->k;
+  ta.out = indices;
+  return hip_status(launch_topk(ta, static_cast<hipStream_t>(hip_stream)), "topk launch");
+}
+
+int idxc_indexer_topk(const void* q_idx, const void* k_idx, const void* w,
+                      const idxc_dims* dims, void* workspace, size_t workspace_bytes,
+                      int32_t* indices, void* hip_stream) {
+  int r = check_dims(dims, 1 | 4);
+  if (r != IDXC_OK) return r;
+  REQUIRE_PTR(q_idx, "q_idx");
+  REQUIRE_PTR(k_idx, "k_idx");
+  REQUIRE_PTR(w, "w");
+  REQUIRE_PTR(workspace, "workspace");
+  REQUIRE_PTR(indices, "indices");
+  const Plan p = plan_for(dims);
+  if (workspace_bytes < p.min_bytes)
+    return fail(IDXC_ERR_INVALID_ARG, "workspace of %zu bytes is below the minimum %zu",
+                workspace_bytes, p.min_bytes);
+  return hip_status(run_indexer_topk(q_idx, k_idx, w, dims, workspace, workspace_bytes, indices,
+                                     static_cast<hipStream_t>(hip_stream)),
+                    "indexer_topk launch");
+}
+
+int idxc_sparse_attn(const void* q, const void* k, const void* v, const int32_t* indices,
+                     const idxc_dims* dims, float scale, void* out, void* hip_stream) {
+  int r = check_dims(dims, 2 | 4);
+  if (r != IDXC_OK) return r;
+  REQUIRE_PTR(q, "q");
+  REQUIRE_PTR(k, "k");
+  REQUIRE_PTR(v, "v");
+  REQUIRE_PTR(indices, "indices");
+  REQUIRE_PTR(out, "out");
+  if (!(scale == scale)) return fail(IDXC_ERR_INVALID_ARG, "scale is NaN");
+  return hip_status(launch_sparse_attn(attn_args(q, k, v, indices, dims, scale, out),
+                                       static_cast<hipStream_t>(hip_stream)),
+                    "sparse_attn launch");
+}
+
+int idxc_layer_stack_forward(const char* pattern, int32_t n_layers, const idxc_layer* layers,
+                             const idxc_dims* dims, float scale, int32_t* index_cache,
+                             void* workspace, size_t workspace_bytes, int32_t* indexer_calls,
+                             int32_t* debug_indices, void* hip_stream) {
+  int r = check_pattern(pattern, n_layers, nullptr);
+  if (r != IDXC_OK) return r;
+  r = check_dims(dims, 1 | 2 | 4);
+  if (r != IDXC_OK) return r;
+  if (layers == nullptr) return fail(IDXC_ERR_INVALID_ARG, "layers is NULL");
+  if (indexer_calls == nullptr) return fail(IDXC_ERR_INVALID_ARG, "indexer_calls is NULL");
+  REQUIRE_PTR(index_cache, "index_cache");
+  REQUIRE_PTR(workspace, "workspace");
+  if (debug_indices != nullptr && !aligned16(debug_indices))
+    return fail(IDXC_ERR_INVALID_ARG, "debug_indices is not 16-byte aligned");
+  if (!(scale == scale)) return fail(IDXC_ERR_INVALID_ARG, "scale is NaN");
+  const Plan p = plan_for(dims);
+  if (workspace_bytes < p.min_bytes)
+    return fail(IDXC_ERR_INVALID_ARG, "workspace of %zu bytes is below the minimum %zu",
+                workspace_bytes, p.min_bytes);
+  for (int l = 0; l < n_layers; ++l) {
+    const idxc_layer& L = layers[l];
+    char name[64];
+    if (pattern[l] == 'F') {
+      snprintf(name, sizeof(name), "layers[%d].q_idx", l);
+      REQUIRE_PTR(L.q_idx, name);
+      snprintf(name, sizeof(name), "layers[%d].k_idx", l);
+      REQUIRE_PTR(L.k_idx, name);
+      snprintf(name, sizeof(name), "layers[%d].w", l);
+      REQUIRE_PTR(L.w, name);
+    }
+    snprintf(name, sizeof(name), "layers[%d].q", l);
+    REQUIRE_PTR(L.q, name);
+    snprintf(name, sizeof(name), "layers[%d].k", l);
+    REQUIRE_PTR(L.k, name);
+    snprintf(name, sizeof(name), "layers[%d].v", l);
+    REQUIRE_PTR(L.v, name);
+    snprintf(name, sizeof(name), "layers[%d].out", l);
+    REQUIRE_PTR(L.out, name);
+  }
+
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const size_t cache_elems = (size_t)dims->B * dims->Lq * dims->k;
+  int calls = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    const idxc_layer& L = layers[l];
+    if (pattern[l] == 'F') {
+      hipError_t e = run_indexer_topk(L.q_idx, L.k_idx, L.w, dims, workspace, workspace_bytes,
+                                      index_cache, st);
+      if (e != hipSuccess) {
+        *indexer_calls = calls;
+        return hip_status(e, "stack indexer launch");
+      }
+      ++calls;
+    }
+    hipError_t e = launch_sparse_attn(attn_args(L.q, L.k, L.v, index_cache, dims, scale, L.out), st);
+    if (e != hipSuccess) {
+      *indexer_calls = calls;
+      return hip_status(e, "stack attention launch");
+    }
+    if (debug_indices != nullptr) {
+      e = hipMemcpyAsync(debug_indices + (size_t)l * cache_elems, index_cache,
+                         cache_elems * sizeof(int32_t), hipMemcpyDeviceToDevice, st);
+      if (e != hipSuccess) {
+        *indexer_calls = calls;
+        return hip_status(e, "debug index copy");
+      }
+    }
+  }
+  *indexer_calls = calls;
+  return ok();
+}
+
+}  // extern "C"

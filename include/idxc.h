@@ -1,0 +1,172 @@
+/*
+ * idxc.h — C ABI of libidxc.so: the IndexCache hot path on AMD MI355X (gfx950).
+ *
+ * What the library computes (sources are web pages, cited by title + section):
+ *
+ *  [W] "IndexCache：跨层复用稀疏注意力的索引" (wineandchord.com), section
+ *      "从 DSA 的成本分解开始" (starting from DSA's cost decomposition): each
+ *      layer has a role c_l in {F, S}; an F layer runs its own indexer and
+ *      produces I_l = TopK(s_l, k), overwriting the cache; an S layer runs no
+ *      indexer and uses the latest F layer's index tensor; the first layer
+ *      must be F. Its executable state machine raises an error for a wrong
+ *      length, a first role other than F, or a role outside {F, S}.
+ *  [J] "NLP——IndexCache" notes (joezjh.github.io), section "IndexCache 方法":
+ *      T_t^(l) <- T_t^(f(l)), f(l) = max{j < l : c_j = F}; in the layer loop,
+ *      F computes and caches the indices, S reads the cache. Section
+ *      "背景 & 问题提出": a lightning indexer picks, for every query, the top-k
+ *      (k = 2048) of all previous tokens; core attention then runs on those k.
+ *
+ *  Where the pages name an operation but do not define it, this library uses:
+ *   - indexer score  s[t, s'] = sum_h w[t,h] * max(0, q_I[t,h,:] . k_I[s',:]),
+ *     one indexer key per token shared by all indexer heads, candidates
+ *     s' in [0, t] (the query's own position included);
+ *   - top-k order: higher score first, then lower position, -0.0 == +0.0;
+ *     output sorted in that order, min(k, t+1) entries, then -1 padding;
+ *   - core attention O[t,h] = sum_{s in I_t} softmax(scale * Q[t,h].K[s]) V[s]
+ *     over the valid (non -1) entries, one shared K/V head (MQA).
+ *
+ * Conventions shared by every entry point
+ *  - All tensors are row-major and contiguous, in DEVICE memory owned by the
+ *    caller. The library never allocates, frees or keeps a tensor, and keeps
+ *    no state between calls. Every device pointer must be 16-byte aligned.
+ *  - Layouts (bf16 = IEEE bfloat16 stored as uint16):
+ *      q_idx   [B, Lq, H_I, d_I] bf16     k_idx [B, Lk, d_I] bf16
+ *      w       [B, Lq, H_I]      bf16
+ *      q       [B, Lq, H, D]     bf16     k, v  [B, Lk, D]   bf16
+ *      out     [B, Lq, H, D]     bf16
+ *      scores  [B, Lq, Lk]       fp32     indices [B, Lq, k] int32
+ *    Query row i of batch b sits at absolute position t = q_pos0 + i and may
+ *    attend to keys 0..t of the same batch; q_pos0 + Lq <= Lk is required
+ *    (prefill: q_pos0 = 0, Lq = Lk; decode: Lq = 1, q_pos0 = Lk - 1; a query
+ *    chunk c of size C: q_pos0 = c*C, Lk = (c+1)*C).
+ *  - Supported sizes: d_I in {32, 64, 128}; 1 <= H_I <= 64; D in {64, 128};
+ *    1 <= H <= 64; 1 <= k <= 2048; Lk <= 2^24; B*Lq <= 2^24. Anything else
+ *    returns IDXC_ERR_UNSUPPORTED.
+ *  - Calls are asynchronous on the given HIP stream (NULL = the default
+ *    stream). The returned status covers argument checks and launch errors;
+ *    a fault inside a kernel surfaces at the caller's next synchronisation.
+ *    All argument checks run on the host before any launch, so a call that
+ *    returns an error has launched nothing and touched no device memory.
+ *  - Thread safety: calls on distinct streams with distinct buffers may run
+ *    concurrently. The error message is thread-local.
+ *  - NaN or infinite inputs are outside the contract.
+ */
+#ifndef IDXC_H
+#define IDXC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  IDXC_OK = 0,
+  IDXC_ERR_INVALID_ARG = 1, /* null pointer, misaligned pointer, size < 1,
+                               q_pos0 + Lq > Lk, workspace too small */
+  IDXC_ERR_PATTERN = 2,     /* pattern length != n_layers, role not in {F,S},
+                               first role not F */
+  IDXC_ERR_UNSUPPORTED = 3, /* sizes outside the compiled set (see above) */
+  IDXC_ERR_HIP = 4          /* HIP runtime error at launch */
+} idxc_status;
+
+/* Problem sizes. q_pos0 = absolute position of query row 0. */
+typedef struct {
+  int32_t B, Lq, Lk, q_pos0;
+  int32_t H_I, d_I; /* indexer heads, indexer head dim */
+  int32_t H, D;     /* attention query heads, head dim (one shared KV head) */
+  int32_t k;        /* top-k size */
+} idxc_dims;
+
+/* Per-layer device pointers for idxc_layer_stack_forward. q_idx, k_idx and w
+ * are read on F layers only and may be NULL on S layers. */
+typedef struct {
+  const void* q_idx;
+  const void* k_idx;
+  const void* w;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+} idxc_layer;
+
+/* Message describing the last non-OK status returned on this thread ("" if
+ * none). The pointer stays valid until the next idxc call on this thread. */
+const char* idxc_last_error(void);
+
+/* Library version string, e.g. "idxc 0.1.0 gfx950". */
+const char* idxc_version(void);
+
+/* Host-only pattern check: [W] state machine rules. Writes the number of F
+ * layers to *n_full (may be NULL). No device is touched. */
+int idxc_validate_pattern(const char* pattern, int32_t n_layers, int32_t* n_full);
+
+/* Host-only nearest-F map: source[l] = l if c_l = F, else
+ * f(l) = max{j < l : c_j = F} ([J] "IndexCache 方法"). source has n_layers
+ * int32 entries in HOST memory. No device is touched. */
+int idxc_schedule(const char* pattern, int32_t n_layers, int32_t* source);
+
+/* Lightning-indexer scores, materialised ([J] "背景 & 问题提出": the indexer
+ * scores every query against all earlier tokens). Writes scores[b,i,s] for
+ * every s in [0, Lk): the fp32 score for s <= t, -inf for s > t; -0.0 is
+ * written as +0.0. Reads q_idx, k_idx, w. Uses B, Lq, Lk, q_pos0, H_I, d_I.
+ * MFMA bf16 products with fp32 accumulation: on integer-valued inputs whose
+ * sums stay below 2^24 the result is exact. */
+int idxc_indexer_scores(const void* q_idx, const void* k_idx, const void* w,
+                        const idxc_dims* dims, float* scores, void* hip_stream);
+
+/* Per-query top-k of materialised scores ([W] I_l = TopK(s_l, k)). Row (b,i)
+ * reads scores[b,i,0..t] only (t = q_pos0 + i) and writes indices[b,i,0..k-1]:
+ * the min(k, t+1) best positions sorted by (score desc, position asc), then
+ * -1. Uses B, Lq, Lk, q_pos0, k. Bit-exact and deterministic. */
+int idxc_topk(const float* scores, const idxc_dims* dims, int32_t* indices,
+              void* hip_stream);
+
+/* Bytes of device workspace that idxc_indexer_topk / idxc_layer_stack_forward
+ * need at full speed for these sizes (written to *bytes). Host-only. */
+int idxc_workspace_bytes(const idxc_dims* dims, size_t* bytes);
+
+/* Fused indexer + top-k: same result as idxc_indexer_scores followed by
+ * idxc_topk, without writing the score matrix. Scores are filtered on chip
+ * against a running per-query threshold; only candidates that can still be
+ * in the top-k are kept, in a caller-provided workspace. Smaller workspaces
+ * (down to 256*ceil(4*B*Lq/256) + 8*B*Lq*64*ceil((k+64)/64) bytes) are
+ * accepted and only cost speed.
+ * Returns IDXC_ERR_INVALID_ARG if the workspace is smaller than that. */
+int idxc_indexer_topk(const void* q_idx, const void* k_idx, const void* w,
+                      const idxc_dims* dims, void* workspace, size_t workspace_bytes,
+                      int32_t* indices, void* hip_stream);
+
+/* Gathered sparse attention ([J] "背景 & 问题提出": core attention only over
+ * the k selected tokens). For each (b,i,h): softmax over the valid entries of
+ * indices[b,i,:] (entries equal to -1 are skipped; every other entry must be
+ * in [0, Lk)) of scale * q[b,i,h,:] . k[b,s,:], then the weighted sum of
+ * v[b,s,:], written to out[b,i,h,:] as bf16. A row with no valid entry gets
+ * zeros. Uses B, Lq, Lk, H, D, k. fp32 softmax and accumulation. */
+int idxc_sparse_attn(const void* q, const void* k, const void* v,
+                     const int32_t* indices, const idxc_dims* dims, float scale,
+                     void* out, void* hip_stream);
+
+/* The whole hot path over a stack of n_layers layers ([W] state machine,
+ * [J] layer loop). The pattern (n_layers chars in {F,S}, first F) is checked
+ * before anything runs. For each layer l in order: if F, the fused indexer +
+ * top-k of layers[l] overwrites index_cache [B,Lq,k] and *indexer_calls is
+ * incremented; then sparse attention of layers[l] reads index_cache and
+ * writes layers[l].out. S layers launch no indexer work. Afterwards
+ * index_cache holds the last F layer's indices. *indexer_calls (HOST
+ * pointer) receives the number of indexer launches (= number of F layers).
+ * debug_indices, if not NULL, is a DEVICE buffer [n_layers, B, Lq, k] that
+ * receives each layer's indices (for tests). workspace as for
+ * idxc_indexer_topk (see idxc_workspace_bytes). */
+int idxc_layer_stack_forward(const char* pattern, int32_t n_layers,
+                             const idxc_layer* layers, const idxc_dims* dims,
+                             float scale, int32_t* index_cache, void* workspace,
+                             size_t workspace_bytes, int32_t* indexer_calls,
+                             int32_t* debug_indices, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IDXC_H */

@@ -1,0 +1,144 @@
+"""CPU-side tests of libidxc.so: it loads, exports every symbol that
+include/idxc.h declares, and its host-only logic and argument checks work
+without a GPU (every error path returns before any HIP call)."""
+import ctypes
+import itertools
+import os
+import re
+
+import pytest
+
+import oracle
+from dsa_lightning_indexer_score_amd import _lib
+from dsa_lightning_indexer_score_amd._lib import IdxcDims, IdxcLayer
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "idxc.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libidxc.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(idxc_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    decl = declared_functions()
+    assert set(decl) == set(_lib.EXPORTED)
+    for name in decl:
+        assert hasattr(lib, name), name
+    assert lib.idxc_version().decode().startswith("idxc")
+
+
+def test_validate_pattern_matches_oracle(lib):
+    for n in range(1, 7):
+        for pat in itertools.product("FSX", repeat=n):
+            p = "".join(pat)
+            nf = ctypes.c_int32(-1)
+            code = lib.idxc_validate_pattern(p.encode(), n, ctypes.byref(nf))
+            try:
+                oracle.validate_pattern(p, n)
+                want_ok = True
+            except ValueError:
+                want_ok = False
+            assert (code == 0) == want_ok, p
+            if want_ok:
+                assert nf.value == p.count("F")
+            else:
+                assert code == _lib.IDXC_ERR_PATTERN
+                assert lib.idxc_last_error().decode() != ""
+    # length mismatch and NULL
+    assert lib.idxc_validate_pattern(b"FSS", 4, None) == _lib.IDXC_ERR_PATTERN
+    assert lib.idxc_validate_pattern(None, 4, None) == _lib.IDXC_ERR_INVALID_ARG
+
+
+def test_schedule_matches_oracle_nearest_full(lib):
+    for n in range(1, 11):
+        for tail in itertools.product("FS", repeat=n - 1):
+            p = "F" + "".join(tail)
+            arr = (ctypes.c_int32 * n)()
+            assert lib.idxc_schedule(p.encode(), n, arr) == 0
+            assert list(arr) == oracle.nearest_full(p)
+
+
+def _dims(**kw):
+    base = dict(B=1, Lq=64, Lk=64, q_pos0=0, H_I=4, d_I=32, H=4, D=64, k=16)
+    base.update(kw)
+    return IdxcDims(*[base[n] for n, _ in IdxcDims._fields_])
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails its checks first
+
+
+def P(x=FAKE):
+    return ctypes.c_void_p(x)
+
+
+def test_indexer_scores_argument_errors(lib):
+    f = lib.idxc_indexer_scores
+    ok = _dims()
+    assert f(None, P(), P(), ctypes.byref(ok), P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(FAKE + 2), P(), P(), ctypes.byref(ok), P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), P(), P(), None, P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    for bad, code in ((dict(Lq=0), 1), (dict(q_pos0=1), 1), (dict(Lk=10, Lq=11), 1),
+                      (dict(d_I=48), 3), (dict(H_I=65), 3), (dict(H_I=0), 1),
+                      (dict(q_pos0=-1), 1)):
+        assert f(P(), P(), P(), ctypes.byref(_dims(**bad)), P(), None) == code, bad
+
+
+def test_topk_argument_errors(lib):
+    f = lib.idxc_topk
+    assert f(P(), ctypes.byref(_dims(k=0)), P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), ctypes.byref(_dims(k=4096)), P(), None) == _lib.IDXC_ERR_UNSUPPORTED
+    assert f(None, ctypes.byref(_dims()), P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), ctypes.byref(_dims()), P(FAKE + 4), None) == _lib.IDXC_ERR_INVALID_ARG
+
+
+def test_sparse_attn_argument_errors(lib):
+    f = lib.idxc_sparse_attn
+    for bad, code in ((dict(D=96), 3), (dict(H=65), 3), (dict(k=0), 1), (dict(B=0), 1)):
+        assert f(P(), P(), P(), P(), ctypes.byref(_dims(**bad)), 0.125, P(), None) == code
+    assert f(P(), None, P(), P(), ctypes.byref(_dims()), 0.125, P(), None) == 1
+    assert f(P(), P(), P(), P(), ctypes.byref(_dims()), float("nan"), P(), None) == 1
+
+
+def test_workspace_and_fused_errors(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.idxc_workspace_bytes(ctypes.byref(_dims()), ctypes.byref(n)) == 0
+    assert n.value >= 64 * (8 * (16 + 64) + 4)
+    f = lib.idxc_indexer_topk
+    assert f(P(), P(), P(), ctypes.byref(_dims()), P(), 16, P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert "workspace" in lib.idxc_last_error().decode()
+
+
+def test_stack_errors_before_launch(lib):
+    f = lib.idxc_layer_stack_forward
+    layers = (IdxcLayer * 4)()
+    for l in range(4):
+        layers[l] = IdxcLayer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    d = _dims()
+    calls = ctypes.c_int32(-7)
+    args = lambda pat, n, ly=layers, dd=d, ws=1 << 30: (
+        pat, n, ly, ctypes.byref(dd), 0.125, P(), P(), ws, ctypes.byref(calls), None, None)
+    assert f(*args(b"SFSF", 4)) == _lib.IDXC_ERR_PATTERN
+    assert f(*args(b"FSS", 4)) == _lib.IDXC_ERR_PATTERN
+    assert f(*args(b"FSQF", 4)) == _lib.IDXC_ERR_PATTERN
+    assert f(*args(None, 4)) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(*args(b"FSSF", 4, ws=8)) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(*args(b"FSSF", 4, dd=_dims(k=0))) == _lib.IDXC_ERR_INVALID_ARG
+    # an F layer without indexer inputs is rejected, an S layer's are never read
+    layers[3] = IdxcLayer(0, 0, 0, FAKE, FAKE, FAKE, FAKE)
+    assert f(*args(b"FSSF", 4)) == _lib.IDXC_ERR_INVALID_ARG
+    assert "layers[3].q_idx" in lib.idxc_last_error().decode()
+    layers[2] = IdxcLayer(0, 0, 0, 0, FAKE, FAKE, FAKE)
+    assert f(*args(b"FSSS", 4)) == _lib.IDXC_ERR_INVALID_ARG
+    assert "layers[2].q" in lib.idxc_last_error().decode()
+    assert calls.value == -7  # nothing ran

@@ -1,0 +1,277 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: bit-exact scores and indices on integer-valued inputs (every partial sum
+is exact in fp32); on random bf16 inputs mean top-k set overlap >= 0.99 and
+attention max-abs error <= 2e-2 against the fp64 oracle. The attention error
+is measured on seeded index sets fed to both sides, so selection near-ties
+do not mix into it.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import idxc_inputs as gen
+import oracle
+import dsa_lightning_indexer_score_amd as idxc
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 2e-2
+MIN_OVERLAP = 0.99
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+def cu(t):
+    return t.to("cuda").contiguous()
+
+
+def f64(t):
+    return gen.to_f64(t)
+
+
+def assert_scores_exact(got, want):
+    got = got.cpu().numpy()
+    assert got.shape == want.shape
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isneginf(got), np.isneginf(want))
+    bad = np.argwhere(got[fin] != want[fin])
+    assert bad.size == 0, "score mismatch at %d entries" % len(bad)
+    assert not np.signbit(got[fin][got[fin] == 0]).any()
+
+
+# --------------------------------------------------------------------------- #
+# indexer scores
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("B,L,H_I,d_I,q_pos0,Lq", [
+    (1, 256, 4, 32, 0, 256),      # tiny configuration shape
+    (1, 600, 64, 128, 0, 600),    # ragged vs 8-row blocks and 64-key tiles
+    (2, 333, 40, 64, 0, 333),     # H_I not a multiple of 32, two batches
+    (1, 700, 64, 128, 500, 200),  # a query chunk at q_pos0 = 500
+])
+def test_indexer_scores_integer_exact(B, L, H_I, d_I, q_pos0, Lq):
+    _say("indexer_scores int B=%d L=%d H_I=%d d_I=%d q_pos0=%d" % (B, L, H_I, d_I, q_pos0))
+    q, k, w = gen.indexer_inputs(B, Lq, L, H_I, d_I, kind="int", seed=11, w_kind="neg-quarter")
+    got = idxc.idxc_indexer_scores(cu(q), cu(k), cu(w), q_pos0=q_pos0)
+    torch.cuda.synchronize()
+    want = oracle.indexer_scores(f64(q), f64(k), f64(w), q_pos0)
+    assert_scores_exact(got, want)
+
+
+def test_indexer_scores_split_path_integer_exact():
+    # few rows against many keys: split-key kernel (decode shape)
+    B, Lk = 3, 20000
+    _say("indexer_scores split B=%d Lk=%d" % (B, Lk))
+    q, k, w = gen.indexer_inputs(B, 1, Lk, 64, 128, kind="int", seed=12, w_kind="quarter")
+    got = idxc.idxc_indexer_scores(cu(q), cu(k), cu(w), q_pos0=Lk - 1)
+    torch.cuda.synchronize()
+    want = oracle.indexer_scores(f64(q), f64(k), f64(w), Lk - 1)
+    assert_scores_exact(got, want)
+    # a split-path call that ends inside the causal range (t < Lk - 1)
+    got = idxc.idxc_indexer_scores(cu(q), cu(k), cu(w), q_pos0=12345)
+    torch.cuda.synchronize()
+    want = oracle.indexer_scores(f64(q), f64(k), f64(w), 12345)
+    assert_scores_exact(got, want)
+
+
+# --------------------------------------------------------------------------- #
+# top-k on seeded score rows
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("kind,B,Lq,Lk,q_pos0,k", [
+    ("normal", 1, 300, 300, 0, 16),
+    ("ties", 2, 130, 130, 0, 100),
+    ("signed-zero", 1, 70, 200, 130, 33),
+    ("const", 1, 50, 50, 0, 7),
+    ("normal", 1, 40, 5000, 4960, 2048),
+    ("ties", 1, 8, 12000, 11992, 2048),     # rows longer than the LDS stage
+    ("normal", 3, 1, 30000, 29999, 2048),   # decode-shaped rows
+    ("normal", 1, 20, 20, 0, 2048),         # every row shorter than k
+])
+def test_topk_exact(kind, B, Lq, Lk, q_pos0, k):
+    _say("topk %s B=%d Lq=%d Lk=%d q_pos0=%d k=%d" % (kind, B, Lq, Lk, q_pos0, k))
+    s = gen.score_rows(B, Lq, Lk, kind=kind, seed=3)
+    got = idxc.idxc_topk(cu(s), k, q_pos0=q_pos0)
+    torch.cuda.synchronize()
+    want = oracle.topk(s.numpy(), k, q_pos0)
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
+# --------------------------------------------------------------------------- #
+# fused indexer + top-k
+# --------------------------------------------------------------------------- #
+def _min_ws(B, Lq, k):
+    rows = B * Lq
+    return ((rows * 4 + 255) // 256) * 256 + rows * ((k + 64 + 63) // 64 * 64) * 8
+
+
+@pytest.mark.parametrize("B,L,H_I,d_I,k,small_ws", [
+    (1, 256, 4, 32, 16, False),
+    (1, 256, 4, 32, 16, True),      # tiny candidate buffers: many compactions
+    (1, 900, 64, 128, 128, False),
+    (1, 900, 64, 128, 128, True),
+    (2, 520, 64, 128, 512, True),
+])
+def test_indexer_topk_integer_exact(B, L, H_I, d_I, k, small_ws):
+    _say("indexer_topk int B=%d L=%d k=%d small_ws=%s" % (B, L, k, small_ws))
+    q, kk, w = gen.indexer_inputs(B, L, L, H_I, d_I, kind="int", seed=21, w_kind="quarter")
+    ws = None
+    if small_ws:
+        ws = torch.empty(_min_ws(B, L, k), dtype=torch.uint8, device="cuda")
+    got = idxc.idxc_indexer_topk(cu(q), cu(kk), cu(w), k, workspace=ws)
+    torch.cuda.synchronize()
+    want = oracle.topk(oracle.indexer_scores(f64(q), f64(kk), f64(w), 0), k, 0)
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
+def test_indexer_topk_random_overlap_and_determinism():
+    B, L, H_I, d_I, k = 1, 1500, 64, 128, 256
+    _say("indexer_topk normal L=%d k=%d" % (L, k))
+    q, kk, w = gen.indexer_inputs(B, L, L, H_I, d_I, kind="normal", seed=5,
+                                  idx_std=d_I ** -0.5)
+    a = idxc.idxc_indexer_topk(cu(q), cu(kk), cu(w), k)
+    b = idxc.idxc_indexer_topk(cu(q), cu(kk), cu(w), k)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    want = oracle.topk(oracle.indexer_scores(f64(q), f64(kk), f64(w), 0), k, 0)
+    mean, mn = oracle.mean_overlap(a.cpu().numpy(), want)
+    _say("overlap mean %.5f min %.5f" % (mean, mn))
+    assert mean >= MIN_OVERLAP
+
+
+def test_fused_equals_materialised_and_decode_equals_last_row():
+    B, L, H_I, d_I, k = 2, 700, 64, 128, 64
+    q, kk, w = gen.indexer_inputs(B, L, L, H_I, d_I, kind="int", seed=8, w_kind="neg-quarter")
+    fused = idxc.idxc_indexer_topk(cu(q), cu(kk), cu(w), k)
+    two = idxc.idxc_topk(idxc.idxc_indexer_scores(cu(q), cu(kk), cu(w)), k)
+    dec = idxc.idxc_indexer_topk(cu(q[:, L - 1:]), cu(kk), cu(w[:, L - 1:]), k, q_pos0=L - 1)
+    chunk = idxc.idxc_indexer_topk(cu(q[:, 256:512]), cu(kk[:, :512]), cu(w[:, 256:512]), k,
+                                   q_pos0=256)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, two)
+    assert torch.equal(dec[:, 0], fused[:, L - 1])
+    assert torch.equal(chunk, fused[:, 256:512])
+
+
+# --------------------------------------------------------------------------- #
+# sparse attention on seeded index sets
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("B,Lq,Lk,q_pos0,H,D,k,pad", [
+    (1, 256, 256, 0, 4, 64, 16, 0.0),
+    (1, 300, 300, 0, 64, 128, 64, 0.3),
+    (2, 1100, 1100, 0, 64, 128, 100, 0.0),    # >= 1024 rows: one wave per query
+    (4, 1, 5000, 4999, 64, 128, 2048, 0.0),   # decode-shaped: 4 waves per query
+    (3, 2, 3000, 2998, 40, 64, 300, 0.5),
+])
+def test_sparse_attn_matches_oracle(B, Lq, Lk, q_pos0, H, D, k, pad):
+    _say("sparse_attn B=%d Lq=%d Lk=%d H=%d D=%d k=%d" % (B, Lq, Lk, H, D, k))
+    Q, K, V = gen.attn_inputs(B, Lq, Lk, H, D, seed=9)
+    idx = gen.index_sets(B, Lq, q_pos0, k, seed=4, pad_frac=pad)
+    scale = D ** -0.5
+    got = idxc.idxc_sparse_attn(cu(Q), cu(K), cu(V), cu(idx), scale)
+    torch.cuda.synchronize()
+    want = oracle.sparse_attention(f64(Q), f64(K), f64(V), idx.numpy(), scale)
+    err = np.abs(got.float().cpu().numpy() - want).max()
+    _say("max abs err %.3e" % err)
+    assert err <= ATOL
+
+
+def test_sparse_attn_single_key_is_exact_copy():
+    B, L, H, D, k = 1, 200, 64, 128, 8
+    Q, K, V = gen.attn_inputs(B, L, L, H, D, seed=10)
+    idx = torch.full((B, L, k), -1, dtype=torch.int32)
+    rng = np.random.default_rng(0)
+    for t in range(L):
+        idx[0, t, int(rng.integers(0, k))] = int(rng.integers(0, t + 1))
+    got = idxc.idxc_sparse_attn(cu(Q), cu(K), cu(V), cu(idx), D ** -0.5)
+    torch.cuda.synchronize()
+    sel = idx.max(dim=-1).values[0].long()
+    want = V[0, sel][:, None, :].expand(L, H, D)
+    assert torch.equal(got[0].cpu(), want)
+
+
+# --------------------------------------------------------------------------- #
+# the stack
+# --------------------------------------------------------------------------- #
+def _layers(cfg, device="cpu"):
+    return [gen.layer_inputs(cfg, l, device=device) for l in range(cfg.n_layers)]
+
+
+def test_stack_tiny_fssf_exact():
+    cfg = gen.C1
+    _say("stack %s" % cfg.name)
+    layers = _layers(cfg)
+    dev_layers = [{n: cu(t) for n, t in L.items()} for L in layers]
+    res = idxc.idxc_layer_stack_forward(cfg.pattern, dev_layers, cfg.k, cfg.scale,
+                                        q_pos0=cfg.q_pos0, debug_indices=True)
+    torch.cuda.synchronize()
+    ref = oracle.layer_stack(cfg.pattern, [{n: f64(t) for n, t in L.items()} for L in layers],
+                             cfg.k, cfg.scale, cfg.q_pos0)
+    assert res["indexer_calls"] == ref["calls"] == 2
+    dbg = res["debug_indices"].cpu().numpy()
+    for l in range(cfg.n_layers):
+        assert np.array_equal(dbg[l], ref["indices"][l]), l
+        err = np.abs(res["out"][l].float().cpu().numpy() - ref["out"][l]).max()
+        assert err <= ATOL, (l, err)
+    assert np.array_equal(dbg[1], dbg[0]) and np.array_equal(dbg[2], dbg[0])
+    assert not np.array_equal(dbg[3], dbg[0])
+    assert np.array_equal(res["index_cache"].cpu().numpy(), ref["indices"][3])
+
+
+def test_stack_s_layers_ignore_indexer_inputs():
+    cfg = gen.C1
+    layers = [{n: cu(t) for n, t in L.items()} for L in _layers(cfg)]
+    for l in (1, 2):
+        for n in ("q_idx", "k_idx", "w"):
+            layers[l][n] = None
+    res = idxc.idxc_layer_stack_forward(cfg.pattern, layers, cfg.k, cfg.scale,
+                                        debug_indices=True)
+    torch.cuda.synchronize()
+    assert res["indexer_calls"] == 2
+
+
+def test_stack_random_small_overlap():
+    import dataclasses
+    cfg = dataclasses.replace(gen.C2, name="small", n_layers=4, pattern="FSFS", Lq=1024,
+                              Lk=1024, k=256)
+    _say("stack random L=%d" % cfg.Lq)
+    layers = _layers(cfg)
+    dev_layers = [{n: cu(t) for n, t in L.items()} for L in layers]
+    res = idxc.idxc_layer_stack_forward(cfg.pattern, dev_layers, cfg.k, cfg.scale,
+                                        debug_indices=True)
+    torch.cuda.synchronize()
+    assert res["indexer_calls"] == 2
+    dbg = res["debug_indices"].cpu().numpy()
+    for l in (0, 2):
+        L = layers[l]
+        want = oracle.topk(oracle.indexer_scores(f64(L["q_idx"]), f64(L["k_idx"]),
+                                                 f64(L["w"]), 0), cfg.k, 0)
+        mean, mn = oracle.mean_overlap(dbg[l], want)
+        _say("layer %d overlap mean %.5f min %.5f" % (l, mean, mn))
+        assert mean >= MIN_OVERLAP
+    assert np.array_equal(dbg[1], dbg[0]) and np.array_equal(dbg[3], dbg[2])
+    # attention of S layer 3 on its (GPU-selected) cache, checked on the rows
+    # whose selected set equals the oracle's own selection for layer 2
+    L3 = layers[3]
+    want2 = oracle.topk(oracle.indexer_scores(f64(layers[2]["q_idx"]), f64(layers[2]["k_idx"]),
+                                              f64(layers[2]["w"]), 0), cfg.k, 0)
+    same = [t for t in range(cfg.Lq) if np.array_equal(dbg[3][0, t], want2[0, t])]
+    assert len(same) >= 0.5 * cfg.Lq
+    rows = np.array(same[:: max(1, len(same) // 64)])
+    ref = oracle.sparse_attention(f64(L3["q"])[:, rows], f64(L3["k"]), f64(L3["v"]),
+                                  want2[:, rows], cfg.scale)
+    err = np.abs(res["out"][3].float().cpu().numpy()[:, rows] - ref).max()
+    assert err <= ATOL
