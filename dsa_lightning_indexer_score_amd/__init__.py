@@ -16,7 +16,7 @@ from ._lib import IdxcDims, IdxcError, IdxcLayer
 
 __all__ = ["idxc_version", "idxc_validate_pattern", "idxc_schedule", "idxc_indexer_scores",
            "idxc_topk", "idxc_workspace_bytes", "idxc_indexer_topk", "idxc_sparse_attn",
-           "idxc_layer_stack_forward", "make_dims", "IdxcError"]
+           "idxc_layer_stack_forward", "make_dims", "IdxcError", "StackCall"]
 
 
 def _stream(stream=None) -> ctypes.c_void_p:
@@ -177,3 +177,51 @@ def idxc_layer_stack_forward(pattern: str, layers: Sequence[Dict[str, torch.Tens
                                             _stream(stream)))
     return dict(out=outs, indexer_calls=calls.value, index_cache=index_cache,
                 debug_indices=dbg)
+
+
+class StackCall:
+    """idxc_layer_stack_forward with its arguments marshalled once.
+
+    Holds references to every tensor it points at; calling it runs the whole
+    stack on the given stream and returns the number of indexer launches.
+    """
+
+    def __init__(self, pattern: str, layers: Sequence[Dict[str, torch.Tensor]], k: int,
+                 scale: float, q_pos0: int = 0, index_cache=None, workspace=None):
+        self._lib = _lib.load()
+        self.layers = layers
+        n = len(layers)
+        ref = next(L for L in layers if L.get("q") is not None)
+        B, Lq, H, D = ref["q"].shape
+        Lk = ref["k"].shape[1]
+        f0 = next(L for L in layers if L.get("q_idx") is not None)
+        H_I, d_I = f0["q_idx"].shape[2], f0["q_idx"].shape[3]
+        dev = ref["q"].device
+        self.dims = make_dims(B, Lq, Lk, q_pos0, H_I, d_I, H, D, k)
+        self.index_cache = index_cache if index_cache is not None else torch.empty(
+            (B, Lq, k), dtype=torch.int32, device=dev)
+        self.workspace = workspace if workspace is not None else _workspace(
+            idxc_workspace_bytes(B, Lq, Lk, q_pos0, H_I, d_I, k), dev)
+        self.arr = (IdxcLayer * n)()
+        for l, L in enumerate(layers):
+            self.arr[l] = IdxcLayer(_ptr(L.get("q_idx"), "q_idx", torch.bfloat16).value,
+                                    _ptr(L.get("k_idx"), "k_idx", torch.bfloat16).value,
+                                    _ptr(L.get("w"), "w", torch.bfloat16).value,
+                                    _ptr(L["q"], "q", torch.bfloat16).value,
+                                    _ptr(L["k"], "k", torch.bfloat16).value,
+                                    _ptr(L["v"], "v", torch.bfloat16).value,
+                                    _ptr(L["out"], "out", torch.bfloat16).value)
+        self.pattern = pattern.encode()
+        self.n = n
+        self.scale = float(scale)
+        self.calls = ctypes.c_int32(-1)
+        self.cache_ptr = _ptr(self.index_cache, "index_cache")
+        self.ws_ptr = _ptr(self.workspace, "workspace")
+        self.ws_bytes = self.workspace.numel() * self.workspace.element_size()
+
+    def __call__(self, stream=None) -> int:
+        _lib.check(self._lib.idxc_layer_stack_forward(
+            self.pattern, self.n, self.arr, ctypes.byref(self.dims), self.scale,
+            self.cache_ptr, self.ws_ptr, self.ws_bytes, ctypes.byref(self.calls), None,
+            _stream(stream)))
+        return self.calls.value

@@ -170,7 +170,7 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
         x[i] = ok ? s[i] * sl2 : -INFINITY;
         mloc = fmaxf(mloc, x[i]);
       }
-      const float mblk = fmaxf(mloc, swap_halves(mloc));
+      const float mblk = pair_max(mloc);
       const float mnew = fmaxf(m[hb], mblk);
       const bool none = mnew == -INFINITY;
       const float alpha = none ? 1.0f : exp2f(m[hb] - mnew);
@@ -205,7 +205,7 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
 
   float lt[HB];
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb) lt[hb] = lsum[hb] + swap_halves(lsum[hb]);
+  for (int hb = 0; hb < HB; ++hb) lt[hb] = pair_sum(lsum[hb]);
 
   if (wpq != 1) {
     // ---- merge the 4 waves' partial softmax states through LDS into wave 0

@@ -27,11 +27,20 @@ __device__ __forceinline__ int acc_row(int i, int lane) {
   return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
 }
 
-// Value of x held by lane (l ^ 32).
-__device__ __forceinline__ float swap_halves(float x) {
+// x[l] + x[l ^ 32] (identical in both lanes of the pair). permlane32_swap
+// returns both halves of the swapped register pair; per lane one of them is
+// the lane's own value and the other its partner's, so their sum (or max) is
+// the pair reduction.
+__device__ __forceinline__ float pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
                                             false, false);
-  return __uint_as_float(r[0]);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                            false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {

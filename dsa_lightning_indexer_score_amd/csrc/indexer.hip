@@ -233,7 +233,7 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
 #pragma unroll
           for (int i = 0; i < 16; ++i) part = fmaf(wv[hb][i], fmaxf(acc[i], 0.0f), part);
         }
-        part += swap_halves(part);
+        part = pair_sum(part);
         sc[nb] = part;
       }
       // lane l now scores key tile_s0 + l
@@ -258,6 +258,10 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
           n_cand += cnt;
         }
       }
+    } else if (MODE == 0 && active) {
+      // a tile wholly above this row's position (the block straddles a tile)
+      const int s = tile_s0 + lane;
+      if (s < Lk) my_scores[s] = -INFINITY;
     }
     if (j + 1 < ntiles) store_tile((j + 1) & 1);
     __syncthreads();
@@ -345,7 +349,7 @@ void indexer_split_kernel(const uint16_t* __restrict__ q_idx,
 #pragma unroll
       for (int i = 0; i < 16; ++i) part = fmaf(wv[hb][i], fmaxf(acc[i], 0.0f), part);
     }
-    part += swap_halves(part);
+    part = pair_sum(part);
     const int s = s0 + lane;
     if (lane < 32 && s < s_end) srow[s] = (s <= t) ? part + 0.0f : -INFINITY;
 #pragma unroll
