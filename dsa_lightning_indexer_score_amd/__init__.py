@@ -15,7 +15,7 @@ from . import _lib
 from ._lib import IdxcDims, IdxcError, IdxcLayer
 
 __all__ = ["idxc_version", "idxc_validate_pattern", "idxc_schedule", "idxc_indexer_scores",
-           "idxc_topk", "idxc_workspace_bytes", "idxc_indexer_topk", "idxc_sparse_attn",
+           "idxc_topk", "idxc_topk_workspace_bytes", "idxc_workspace_bytes", "idxc_indexer_topk", "idxc_sparse_attn", "idxc_sparse_attn_workspace_bytes",
            "idxc_layer_stack_forward", "make_dims", "IdxcError", "StackCall"]
 
 
@@ -79,20 +79,33 @@ def idxc_indexer_scores(q_idx, k_idx, w, q_pos0: int = 0, out=None, stream=None)
     return out
 
 
-def idxc_topk(scores, k: int, q_pos0: int = 0, out=None, stream=None):
+def idxc_topk_workspace_bytes(B, Lq, Lk, q_pos0, k) -> int:
+    lib = _lib.load()
+    d = make_dims(B, Lq, Lk, q_pos0, k=k)
+    n = ctypes.c_size_t(0)
+    _lib.check(lib.idxc_topk_workspace_bytes(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def idxc_topk(scores, k: int, q_pos0: int = 0, workspace=None, out=None, stream=None):
     lib = _lib.load()
     B, Lq, Lk = scores.shape
     d = make_dims(B, Lq, Lk, q_pos0, k=k)
+    if workspace is None:
+        nb = idxc_topk_workspace_bytes(B, Lq, Lk, q_pos0, k)
+        workspace = _workspace(nb, scores.device) if nb else None
     if out is None:
         out = torch.empty((B, Lq, k), dtype=torch.int32, device=scores.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _lib.check(lib.idxc_topk(_ptr(scores, "scores", torch.float32), ctypes.byref(d),
+                             _ptr(workspace, "workspace"), nbytes,
                              _ptr(out, "indices", torch.int32), _stream(stream)))
     return out
 
 
-def idxc_workspace_bytes(B, Lq, Lk, q_pos0, H_I, d_I, k) -> int:
+def idxc_workspace_bytes(B, Lq, Lk, q_pos0, H_I, d_I, k, H=0, D=0) -> int:
     lib = _lib.load()
-    d = make_dims(B, Lq, Lk, q_pos0, H_I, d_I, 0, 0, k)
+    d = make_dims(B, Lq, Lk, q_pos0, H_I, d_I, H, D, k)
     n = ctypes.c_size_t(0)
     _lib.check(lib.idxc_workspace_bytes(ctypes.byref(d), ctypes.byref(n)))
     return n.value
@@ -120,17 +133,30 @@ def idxc_indexer_topk(q_idx, k_idx, w, k: int, q_pos0: int = 0, workspace=None, 
     return out
 
 
-def idxc_sparse_attn(q, k, v, indices, scale: float, out=None, stream=None):
+def idxc_sparse_attn_workspace_bytes(B, Lq, Lk, H, D, k) -> int:
+    lib = _lib.load()
+    d = make_dims(B, Lq, Lk, 0, 0, 0, H, D, k)
+    n = ctypes.c_size_t(0)
+    _lib.check(lib.idxc_sparse_attn_workspace_bytes(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def idxc_sparse_attn(q, k, v, indices, scale: float, workspace="auto", out=None, stream=None):
+    """workspace: "auto" (allocate what a split needs), None (no split) or a tensor."""
     lib = _lib.load()
     B, Lq, H, D = q.shape
     d = make_dims(B, Lq, k.shape[1], 0, 0, 0, H, D, indices.shape[-1])
+    if isinstance(workspace, str):
+        nb = idxc_sparse_attn_workspace_bytes(B, Lq, k.shape[1], H, D, indices.shape[-1])
+        workspace = _workspace(nb, q.device) if nb else None
     if out is None:
         out = torch.empty_like(q)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _lib.check(lib.idxc_sparse_attn(_ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
                                     _ptr(v, "v", torch.bfloat16),
                                     _ptr(indices, "indices", torch.int32), ctypes.byref(d),
-                                    float(scale), _ptr(out, "out", torch.bfloat16),
-                                    _stream(stream)))
+                                    float(scale), _ptr(workspace, "workspace"), nbytes,
+                                    _ptr(out, "out", torch.bfloat16), _stream(stream)))
     return out
 
 
@@ -152,7 +178,7 @@ def idxc_layer_stack_forward(pattern: str, layers: Sequence[Dict[str, torch.Tens
     if index_cache is None:
         index_cache = torch.empty((B, Lq, k), dtype=torch.int32, device=dev)
     if workspace is None:
-        workspace = _workspace(idxc_workspace_bytes(B, Lq, Lk, q_pos0, H_I, d_I, k), dev)
+        workspace = _workspace(idxc_workspace_bytes(B, Lq, Lk, q_pos0, H_I, d_I, k, H, D), dev)
     dbg = torch.empty((n, B, Lq, k), dtype=torch.int32, device=dev) if debug_indices else None
     arr = (IdxcLayer * n)()
     outs = []
@@ -201,7 +227,7 @@ class StackCall:
         self.index_cache = index_cache if index_cache is not None else torch.empty(
             (B, Lq, k), dtype=torch.int32, device=dev)
         self.workspace = workspace if workspace is not None else _workspace(
-            idxc_workspace_bytes(B, Lq, Lk, q_pos0, H_I, d_I, k), dev)
+            idxc_workspace_bytes(B, Lq, Lk, q_pos0, H_I, d_I, k, H, D), dev)
         self.arr = (IdxcLayer * n)()
         for l, L in enumerate(layers):
             self.arr[l] = IdxcLayer(_ptr(L.get("q_idx"), "q_idx", torch.bfloat16).value,

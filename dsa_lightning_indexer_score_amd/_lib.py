@@ -28,8 +28,9 @@ STATUS_NAMES = {
 # Every symbol declared in include/idxc.h.
 EXPORTED = (
     "idxc_last_error", "idxc_version", "idxc_validate_pattern", "idxc_schedule",
-    "idxc_indexer_scores", "idxc_topk", "idxc_workspace_bytes", "idxc_indexer_topk",
-    "idxc_sparse_attn", "idxc_layer_stack_forward",
+    "idxc_indexer_scores", "idxc_topk", "idxc_topk_workspace_bytes", "idxc_workspace_bytes",
+    "idxc_indexer_topk", "idxc_sparse_attn", "idxc_sparse_attn_workspace_bytes",
+    "idxc_layer_stack_forward",
 )
 
 
@@ -69,11 +70,13 @@ def load() -> ctypes.CDLL:
         "idxc_validate_pattern": ([ctypes.c_char_p, i32, P(i32)], ctypes.c_int),
         "idxc_schedule": ([ctypes.c_char_p, i32, P(i32)], ctypes.c_int),
         "idxc_indexer_scores": ([vp, vp, vp, P(IdxcDims), vp, vp], ctypes.c_int),
-        "idxc_topk": ([vp, P(IdxcDims), vp, vp], ctypes.c_int),
+        "idxc_topk": ([vp, P(IdxcDims), vp, sz, vp, vp], ctypes.c_int),
+        "idxc_topk_workspace_bytes": ([P(IdxcDims), P(sz)], ctypes.c_int),
         "idxc_workspace_bytes": ([P(IdxcDims), P(sz)], ctypes.c_int),
         "idxc_indexer_topk": ([vp, vp, vp, P(IdxcDims), vp, sz, vp, vp], ctypes.c_int),
-        "idxc_sparse_attn": ([vp, vp, vp, vp, P(IdxcDims), ctypes.c_float, vp, vp],
+        "idxc_sparse_attn": ([vp, vp, vp, vp, P(IdxcDims), ctypes.c_float, vp, sz, vp, vp],
                              ctypes.c_int),
+        "idxc_sparse_attn_workspace_bytes": ([P(IdxcDims), P(sz)], ctypes.c_int),
         "idxc_layer_stack_forward": ([ctypes.c_char_p, i32, P(IdxcLayer), P(IdxcDims),
                                       ctypes.c_float, vp, vp, sz, P(i32), vp, vp],
                                      ctypes.c_int),

@@ -109,10 +109,13 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // must still take one more 64-key tile.
 int min_cap(int k) { return (k + 64 + 63) / 64 * 64; }
 
+// Default candidate capacity: room for the ~2.5k keys a sampled threshold
+// lets through, with margin.
 int default_cap(int k) {
-  int cap = 2 * k;
+  int cap = 4 * k;
   if (cap < k + 64) cap = k + 64;
-  if (cap < 4096) cap = 4096;
+  if (cap < 8192) cap = 8192;
+  if (cap > kMaxStagePairs) cap = kMaxStagePairs;
   return (cap + 63) / 64 * 64;
 }
 
@@ -122,16 +125,22 @@ struct Plan {
   size_t min_bytes;
 };
 
-Plan plan_for(const idxc_dims* d) {
+Plan plan_for(const idxc_dims* d, bool with_attn = false) {
   Plan p;
   const size_t rows = (size_t)d->B * d->Lq;
   p.split = indexer_prefers_split(d->B, d->Lq, d->Lk);
   if (p.split) {
-    p.bytes = align_up(rows * (size_t)d->Lk * 4);
+    p.bytes = align_up(rows * (size_t)d->Lk * 4) + align_up(topk_part_bytes((int)rows, d->Lk, d->k));
     p.min_bytes = p.bytes;
   } else {
     p.bytes = align_up(rows * 4) + rows * (size_t)default_cap(d->k) * 8;
     p.min_bytes = align_up(rows * 4) + rows * (size_t)min_cap(d->k) * 8;
+  }
+  if (with_attn) {
+    // the layer loop reuses the same workspace for attention partials
+    const size_t att = attn_workspace_bytes(d->B, d->Lq, d->H, d->D, d->k);
+    if (att > p.bytes) p.bytes = att;
+    if (att > p.min_bytes) p.min_bytes = att;
   }
   return p;
 }
@@ -146,6 +155,22 @@ int cap_for(const idxc_dims* d, size_t ws_bytes) {
   const size_t dc = (size_t)default_cap(d->k);
   if (cap > dc) cap = dc;
   return (int)cap;
+}
+
+// Scratch of the two-stage top-k for long materialised rows, at `base`.
+void set_parts(TopkArgs& ta, uint8_t* base, const idxc_dims* d) {
+  const int rows = d->B * d->Lq;
+  const int nch = topk_row_chunks(d->Lk);
+  if (nch <= 1) return;
+  ta.part = reinterpret_cast<u32x2_t*>(base);
+  ta.part_count = reinterpret_cast<int*>(base + (size_t)rows * nch * d->k * 8);
+}
+
+// Long materialised rows are selected in two stages; the second stage must
+// hold every chunk's winners in one workgroup.
+bool topk_rows_supported(const idxc_dims* d) {
+  const int nch = topk_row_chunks(d->Lk);
+  return nch <= 1 || (nch <= kMaxSegments && (long long)nch * d->k <= kMaxStagePairs);
 }
 
 // Indexer + top-k for one layer into `indices`, using the workspace.
@@ -176,6 +201,7 @@ hipError_t run_indexer_topk(const void* q_idx, const void* k_idx, const void* w,
     hipError_t e = launch_indexer_scores(ia, st);
     if (e != hipSuccess) return e;
     ta.scores = ia.scores;
+    set_parts(ta, static_cast<uint8_t*>(ws) + align_up((size_t)rows * d->Lk * 4), d);
     return launch_topk(ta, st);
   }
   const int cap = cap_for(d, ws_bytes);
@@ -186,13 +212,16 @@ hipError_t run_indexer_topk(const void* q_idx, const void* k_idx, const void* w,
   if (e != hipSuccess) return e;
   ta.cand = ia.cand;
   ta.cand_count = ia.cand_count;
-  ta.cap = cap;
+  ta.nseg = 1;
+  ta.seg_cap = cap;
+  ta.stage_cap = d->k;  // the candidate kernel leaves at most k per row
   return launch_topk(ta, st);
 }
 
 AttnArgs attn_args(const void* q, const void* k, const void* v, const int32_t* indices,
-                   const idxc_dims* d, float scale, void* out) {
+                   const idxc_dims* d, float scale, void* out, void* workspace) {
   AttnArgs a{};
+  a.workspace = workspace;
   a.q = static_cast<const uint16_t*>(q);
   a.key = static_cast<const uint16_t*>(k);
   a.val = static_cast<const uint16_t*>(v);
@@ -237,9 +266,12 @@ int idxc_workspace_bytes(const idxc_dims* dims, size_t* bytes) {
   int r = check_dims(dims, 1 | 4);
   if (r != IDXC_OK) return r;
   if (bytes == nullptr) return fail(IDXC_ERR_INVALID_ARG, "bytes is NULL");
-  const Plan p = plan_for(dims);
-  // the stack also needs nothing else: attention runs without workspace
-  *bytes = p.bytes;
+  const bool with_attn = dims->H > 0 && dims->D > 0;
+  if (with_attn) {
+    r = check_dims(dims, 2);
+    if (r != IDXC_OK) return r;
+  }
+  *bytes = plan_for(dims, with_attn).bytes;
   return ok();
 }
 
@@ -267,11 +299,30 @@ int idxc_indexer_scores(const void* q_idx, const void* k_idx, const void* w,
                     "indexer_scores launch");
 }
 
-int idxc_topk(const float* scores, const idxc_dims* dims, int32_t* indices, void* hip_stream) {
+int idxc_topk_workspace_bytes(const idxc_dims* dims, size_t* bytes) {
+  int r = check_dims(dims, 4);
+  if (r != IDXC_OK) return r;
+  if (bytes == nullptr) return fail(IDXC_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = topk_part_bytes(dims->B * dims->Lq, dims->Lk, dims->k);
+  return ok();
+}
+
+int idxc_topk(const float* scores, const idxc_dims* dims, void* workspace, size_t workspace_bytes,
+              int32_t* indices, void* hip_stream) {
   int r = check_dims(dims, 4);
   if (r != IDXC_OK) return r;
   REQUIRE_PTR(scores, "scores");
   REQUIRE_PTR(indices, "indices");
+  if (!topk_rows_supported(dims))
+    return fail(IDXC_ERR_UNSUPPORTED, "rows of %d scores with k = %d exceed the two-stage top-k",
+                dims->Lk, dims->k);
+  const size_t need = topk_part_bytes(dims->B * dims->Lq, dims->Lk, dims->k);
+  if (need > 0) {
+    REQUIRE_PTR(workspace, "workspace");
+    if (workspace_bytes < need)
+      return fail(IDXC_ERR_INVALID_ARG, "workspace of %zu bytes is below the minimum %zu",
+                  workspace_bytes, need);
+  }
   TopkArgs ta{};
   ta.scores = scores;
   ta.Lq = dims->Lq;
@@ -280,6 +331,7 @@ int idxc_topk(const float* scores, const idxc_dims* dims, int32_t* indices, void
   ta.rows = dims->B * dims->Lq;
   ta.k = dims->k;
   ta.out = indices;
+  set_parts(ta, static_cast<uint8_t*>(workspace), dims);
   return hip_status(launch_topk(ta, static_cast<hipStream_t>(hip_stream)), "topk launch");
 }
 
@@ -294,6 +346,9 @@ int idxc_indexer_topk(const void* q_idx, const void* k_idx, const void* w,
   REQUIRE_PTR(workspace, "workspace");
   REQUIRE_PTR(indices, "indices");
   const Plan p = plan_for(dims);
+  if (p.split && !topk_rows_supported(dims))
+    return fail(IDXC_ERR_UNSUPPORTED, "Lk = %d with k = %d exceeds the two-stage top-k", dims->Lk,
+                dims->k);
   if (workspace_bytes < p.min_bytes)
     return fail(IDXC_ERR_INVALID_ARG, "workspace of %zu bytes is below the minimum %zu",
                 workspace_bytes, p.min_bytes);
@@ -302,8 +357,17 @@ int idxc_indexer_topk(const void* q_idx, const void* k_idx, const void* w,
                     "indexer_topk launch");
 }
 
+int idxc_sparse_attn_workspace_bytes(const idxc_dims* dims, size_t* bytes) {
+  int r = check_dims(dims, 2 | 4);
+  if (r != IDXC_OK) return r;
+  if (bytes == nullptr) return fail(IDXC_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = attn_workspace_bytes(dims->B, dims->Lq, dims->H, dims->D, dims->k);
+  return ok();
+}
+
 int idxc_sparse_attn(const void* q, const void* k, const void* v, const int32_t* indices,
-                     const idxc_dims* dims, float scale, void* out, void* hip_stream) {
+                     const idxc_dims* dims, float scale, void* workspace, size_t workspace_bytes,
+                     void* out, void* hip_stream) {
   int r = check_dims(dims, 2 | 4);
   if (r != IDXC_OK) return r;
   REQUIRE_PTR(q, "q");
@@ -312,7 +376,18 @@ int idxc_sparse_attn(const void* q, const void* k, const void* v, const int32_t*
   REQUIRE_PTR(indices, "indices");
   REQUIRE_PTR(out, "out");
   if (!(scale == scale)) return fail(IDXC_ERR_INVALID_ARG, "scale is NaN");
-  return hip_status(launch_sparse_attn(attn_args(q, k, v, indices, dims, scale, out),
+  void* ws = nullptr;
+  if (workspace != nullptr) {
+    if (!aligned16(workspace)) return fail(IDXC_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    const size_t need = attn_workspace_bytes(dims->B, dims->Lq, dims->H, dims->D, dims->k);
+    if (need > 0) {
+      if (workspace_bytes < need)
+        return fail(IDXC_ERR_INVALID_ARG, "workspace of %zu bytes is below the %zu needed",
+                    workspace_bytes, need);
+      ws = workspace;
+    }
+  }
+  return hip_status(launch_sparse_attn(attn_args(q, k, v, indices, dims, scale, out, ws),
                                        static_cast<hipStream_t>(hip_stream)),
                     "sparse_attn launch");
 }
@@ -332,7 +407,10 @@ int idxc_layer_stack_forward(const char* pattern, int32_t n_layers, const idxc_l
   if (debug_indices != nullptr && !aligned16(debug_indices))
     return fail(IDXC_ERR_INVALID_ARG, "debug_indices is not 16-byte aligned");
   if (!(scale == scale)) return fail(IDXC_ERR_INVALID_ARG, "scale is NaN");
-  const Plan p = plan_for(dims);
+  const Plan p = plan_for(dims, true);
+  if (p.split && !topk_rows_supported(dims))
+    return fail(IDXC_ERR_UNSUPPORTED, "Lk = %d with k = %d exceeds the two-stage top-k", dims->Lk,
+                dims->k);
   if (workspace_bytes < p.min_bytes)
     return fail(IDXC_ERR_INVALID_ARG, "workspace of %zu bytes is below the minimum %zu",
                 workspace_bytes, p.min_bytes);
@@ -371,7 +449,8 @@ int idxc_layer_stack_forward(const char* pattern, int32_t n_layers, const idxc_l
       }
       ++calls;
     }
-    hipError_t e = launch_sparse_attn(attn_args(L.q, L.k, L.v, index_cache, dims, scale, L.out), st);
+    hipError_t e = launch_sparse_attn(
+        attn_args(L.q, L.k, L.v, index_cache, dims, scale, L.out, workspace), st);
     if (e != hipSuccess) {
       *indexer_calls = calls;
       return hip_status(e, "stack attention launch");

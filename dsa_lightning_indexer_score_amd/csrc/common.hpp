@@ -43,6 +43,13 @@ __device__ __forceinline__ float pair_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// max(x, 0) for a finite float, on its bit pattern: non-negative floats are
+// non-negative ints, negative floats (and -0.0) are negative ints, so an
+// integer max with 0 is an exact ReLU that returns +0.0 for x <= 0.
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }

@@ -33,72 +33,122 @@ __device__ __forceinline__ void wave_mem_sync() {
 // ---------------------------------------------------------------------------
 // Candidate buffer compaction (one wave, one query).
 //
-// buf[0..n) holds (score bits, position) pairs in increasing position order.
-// Keeps exactly the k best under (score desc, position asc), stably, and
+// buf[0..n) holds (order key, position) pairs in increasing position order.
+// Keeps exactly the k best under (key desc, position asc), stably, and
 // returns the order key of the k-th best in *tkey: every later key position
 // is larger than all buffered ones, so it can only enter the top-k with a
-// strictly larger order key. Radix select over the 32-bit order keys, 8 bits
-// per pass, with a 256-bin histogram in this wave's LDS slice.
+// strictly larger order key. Radix select over the key bits below the
+// highest bit in which the keys differ, 11 bits per pass, with a 2048-bin
+// histogram in `hist` (this wave's 8 KB of LDS). Global loads are batched.
 // ---------------------------------------------------------------------------
+constexpr int kCompactBins = 2048;
+
 __device__ void wave_compact(u32x2* __restrict__ buf, int& n, int k, uint32_t& tkey,
                              uint32_t* hist) {
+  constexpr int kBatch = 8;  // loads in flight per lane
   const int lane = lane_id();
   wave_mem_sync();
-  uint32_t prefix = 0, pmask = 0;
+  // bits shared by every key
+  const uint32_t first = buf[0].x;
+  uint32_t diff = 0u;
+  for (int base = 0; base < n; base += kWave * kBatch) {
+    uint32_t keys[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int e = base + j * kWave + lane;
+      keys[j] = e < n ? buf[e].x : first;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) diff |= keys[j] ^ first;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) diff |= __shfl_xor(diff, off, kWave);
+
+  uint32_t prefix = first, pmask = 0xFFFFFFFFu;
   int rem = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int b = lane; b < 256; b += kWave) hist[b] = 0u;
-    wave_mem_sync();
-    for (int e = lane; e < n; e += kWave) {
-      uint32_t key = order_key(__uint_as_float(buf[e].x));
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+  if (diff != 0u) {
+    const int top = 31 - __builtin_clz(diff);  // highest differing bit
+    pmask = (top == 31) ? 0u : (0xFFFFFFFFu << (top + 1));
+    prefix = first & pmask;
+    int shift = top + 1;
+    while (shift > 0) {
+      const int nbits = min(11, shift);
+      shift -= nbits;
+      const int nbins = 1 << nbits;
+      const uint32_t dmask = (uint32_t)nbins - 1u;
+      for (int b = lane; b < nbins; b += kWave) hist[b] = 0u;
+      wave_mem_sync();
+      for (int base = 0; base < n; base += kWave * kBatch) {
+        uint32_t keys[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int e = base + j * kWave + lane;
+          keys[j] = e < n ? buf[e].x : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int e = base + j * kWave + lane;
+          if (e < n && (keys[j] & pmask) == prefix)
+            atomicAdd(&hist[(keys[j] >> shift) & dmask], 1u);
+        }
+      }
+      wave_mem_sync();
+      // lane owns bins [hi - bpl + 1, hi], hi = nbins - 1 - lane * bpl (descending)
+      const int bpl = nbins >= kWave ? nbins / kWave : 1;
+      const int hi = nbins - 1 - lane * bpl;
+      int local = 0;
+      if (hi >= 0)
+        for (int q = 0; q < bpl; ++q) local += (int)hist[hi - q];
+      const int incl = wave_incl_scan(local);
+      const int excl = incl - local;
+      const int src = __builtin_ctzll(ballot(incl >= rem));
+      int bin = 0, above = 0;
+      if (lane == src) {
+        int acc = excl;
+        for (int q = 0; q < bpl; ++q) {
+          const int c = (int)hist[hi - q];
+          if (acc + c >= rem) {
+            bin = hi - q;
+            above = acc;
+            break;
+          }
+          acc += c;
+        }
+      }
+      bin = __shfl(bin, src, kWave);
+      above = __shfl(above, src, kWave);
+      prefix |= ((uint32_t)bin) << shift;
+      pmask |= dmask << shift;
+      rem -= above;
+      wave_mem_sync();
     }
-    wave_mem_sync();
-    // lane owns bins 255-4l .. 252-4l (descending)
-    const int b0 = 255 - 4 * lane;
-    const int c0 = (int)hist[b0], c1 = (int)hist[b0 - 1], c2 = (int)hist[b0 - 2],
-              c3 = (int)hist[b0 - 3];
-    const int local = c0 + c1 + c2 + c3;
-    const int incl = wave_incl_scan(local);
-    const int excl = incl - local;
-    const uint64_t hit = ballot(incl >= rem);
-    const int src = __builtin_ctzll(hit);
-    int bin = 0, above = 0;
-    if (lane == src) {
-      int acc = excl;
-      if (acc + c0 >= rem) { bin = b0; above = acc; }
-      else if (acc + c0 + c1 >= rem) { bin = b0 - 1; above = acc + c0; }
-      else if (acc + c0 + c1 + c2 >= rem) { bin = b0 - 2; above = acc + c0 + c1; }
-      else { bin = b0 - 3; above = acc + c0 + c1 + c2; }
-    }
-    bin = __shfl(bin, src, kWave);
-    above = __shfl(above, src, kWave);
-    prefix |= ((uint32_t)bin) << shift;
-    pmask |= 255u << shift;
-    rem -= above;
-    wave_mem_sync();
   }
   // prefix = order key of the k-th best; keep all larger keys and the first
   // `rem` entries equal to it (lowest positions: the buffer is position-sorted).
+  // Windows are read a batch ahead of the in-place writes, which never pass
+  // the read position.
   int out = 0, eq_seen = 0;
-  for (int base = 0; base < n; base += kWave) {
-    const int e = base + lane;
-    u32x2 v = {0u, 0u};
-    uint32_t key = 0u;
-    if (e < n) {
-      v = buf[e];
-      key = order_key(__uint_as_float(v.x));
+  for (int base = 0; base < n; base += kWave * kBatch) {
+    u32x2 v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int e = base + j * kWave + lane;
+      v[j] = e < n ? buf[e] : u32x2{0u, 0u};
     }
-    const bool gt = (e < n) && key > prefix;
-    const bool eq = (e < n) && key == prefix;
-    const uint64_t me = ballot(eq);
-    const int eqr = eq_seen + lanes_below(me);
-    const bool keep = gt || (eq && eqr < rem);
-    const uint64_t mk = ballot(keep);
-    wave_mem_sync();  // all lanes have read this window before any write
-    if (keep) buf[out + lanes_below(mk)] = v;
-    out += popc64(mk);
-    eq_seen += popc64(me);
+    wave_mem_sync();
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int e = base + j * kWave + lane;
+      const bool gt = (e < n) && v[j].x > prefix;
+      const bool eq = (e < n) && v[j].x == prefix;
+      const uint64_t me = ballot(eq);
+      const int eqr = eq_seen + lanes_below(me);
+      const bool keep = gt || (eq && eqr < rem);
+      const uint64_t mk = ballot(keep);
+      if (keep) buf[out + lanes_below(mk)] = v[j];
+      out += popc64(mk);
+      eq_seen += popc64(me);
+    }
   }
   wave_mem_sync();
   n = out;
@@ -107,12 +157,37 @@ __device__ void wave_compact(u32x2* __restrict__ buf, int& n, int k, uint32_t& t
 
 // ---------------------------------------------------------------------------
 // Row-stationary kernel: a workgroup owns 8 consecutive query rows (one per
-// wave) and streams all their causal keys through LDS in 64-key tiles.
+// wave) and streams all their causal keys through LDS in 64-key tiles, two
+// tiles ahead.
 //   MODE 0: write scores[b, i, 0..Lk) (score for s <= t, -inf beyond).
-//   MODE 1: append (score, s) with order key above the query's threshold to
-//           cand[row*cap ..], compacting to the k best when full; the final
-//           count goes to cand_count[row].
+//   MODE 1: append (order key, s) for keys at or above the row's threshold to
+//           cand[row*cap ..] (position order); the final count goes to
+//           cand_count[row].
+//
+// MODE 1 threshold. Rows longer than the candidate capacity first score a
+// stratified sample of their keys: up to 32 tiles of 64 consecutive keys
+// spread evenly over [0, t_first] (t_first = the workgroup's first row), run
+// through the same pipeline before the key sweep; the tile count grows with
+// the row length so that about kSampleHits sampled keys land above the
+// threshold. A row's threshold is the m-th largest sampled order key, m
+// chosen so that about kSampleSlack * k keys of the row are expected at or
+// above it. The threshold is only a filter:
+//  * if the buffer still overflows, it is compacted to the exact k best seen
+//    so far (wave_compact) and the threshold rises to the k-th of them;
+//  * if a row ends with fewer than k candidates and never compacted, keys of
+//    its top-k may have been filtered out, so the workgroup sweeps the keys
+//    again for that row without a threshold.
+// Otherwise the buffer holds every key at or above the threshold, at least k
+// of them, hence the whole top-k. At the end each row's buffer is compacted
+// to exactly its k best, so the selection kernel only has to sort them.
 // ---------------------------------------------------------------------------
+constexpr int kSampleTiles = 32;  // at most
+constexpr int kSampleKeys = kSampleTiles * kKeyTile;
+constexpr float kSampleSlack = 2.5f;
+// expected sampled keys at or above the threshold; the threshold's rank in the
+// row then has a relative spread of about 1/sqrt(kSampleHits)
+constexpr float kSampleHits = 100.0f;
+
 template <int DI, int HB, int MODE>
 __global__ __launch_bounds__(kRowWaves * kWave, 1)
 void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
@@ -129,7 +204,8 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
   constexpr int CPT = (TILE_CHUNKS + THREADS - 1) / THREADS;  // chunks per thread
 
   __shared__ __attribute__((aligned(16))) uint8_t tile_lds[2][kKeyTile * ROW_BYTES];
-  __shared__ uint32_t hist_lds[MODE == 1 ? kRowWaves * 256 : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t samp_lds[MODE == 1 ? kRowWaves * kSampleKeys : 4];
+  __shared__ int rescan_lds;
 
   const int nqb = (Lq + kRowWaves - 1) / kRowWaves;
   // longest rows first: block 0 takes the last query block of every batch
@@ -140,6 +216,7 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
   const int i_row = qb * kRowWaves + wave;
   const bool active = i_row < Lq;
   const int t = q_pos0 + i_row;
+  const int t_first = q_pos0 + qb * kRowWaves;
   const int last_row = min(qb * kRowWaves + kRowWaves - 1, Lq - 1);
   const int t_last = q_pos0 + last_row;
   const int ntiles = t_last / kKeyTile + 1;
@@ -170,22 +247,22 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
 
   const uint16_t* kbase = k_idx + (size_t)b * Lk * DI;
 
-  // --- cooperative tile load: global -> registers -> swizzled LDS
-  u32x4 pref[CPT];
-  auto load_tile = [&](int j) {
+  // --- cooperative tile load: global -> registers -> swizzled LDS. Two tiles
+  // are in flight in registers (pa: the tile two ahead, pb: the next one).
+  u32x4 pa[CPT], pb[CPT];
+  auto load_tile = [&](int s_begin, u32x4* dst) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int chunk = threadIdx.x + c * THREADS;
-      const int r = chunk / NCH;
-      const int s = j * kKeyTile + r;
+      const int s = s_begin + chunk / NCH;
       if (chunk < TILE_CHUNKS && s < Lk) {
-        pref[c] = *reinterpret_cast<const u32x4*>(kbase + (size_t)s * DI + (chunk % NCH) * 8);
+        dst[c] = *reinterpret_cast<const u32x4*>(kbase + (size_t)s * DI + (chunk % NCH) * 8);
       } else {
-        pref[c] = u32x4{0u, 0u, 0u, 0u};
+        dst[c] = u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, const u32x4* src) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int chunk = threadIdx.x + c * THREADS;
@@ -193,84 +270,148 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
         const int r = chunk / NCH;
         const int cc = chunk % NCH;
         *reinterpret_cast<u32x4*>(&tile_lds[buf][r * ROW_BYTES + ((cc ^ (r % NCH)) * 16)]) =
-            pref[c];
+            src[c];
       }
     }
+  };
+  // scores of this wave's row against the 64 keys of LDS tile `buf`; lane l
+  // gets key l of the tile
+  auto tile_scores = [&](int buf) {
+    const uint8_t* tl = tile_lds[buf];
+    float sc[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int r = nb * 32 + (lane & 31);
+      bf16x8 b_op[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int c = ks * 2 + (lane >> 5);
+        b_op[ks] = *reinterpret_cast<const bf16x8*>(&tl[r * ROW_BYTES + ((c ^ (r % NCH)) * 16)]);
+      }
+      float part0 = 0.0f, part1 = 0.0f;
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = mfma32(a_op[hb][ks], b_op[ks], acc);
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          part0 = fmaf(wv[hb][i], relu_bits(acc[i]), part0);
+          part1 = fmaf(wv[hb][i + 1], relu_bits(acc[i + 1]), part1);
+        }
+      }
+      sc[nb] = pair_sum(part0 + part1);
+    }
+    return ((lane < 32) ? sc[0] : sc[1]) + 0.0f;
   };
 
   // --- candidate state (MODE 1)
   int n_cand = 0;
-  uint32_t tkey = 0u;
+  uint32_t tkey = 0u;  // keep keys > tkey
+  bool compacted = false;
   u32x2* my_cand = (MODE == 1) ? cand + row * (size_t)cap : nullptr;
-  uint32_t* my_hist = (MODE == 1) ? hist_lds + wave * 256 : nullptr;
+  uint32_t* my_samp = (MODE == 1) ? samp_lds + wave * kSampleKeys : nullptr;
   float* my_scores = (MODE == 0) ? scores + row * (size_t)Lk : nullptr;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    if (j + 1 < ntiles) load_tile(j + 1);
-    const int tile_s0 = j * kKeyTile;
-    if (active && tile_s0 <= t) {
-      const uint8_t* tl = tile_lds[j & 1];
-      float sc[2];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int r = nb * 32 + (lane & 31);
-        bf16x8 b_op[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int c = ks * 2 + (lane >> 5);
-          b_op[ks] = *reinterpret_cast<const bf16x8*>(&tl[r * ROW_BYTES + ((c ^ (r % NCH)) * 16)]);
-        }
-        float part = 0.0f;
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-          f32x16 acc = {};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) acc = mfma32(a_op[hb][ks], b_op[ks], acc);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) part = fmaf(wv[hb][i], fmaxf(acc[i], 0.0f), part);
-        }
-        part = pair_sum(part);
-        sc[nb] = part;
-      }
-      // lane l now scores key tile_s0 + l
-      const float val = ((lane < 32) ? sc[0] : sc[1]) + 0.0f;
-      const int s = tile_s0 + lane;
-      if (MODE == 0) {
-        if (s < Lk) my_scores[s] = (s <= t) ? val : -INFINITY;
-      } else {
-        bool pass = (s <= t) && order_key(val) > tkey;
-        uint64_t m = ballot(pass);
-        int cnt = popc64(m);
-        if (cnt > 0) {
-          if (n_cand + cnt > cap) {
-            wave_compact(my_cand, n_cand, k, tkey, my_hist);
-            pass = (s <= t) && order_key(val) > tkey;
-            m = ballot(pass);
-            cnt = popc64(m);
-          }
-          if (pass) {
-            my_cand[n_cand + lanes_below(m)] = u32x2{__float_as_uint(val), (uint32_t)s};
-          }
-          n_cand += cnt;
-        }
-      }
-    } else if (MODE == 0 && active) {
-      // a tile wholly above this row's position (the block straddles a tile)
-      const int s = tile_s0 + lane;
-      if (s < Lk) my_scores[s] = -INFINITY;
+  // pass 0: sample tiles (if any) then the causal key sweep; pass 1 (rare):
+  // the sweep again, without threshold, for rows whose sampled threshold
+  // turned out too high
+  bool compute_row = active;
+  for (int pass = 0; pass < (MODE == 1 ? 2 : 1); ++pass) {
+    int nsamp = 0;
+    if (MODE == 1 && pass == 0 && t_first + 1 > cap) {
+      const float tiles = kSampleHits * (float)(t_first + 1) / (kSampleSlack * (float)k * kKeyTile);
+      nsamp = max(4, min(kSampleTiles, (int)ceilf(tiles)));
     }
-    if (j + 1 < ntiles) store_tile((j + 1) & 1);
+    const int nv = nsamp + ntiles;
+    const int span = t_first + 1 - kKeyTile;
+    auto tile_start = [&](int v) {
+      return v < nsamp ? (int)(((long long)v * span) / (nsamp - 1)) : (v - nsamp) * kKeyTile;
+    };
+
+    load_tile(tile_start(0), pa);
+    if (nv > 1) load_tile(tile_start(1), pb);
+    store_tile(0, pa);
     __syncthreads();
+
+    for (int v = 0; v < nv; ++v) {
+      // pb holds tile v+1 (in flight); fetch tile v+2 into pa (tile v is in LDS)
+      if (v + 2 < nv) load_tile(tile_start(v + 2), pa);
+      if (MODE == 1 && v == nsamp && nsamp > 0 && compute_row) {
+        // threshold = m-th largest sampled order key (binary search on bits)
+        const int nkeys = nsamp * kKeyTile;
+        const float want = kSampleSlack * (float)k * (float)nkeys / (float)(t + 1);
+        const int m = max(1, min(nkeys, (int)ceilf(want)));
+        uint32_t T = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t candT = T | (1u << bit);
+          int c = 0;
+          for (int e = lane * 4; e < nkeys; e += kWave * 4) {
+            const u32x4 kv = *reinterpret_cast<const u32x4*>(my_samp + e);
+            c += (kv[0] >= candT) + (kv[1] >= candT) + (kv[2] >= candT) + (kv[3] >= candT);
+          }
+          if (wave_sum(c) >= m) T = candT;
+        }
+        tkey = T - 1u;  // keep keys >= T (finite scores have keys > 0)
+      }
+      const int tile_s0 = tile_start(v);
+      if (v < nsamp) {
+        // sampled keys are all <= t_first <= t
+        if (compute_row) my_samp[v * kKeyTile + lane] = order_key(tile_scores(v & 1));
+      } else if (compute_row && tile_s0 <= t) {
+        const float val = tile_scores(v & 1);
+        const int s = tile_s0 + lane;
+        if (MODE == 0) {
+          if (s < Lk) my_scores[s] = (s <= t) ? val : -INFINITY;
+        } else {
+          const uint32_t key = order_key(val);
+          bool pass_key = (s <= t) && key > tkey;
+          uint64_t m = ballot(pass_key);
+          int cnt = popc64(m);
+          if (cnt > 0) {
+            if (n_cand + cnt > cap) {
+              wave_compact(my_cand, n_cand, k, tkey, my_samp);
+              compacted = true;
+              pass_key = (s <= t) && key > tkey;
+              m = ballot(pass_key);
+              cnt = popc64(m);
+            }
+            if (pass_key) my_cand[n_cand + lanes_below(m)] = u32x2{key, (uint32_t)s};
+            n_cand += cnt;
+          }
+        }
+      } else if (MODE == 0 && active) {
+        // a tile wholly above this row's position (the block straddles a tile)
+        const int s = tile_s0 + lane;
+        if (s < Lk) my_scores[s] = -INFINITY;
+      }
+      if (v + 1 < nv) store_tile((v + 1) & 1, pb);
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) pb[c] = pa[c];
+      __syncthreads();
+    }
+
+    if (MODE == 0 || nsamp == 0) break;
+    // rows whose filtered buffer may miss part of the top-k sweep again
+    const bool redo = compute_row && !compacted && n_cand < k;
+    if (threadIdx.x == 0) rescan_lds = 0;
+    __syncthreads();
+    if (redo && lane == 0) atomicOr(&rescan_lds, 1);
+    __syncthreads();
+    if (rescan_lds == 0) break;
+    compute_row = redo;
+    if (redo) {
+      n_cand = 0;
+      tkey = 0u;
+    }
   }
 
   if (!active) return;
   if (MODE == 0) {
     for (int s = ntiles * kKeyTile + lane; s < Lk; s += kWave) my_scores[s] = -INFINITY;
   } else {
+    // exactly the k best (the sample slice is free again)
+    if (n_cand > k) wave_compact(my_cand, n_cand, k, tkey, my_samp);
     if (lane == 0) cand_count[row] = n_cand;
   }
 }
@@ -340,16 +481,19 @@ void indexer_split_kernel(const uint16_t* __restrict__ q_idx,
   load_b(s_begin, cur);
   for (int s0 = s_begin; s0 < s_end; s0 += 32) {
     if (s0 + 32 < s_end) load_b(s0 + 32, nxt);
-    float part = 0.0f;
+    float part0 = 0.0f, part1 = 0.0f;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       f32x16 acc = {};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) acc = mfma32(a_op[hb][ks], cur[ks], acc);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) part = fmaf(wv[hb][i], fmaxf(acc[i], 0.0f), part);
+      for (int i = 0; i < 16; i += 2) {
+        part0 = fmaf(wv[hb][i], relu_bits(acc[i]), part0);
+        part1 = fmaf(wv[hb][i + 1], relu_bits(acc[i + 1]), part1);
+      }
     }
-    part = pair_sum(part);
+    const float part = pair_sum(part0 + part1);
     const int s = s0 + lane;
     if (lane < 32 && s < s_end) srow[s] = (s <= t) ? part + 0.0f : -INFINITY;
 #pragma unroll

@@ -13,7 +13,7 @@ struct IndexerArgs {
   const uint16_t* w;
   int B, Lq, Lk, q_pos0, H_I, d_I, k;
   float* scores;                       // materialising mode
-  uint32_t __attribute__((ext_vector_type(2)))* cand;  // candidate mode
+  uint32_t __attribute__((ext_vector_type(2)))* cand;  // candidate mode: (order key, s)
   int* cand_count;
   int cap;
 };
@@ -25,18 +25,32 @@ hipError_t launch_indexer_scores(const IndexerArgs& a, hipStream_t st);
 hipError_t launch_indexer_candidates(const IndexerArgs& a, hipStream_t st);
 bool indexer_prefers_split(int B, int Lq, int Lk);
 
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kTopkChunk = 8192;       // keys per workgroup for materialised rows
+constexpr int kMaxSegments = 64;       // candidate segments per row
+constexpr int kMaxStagePairs = 16384;  // candidate pairs one workgroup can stage
+
 struct TopkArgs {
-  // source A: materialised scores rows (row r = b*Lq + i, candidates 0..t)
+  // source A: materialised score rows (row r = b*Lq + i, candidates 0..t)
   const float* scores;
   int Lq, Lk, q_pos0;
-  // source B: candidate lists (cand != nullptr)
-  const uint32_t __attribute__((ext_vector_type(2)))* cand;
+  // source B: candidate lists of (order key, position), position-ordered:
+  // nseg segments of seg_cap entries per row, counts in cand_count[row*nseg+s]
+  const u32x2_t* cand;
   const int* cand_count;
-  int cap;
+  int nseg, seg_cap, stage_cap;
+  // scratch for long materialised rows (two-stage selection)
+  u32x2_t* part;
+  int* part_count;
   int rows, k;
   int32_t* out;  // [rows, k]
 };
 
+// Number of stage-1 chunks for materialised rows of length Lk (1 = single pass).
+int topk_row_chunks(int Lk);
+// Scratch bytes launch_topk needs for materialised rows of length Lk.
+size_t topk_part_bytes(int rows, int Lk, int k);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 
 struct AttnArgs {
@@ -47,8 +61,13 @@ struct AttnArgs {
   int B, Lq, Lk, H, D, topk;
   float scale;
   uint16_t* out;
+  void* workspace;  // NULL: one pass per row; else partials of split rows
 };
 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st);
+// Index-list slices per row (1 = no split) and the workspace they need.
+int attn_splits(int B, int Lq, int k);
+size_t attn_part_o_bytes(int B, int Lq, int H, int D, int nsplit);
+size_t attn_workspace_bytes(int B, int Lq, int H, int D, int k);
 
 }  // namespace idxc

@@ -1,18 +1,24 @@
-// Per-query top-k for gfx950: one workgroup per query row.
+// Per-query top-k for gfx950.
 //
 // I_l = TopK(s_l, k) ("IndexCache：跨层复用稀疏注意力的索引", section
 // "从 DSA 的成本分解开始"); the order is fixed as higher score first, then
 // lower position, with -0.0 == +0.0, and rows shorter than k return all of
 // their t+1 positions followed by -1.
 //
-// Scores become order-preserving 32-bit keys. A radix select (8 bits per
-// pass, per-wave LDS histograms) finds the key T of the k-th best entry and
-// how many entries equal to T are still needed; an ordered pass then keeps
+// Scores become order-preserving 32-bit keys. A workgroup stages its input in
+// LDS once (loads batched so many are in flight), then a radix select (8 bits
+// per pass, per-wave LDS histograms) finds the key T of the k-th best entry
+// and how many entries equal to T are still needed; an ordered pass keeps
 // every key above T and the lowest-position entries equal to T; a bitonic sort
-// in LDS of 64-bit (key, ~position) words puts the k winners in order. The
-// input is either a materialised score row (positions implicit) or a candidate
-// list of (score, position) pairs in increasing position order. Rows that fit
-// are staged in LDS once; longer rows are re-read from global memory (L2).
+// in LDS of 64-bit (key, ~position) words puts the k winners in order.
+//
+// Inputs: a materialised score row (positions implicit), or candidate lists of
+// (order key, position) pairs in increasing position order, possibly split in
+// segments whose concatenation is position-ordered. Rows longer than one
+// workgroup's stage are cut into chunks; each chunk's exact top-k is written
+// as a position-ordered candidate segment (stage 1) and a second launch
+// selects from the concatenated segments (stage 2). Every entry of the final
+// top-k is in its chunk's top-k, so the result is the same.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -22,18 +28,23 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kStageBytes = 40 * 1024;
-constexpr int kStageKeys = kStageBytes / 4;      // materialised rows
-constexpr int kStagePairs = kStageBytes / 8;     // candidate lists
 constexpr int kPerThread = 8;                    // ordered pass: consecutive entries
 constexpr int kChunk = kThreads * kPerThread;
+constexpr int kBatch = 8;                        // staged loads in flight per thread
 
 struct Smem {
   uint64_t sortbuf[kMaxK];
   uint32_t hist[kWaves * 256];
   int scan[kWaves];
   int bcast[4];
+  int seg_off[kMaxSegments + 1];
 };
+
+// LDS bytes before the staged input (keeps the stage 16-byte aligned).
+constexpr size_t kSmemBytes = (sizeof(Smem) + 15) / 16 * 16;
+
+enum SrcKind { kSrcRow = 0, kSrcCand = 1 };
+enum OutKind { kOutFinal = 0, kOutPart = 1 };
 
 // Block-wide exclusive prefix sum; *total gets the block total.
 __device__ __forceinline__ int block_excl_scan(int v, int* scan, int* total) {
@@ -54,70 +65,79 @@ __device__ __forceinline__ int block_excl_scan(int v, int* scan, int* total) {
   return off + incl - v;
 }
 
-template <bool CAND>
-struct RowSource {
-  // materialised
-  const float* srow;
-  // candidates
-  const u32x2* crow;
-  // staging
-  const uint32_t* skeys;
-  const u32x2* spairs;
-  bool staged;
-
-  __device__ __forceinline__ void fetch(int e, uint32_t& key, uint32_t& pos) const {
-    if (CAND) {
-      u32x2 v = staged ? spairs[e] : crow[e];
-      key = staged ? v.x : order_key(__uint_as_float(v.x));
-      pos = v.y;
-    } else {
-      key = staged ? skeys[e] : order_key(srow[e]);
-      pos = (uint32_t)e;
-    }
-  }
-};
-
-template <bool CAND>
+// One workgroup = one (row, chunk). SRC kSrcRow: positions [c0, c1) of a score
+// row. SRC kSrcCand: the concatenation of nseg segments of a row.
+template <int SRC, int OUT>
 __global__ __launch_bounds__(kThreads)
-void topk_rows_kernel(TopkArgs a) {
+void topk_kernel(TopkArgs a, int chunk_len, int nchunks) {
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   Smem& sm = *reinterpret_cast<Smem*>(dyn);
-  uint8_t* stage = dyn + sizeof(Smem);
+  uint32_t* skey = reinterpret_cast<uint32_t*>(dyn + kSmemBytes);
+  uint32_t* spos = nullptr;  // SRC kSrcCand: positions after the keys
 
-  const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int k = a.k;
+  const int row = blockIdx.x / nchunks;
+  const int chunk = blockIdx.x % nchunks;
 
+  // ---- stage the input in LDS (keys, and positions for candidate lists)
   int n;
-  RowSource<CAND> src;
-  src.srow = nullptr;
-  src.crow = nullptr;
-  if (CAND) {
-    n = a.cand_count[row];
-    src.crow = a.cand + (size_t)row * a.cap;
-  } else {
+  int pos0 = 0;  // kSrcRow: position of entry 0
+  if (SRC == kSrcRow) {
     const int i = row % a.Lq;
-    n = min(a.q_pos0 + i + 1, a.Lk);
-    src.srow = a.scores + (size_t)row * a.Lk;
-  }
-  src.skeys = reinterpret_cast<const uint32_t*>(stage);
-  src.spairs = reinterpret_cast<const u32x2*>(stage);
-  src.staged = CAND ? (n <= kStagePairs) : (n <= kStageKeys);
-
-  if (src.staged) {
-    if (CAND) {
-      u32x2* sp = reinterpret_cast<u32x2*>(stage);
-      for (int e = tid; e < n; e += kThreads) {
-        u32x2 v = src.crow[e];
-        sp[e] = u32x2{order_key(__uint_as_float(v.x)), v.y};
+    const int len = min(a.q_pos0 + i + 1, a.Lk);
+    pos0 = chunk * chunk_len;
+    n = max(0, min(len, pos0 + chunk_len) - pos0);
+    const float* src = a.scores + (size_t)row * a.Lk + pos0;
+    for (int base = 0; base < n; base += kThreads * kBatch) {
+      float v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int e = base + j * kThreads + tid;
+        v[j] = e < n ? src[e] : 0.0f;
       }
-    } else {
-      uint32_t* sk = reinterpret_cast<uint32_t*>(stage);
-      for (int e = tid; e < n; e += kThreads) sk[e] = order_key(src.srow[e]);
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int e = base + j * kThreads + tid;
+        if (e < n) skey[e] = order_key(v[j]);
+      }
+    }
+  } else {
+    if (tid == 0) {
+      int off = 0;
+      for (int s = 0; s < a.nseg; ++s) {
+        sm.seg_off[s] = off;
+        off += a.cand_count[row * a.nseg + s];
+      }
+      sm.seg_off[a.nseg] = off;
     }
     __syncthreads();
+    n = sm.seg_off[a.nseg];
+    spos = skey + a.stage_cap;
+    for (int s = 0; s < a.nseg; ++s) {
+      const int off = sm.seg_off[s];
+      const int cnt = sm.seg_off[s + 1] - off;
+      const u32x2* src = a.cand + ((size_t)row * a.nseg + s) * a.seg_cap;
+      for (int base = 0; base < cnt; base += kThreads * kBatch) {
+        u32x2 v[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int e = base + j * kThreads + tid;
+          v[j] = e < cnt ? src[e] : u32x2{0u, 0u};
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int e = base + j * kThreads + tid;
+          if (e < cnt) {
+            skey[off + e] = v[j].x;
+            spos[off + e] = v[j].y;
+          }
+        }
+      }
+    }
   }
+  __syncthreads();
 
   // ---- radix select of the k-th best key (only needed when n > k)
   uint32_t prefix = 0u;
@@ -131,8 +151,7 @@ void topk_rows_kernel(TopkArgs a) {
       __syncthreads();
       uint32_t* wh = sm.hist + wave * 256;
       for (int e = tid; e < n; e += kThreads) {
-        uint32_t key, pos;
-        src.fetch(e, key, pos);
+        const uint32_t key = skey[e];
         if ((key & pmask) == prefix) atomicAdd(&wh[(key >> shift) & 255u], 1u);
       }
       __syncthreads();
@@ -154,21 +173,53 @@ void topk_rows_kernel(TopkArgs a) {
     }
   }
 
-  // ---- ordered collection into the sort buffer (entries kept in position
-  // order; equal-to-T entries limited to the `rem` lowest positions)
+  // ---- ordered collection (position order; equal-to-T entries limited to
+  // the `rem` lowest positions)
+  u32x2* part = nullptr;
+  if (OUT == kOutPart) part = a.part + ((size_t)row * nchunks + chunk) * a.k;
   int out_count = 0, eq_seen = 0;
   for (int base = 0; base < n; base += kChunk) {
     uint32_t keys[kPerThread], poss[kPerThread];
     unsigned gt_bits = 0u, eq_bits = 0u;
+    const int e0 = base + tid * kPerThread;
+    if (e0 + kPerThread <= n) {
+      // whole group in range: two 16-byte LDS reads (lanes 32 bytes apart)
+      const u32x4 k0 = *reinterpret_cast<const u32x4*>(skey + e0);
+      const u32x4 k1 = *reinterpret_cast<const u32x4*>(skey + e0 + 4);
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const int e = base + tid * kPerThread + j;
-      keys[j] = 0u;
-      poss[j] = 0u;
-      if (e < n) {
-        src.fetch(e, keys[j], poss[j]);
+      for (int j = 0; j < 4; ++j) {
+        keys[j] = k0[j];
+        keys[4 + j] = k1[j];
+      }
+      if (SRC == kSrcRow) {
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) poss[j] = (uint32_t)(pos0 + e0 + j);
+      } else {
+        const u32x4 p0 = *reinterpret_cast<const u32x4*>(spos + e0);
+        const u32x4 p1 = *reinterpret_cast<const u32x4*>(spos + e0 + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          poss[j] = p0[j];
+          poss[4 + j] = p1[j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kPerThread; ++j) {
         if (select_all || keys[j] > prefix) gt_bits |= 1u << j;
         else if (keys[j] == prefix) eq_bits |= 1u << j;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kPerThread; ++j) {
+        const int e = e0 + j;
+        keys[j] = 0u;
+        poss[j] = 0u;
+        if (e < n) {
+          keys[j] = skey[e];
+          poss[j] = (SRC == kSrcRow) ? (uint32_t)(pos0 + e) : spos[e];
+          if (select_all || keys[j] > prefix) gt_bits |= 1u << j;
+          else if (keys[j] == prefix) eq_bits |= 1u << j;
+        }
       }
     }
     int eq_total;
@@ -187,13 +238,22 @@ void topk_rows_kernel(TopkArgs a) {
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
       if (keep_bits & (1u << j)) {
-        sm.sortbuf[pos++] = (((uint64_t)keys[j]) << 32) | (uint64_t)(~poss[j]);
+        if (OUT == kOutPart) {
+          part[pos] = u32x2{keys[j], poss[j]};
+        } else {
+          sm.sortbuf[pos] = (((uint64_t)keys[j]) << 32) | (uint64_t)(~poss[j]);
+        }
+        ++pos;
       }
     }
     out_count += keep_total;
     eq_seen += eq_total;
   }
   const int kk = out_count;  // == min(k, n)
+  if (OUT == kOutPart) {
+    if (tid == 0) a.part_count[row * nchunks + chunk] = kk;
+    return;
+  }
 
   // ---- bitonic sort, descending, of the kk winners padded to a power of two
   int P = 1;
@@ -222,17 +282,54 @@ void topk_rows_kernel(TopkArgs a) {
   }
 }
 
+template <int SRC, int OUT>
+hipError_t launch_one(const TopkArgs& a, int chunk_len, int nchunks, size_t stage_bytes,
+                      hipStream_t st) {
+  const size_t shmem = kSmemBytes + stage_bytes;
+  auto fn = topk_kernel<SRC, OUT>;
+  if (shmem > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(fn, dim3((unsigned)(a.rows * nchunks)), dim3(kThreads), shmem, st, a,
+                     chunk_len, nchunks);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
-  const size_t shmem = sizeof(Smem) + kStageBytes;
-  dim3 grid((unsigned)a.rows), block(kThreads);
+int topk_row_chunks(int Lk) { return (Lk + kTopkChunk - 1) / kTopkChunk; }
+
+size_t topk_part_bytes(int rows, int Lk, int k) {
+  const int nch = topk_row_chunks(Lk);
+  if (nch <= 1) return 0;
+  return (size_t)rows * nch * k * 8 + (size_t)rows * nch * 4 + 256;
+}
+
+hipError_t launch_topk(const TopkArgs& a0, hipStream_t st) {
+  TopkArgs a = a0;
   if (a.cand) {
-    hipLaunchKernelGGL(topk_rows_kernel<true>, grid, block, shmem, st, a);
-  } else {
-    hipLaunchKernelGGL(topk_rows_kernel<false>, grid, block, shmem, st, a);
+    // candidate lists (one or more position-ordered segments per row); keys
+    // then positions, each area a multiple of 16 bytes
+    a.stage_cap = (a.stage_cap + 3) / 4 * 4;
+    const size_t stage = (size_t)a.stage_cap * 8;
+    return launch_one<kSrcCand, kOutFinal>(a, 0, 1, stage, st);
   }
-  return hipGetLastError();
+  const int nch = topk_row_chunks(a.Lk);
+  if (nch <= 1) {
+    return launch_one<kSrcRow, kOutFinal>(a, kTopkChunk, 1, (size_t)kTopkChunk * 4, st);
+  }
+  // long rows: exact top-k per chunk, then top-k of the chunks' winners
+  hipError_t e = launch_one<kSrcRow, kOutPart>(a, kTopkChunk, nch, (size_t)kTopkChunk * 4, st);
+  if (e != hipSuccess) return e;
+  TopkArgs b = a;
+  b.cand = a.part;
+  b.cand_count = a.part_count;
+  b.nseg = nch;
+  b.seg_cap = a.k;
+  b.stage_cap = (nch * a.k + 3) / 4 * 4;
+  return launch_one<kSrcCand, kOutFinal>(b, 0, 1, (size_t)b.stage_cap * 8, st);
 }
 
 }  // namespace idxc

@@ -119,12 +119,20 @@ int idxc_indexer_scores(const void* q_idx, const void* k_idx, const void* w,
 /* Per-query top-k of materialised scores ([W] I_l = TopK(s_l, k)). Row (b,i)
  * reads scores[b,i,0..t] only (t = q_pos0 + i) and writes indices[b,i,0..k-1]:
  * the min(k, t+1) best positions sorted by (score desc, position asc), then
- * -1. Uses B, Lq, Lk, q_pos0, k. Bit-exact and deterministic. */
-int idxc_topk(const float* scores, const idxc_dims* dims, int32_t* indices,
-              void* hip_stream);
+ * -1. Uses B, Lq, Lk, q_pos0, k. Bit-exact and deterministic. Rows longer
+ * than 8192 are selected in two stages through a device workspace of at
+ * least idxc_topk_workspace_bytes() bytes (NULL/0 is fine when that is 0);
+ * Lk > 8192 * floor(16384 / k) returns IDXC_ERR_UNSUPPORTED. */
+int idxc_topk(const float* scores, const idxc_dims* dims, void* workspace,
+              size_t workspace_bytes, int32_t* indices, void* hip_stream);
 
-/* Bytes of device workspace that idxc_indexer_topk / idxc_layer_stack_forward
- * need at full speed for these sizes (written to *bytes). Host-only. */
+/* Workspace bytes idxc_topk needs for these sizes (0 when Lk <= 8192).
+ * Host-only. */
+int idxc_topk_workspace_bytes(const idxc_dims* dims, size_t* bytes);
+
+/* Bytes of device workspace for these sizes (written to *bytes), host-only:
+ * with dims->H and dims->D set (> 0), what idxc_layer_stack_forward needs at
+ * full speed; with H = D = 0, what idxc_indexer_topk needs at full speed. */
 int idxc_workspace_bytes(const idxc_dims* dims, size_t* bytes);
 
 /* Fused indexer + top-k: same result as idxc_indexer_scores followed by
@@ -143,10 +151,18 @@ int idxc_indexer_topk(const void* q_idx, const void* k_idx, const void* w,
  * indices[b,i,:] (entries equal to -1 are skipped; every other entry must be
  * in [0, Lk)) of scale * q[b,i,h,:] . k[b,s,:], then the weighted sum of
  * v[b,s,:], written to out[b,i,h,:] as bf16. A row with no valid entry gets
- * zeros. Uses B, Lq, Lk, H, D, k. fp32 softmax and accumulation. */
+ * zeros. Uses B, Lq, Lk, H, D, k. fp32 softmax and accumulation, bf16 P.
+ * workspace (optional, NULL = none): with at least
+ * idxc_sparse_attn_workspace_bytes() bytes, calls with few query rows split
+ * each index list over several workgroups and merge the partial results. */
 int idxc_sparse_attn(const void* q, const void* k, const void* v,
                      const int32_t* indices, const idxc_dims* dims, float scale,
-                     void* out, void* hip_stream);
+                     void* workspace, size_t workspace_bytes, void* out,
+                     void* hip_stream);
+
+/* Workspace bytes that let idxc_sparse_attn split index lists (0 when it
+ * would not split for these sizes). Host-only. */
+int idxc_sparse_attn_workspace_bytes(const idxc_dims* dims, size_t* bytes);
 
 /* The whole hot path over a stack of n_layers layers ([W] state machine,
  * [J] layer loop). The pattern (n_layers chars in {F,S}, first F) is checked
@@ -158,7 +174,8 @@ int idxc_sparse_attn(const void* q, const void* k, const void* v,
  * pointer) receives the number of indexer launches (= number of F layers).
  * debug_indices, if not NULL, is a DEVICE buffer [n_layers, B, Lq, k] that
  * receives each layer's indices (for tests). workspace as for
- * idxc_indexer_topk (see idxc_workspace_bytes). */
+ * idxc_indexer_topk, plus room for attention partials; idxc_workspace_bytes
+ * with H and D set gives the full-speed size. */
 int idxc_layer_stack_forward(const char* pattern, int32_t n_layers,
                              const idxc_layer* layers, const idxc_dims* dims,
                              float scale, int32_t* index_cache, void* workspace,

@@ -96,18 +96,39 @@ def test_indexer_scores_argument_errors(lib):
 
 def test_topk_argument_errors(lib):
     f = lib.idxc_topk
-    assert f(P(), ctypes.byref(_dims(k=0)), P(), None) == _lib.IDXC_ERR_INVALID_ARG
-    assert f(P(), ctypes.byref(_dims(k=4096)), P(), None) == _lib.IDXC_ERR_UNSUPPORTED
-    assert f(None, ctypes.byref(_dims()), P(), None) == _lib.IDXC_ERR_INVALID_ARG
-    assert f(P(), ctypes.byref(_dims()), P(FAKE + 4), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), ctypes.byref(_dims(k=0)), None, 0, P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), ctypes.byref(_dims(k=4096)), None, 0, P(), None) == _lib.IDXC_ERR_UNSUPPORTED
+    assert f(None, ctypes.byref(_dims()), None, 0, P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), ctypes.byref(_dims()), None, 0, P(FAKE + 4), None) == _lib.IDXC_ERR_INVALID_ARG
+    # long rows need the two-stage workspace; too long rows are unsupported
+    long_rows = _dims(Lq=1, Lk=65536, q_pos0=65535, k=2048)
+    n = ctypes.c_size_t(0)
+    assert lib.idxc_topk_workspace_bytes(ctypes.byref(long_rows), ctypes.byref(n)) == 0
+    assert n.value >= 8 * 2048 * 8
+    assert f(P(), ctypes.byref(long_rows), None, 0, P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), ctypes.byref(long_rows), P(), n.value - 1, P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    too_long = _dims(Lq=1, Lk=65537, q_pos0=65536, k=2048)
+    assert f(P(), ctypes.byref(too_long), P(), 1 << 30, P(), None) == _lib.IDXC_ERR_UNSUPPORTED
+    short = _dims(Lq=1, Lk=8192, q_pos0=8191, k=2048)
+    assert lib.idxc_topk_workspace_bytes(ctypes.byref(short), ctypes.byref(n)) == 0
+    assert n.value == 0
 
 
 def test_sparse_attn_argument_errors(lib):
     f = lib.idxc_sparse_attn
     for bad, code in ((dict(D=96), 3), (dict(H=65), 3), (dict(k=0), 1), (dict(B=0), 1)):
-        assert f(P(), P(), P(), P(), ctypes.byref(_dims(**bad)), 0.125, P(), None) == code
-    assert f(P(), None, P(), P(), ctypes.byref(_dims()), 0.125, P(), None) == 1
-    assert f(P(), P(), P(), P(), ctypes.byref(_dims()), float("nan"), P(), None) == 1
+        assert f(P(), P(), P(), P(), ctypes.byref(_dims(**bad)), 0.125, None, 0, P(), None) == code
+    assert f(P(), None, P(), P(), ctypes.byref(_dims()), 0.125, None, 0, P(), None) == 1
+    assert f(P(), P(), P(), P(), ctypes.byref(_dims()), float("nan"), None, 0, P(), None) == 1
+    # few rows: a split needs a workspace; a short one is rejected
+    dec = _dims(B=64, Lq=1, Lk=65536, q_pos0=65535, H=64, D=128, k=2048)
+    n = ctypes.c_size_t(0)
+    assert lib.idxc_sparse_attn_workspace_bytes(ctypes.byref(dec), ctypes.byref(n)) == 0
+    assert n.value > 64 * 64 * 128 * 2
+    assert f(P(), P(), P(), P(), ctypes.byref(dec), 0.1, P(), 64, P(), None) == 1
+    many = _dims(B=1, Lq=32768, Lk=32768, H=64, D=128, k=2048)
+    assert lib.idxc_sparse_attn_workspace_bytes(ctypes.byref(many), ctypes.byref(n)) == 0
+    assert n.value == 0
 
 
 def test_workspace_and_fused_errors(lib):

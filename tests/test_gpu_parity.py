@@ -98,7 +98,9 @@ def test_indexer_scores_split_path_integer_exact():
     ("const", 1, 50, 50, 0, 7),
     ("normal", 1, 40, 5000, 4960, 2048),
     ("ties", 1, 8, 12000, 11992, 2048),     # rows longer than the LDS stage
-    ("normal", 3, 1, 30000, 29999, 2048),   # decode-shaped rows
+    ("normal", 3, 1, 30000, 29999, 2048),   # decode-shaped rows (two-stage)
+    ("ties", 2, 1, 65536, 65535, 2048),     # longest two-stage rows, heavy ties
+    ("normal", 1, 3, 40000, 39997, 300),    # many chunks, small k
     ("normal", 1, 20, 20, 0, 2048),         # every row shorter than k
 ])
 def test_topk_exact(kind, B, Lq, Lk, q_pos0, k):
@@ -134,6 +136,43 @@ def test_indexer_topk_integer_exact(B, L, H_I, d_I, k, small_ws):
     got = idxc.idxc_indexer_topk(cu(q), cu(kk), cu(w), k, workspace=ws)
     torch.cuda.synchronize()
     want = oracle.topk(oracle.indexer_scores(f64(q), f64(kk), f64(w), 0), k, 0)
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
+def test_indexer_topk_threshold_rescan_exact():
+    # A row whose sampled threshold is too high must still come out exact.
+    # With one workgroup of rows at q_pos0 = 7992 the stratified sample
+    # starts with keys [0, 64), [255, 319) and [511, 575); only those keys
+    # score high, so the sample suggests far more high keys than exist
+    # (192 < k) and the kernel has to sweep the row again without a threshold.
+    L, q_pos0, k = 8000, 7992, 256
+    q = torch.ones((1, 8, 1, 32), dtype=torch.bfloat16)
+    kk = torch.ones((1, L, 32), dtype=torch.bfloat16)
+    kk[0, 0:64] = 4.0
+    kk[0, 255:319] = 4.0
+    kk[0, 511:575] = 4.0
+    w = torch.ones((1, 8, 1), dtype=torch.bfloat16)
+    ws = torch.empty(_min_ws(1, 8, k), dtype=torch.uint8, device="cuda")
+    got = idxc.idxc_indexer_topk(cu(q), cu(kk), cu(w), k, q_pos0=q_pos0, workspace=ws)
+    torch.cuda.synchronize()
+    want = oracle.topk(oracle.indexer_scores(f64(q), f64(kk), f64(w), q_pos0), k, q_pos0)
+    assert np.array_equal(got.cpu().numpy(), want)
+    # and with random inputs in the same geometry (threshold usually fine)
+    q, kk, w = gen.indexer_inputs(1, 8, L, 4, 32, kind="int", seed=31, w_kind="quarter")
+    got = idxc.idxc_indexer_topk(cu(q), cu(kk), cu(w), k, q_pos0=q_pos0, workspace=ws)
+    torch.cuda.synchronize()
+    want = oracle.topk(oracle.indexer_scores(f64(q), f64(kk), f64(w), q_pos0), k, q_pos0)
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
+def test_indexer_topk_long_rows_integer_exact():
+    # rows longer than the default candidate capacity (sampled threshold path)
+    L, Lq, k = 20000, 48, 2048
+    q_pos0 = L - Lq
+    q, kk, w = gen.indexer_inputs(1, Lq, L, 64, 128, kind="int", seed=41, w_kind="quarter")
+    got = idxc.idxc_indexer_topk(cu(q), cu(kk), cu(w), k, q_pos0=q_pos0)
+    torch.cuda.synchronize()
+    want = oracle.topk(oracle.indexer_scores(f64(q), f64(kk), f64(w), q_pos0), k, q_pos0)
     assert np.array_equal(got.cpu().numpy(), want)
 
 
@@ -187,6 +226,19 @@ def test_sparse_attn_matches_oracle(B, Lq, Lk, q_pos0, H, D, k, pad):
     err = np.abs(got.float().cpu().numpy() - want).max()
     _say("max abs err %.3e" % err)
     assert err <= ATOL
+
+
+def test_sparse_attn_split_equals_single_pass():
+    B, Lk, H, D, k = 8, 6000, 64, 128, 2048
+    Q, K, V = gen.attn_inputs(B, 1, Lk, H, D, seed=13)
+    idx = gen.index_sets(B, 1, Lk - 1, k, seed=6, pad_frac=0.2)
+    split = idxc.idxc_sparse_attn(cu(Q), cu(K), cu(V), cu(idx), D ** -0.5)
+    single = idxc.idxc_sparse_attn(cu(Q), cu(K), cu(V), cu(idx), D ** -0.5, workspace=None)
+    torch.cuda.synchronize()
+    want = oracle.sparse_attention(f64(Q), f64(K), f64(V), idx.numpy(), D ** -0.5)
+    for got in (split, single):
+        assert np.abs(got.float().cpu().numpy() - want).max() <= ATOL
+    assert (split.float() - single.float()).abs().max().item() <= ATOL
 
 
 def test_sparse_attn_single_key_is_exact_copy():
