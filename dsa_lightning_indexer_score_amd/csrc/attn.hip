@@ -219,12 +219,12 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   }
   __syncthreads();
 
-  for (int j = 0; j < nblk; ++j) {
-    // vm_c: valid slots of block j (in LDS buffer j&1); gb: block j+1 in
-    // flight; ix2/ix3: raw list entries of blocks j+2 and j+3
+  // One 32-key block. g_far receives block j+2, g_next (block j+1) is staged
+  // at the end; the loop alternates the two register sets.
+  auto block = [&](int j, Gather<D, NR>& g_far, Gather<D, NR>& g_next) {
     if (j + 2 < nblk) {
       const int r2 = resolve(ix2, &vm_a);
-      gather(ga, r2);
+      gather(g_far, r2);
     }
     ix2 = ix3;
     ix3 = raw_index(j + 4);
@@ -241,48 +241,63 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     // ---- online softmax in the exp2 domain with a lazily moved maximum
     float x[16];
     float mloc = -INFINITY;
+    if (vm_c == 0xFFFFFFFFu) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const bool ok = (vm_c >> acc_row(i, lane)) & 1u;
-      x[i] = ok ? s[i] * sl2 : -INFINITY;
-      mloc = fmaxf(mloc, x[i]);
+      for (int i = 0; i < 16; ++i) {
+        x[i] = s[i] * sl2;
+        mloc = fmaxf(mloc, x[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bool ok = (vm_c >> acc_row(i, lane)) & 1u;
+        x[i] = ok ? s[i] * sl2 : -INFINITY;
+        mloc = fmaxf(mloc, x[i]);
+      }
     }
     const float mblk = pair_max(mloc);
     const bool move = mblk > m_used + kLazyLog2;
     if (ballot(move)) {
       const float mnew = move ? mblk : m_used;
-      const float alpha = move ? exp2f(m_used - mnew) : 1.0f;  // exp2(-inf) = 0
+      const float alpha = move ? __builtin_amdgcn_exp2f(m_used - mnew) : 1.0f;  // 2^-inf = 0
       lsum *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
       m_used = mnew;
     }
-    bf16x8 pb[2];
+    // x - m_used <= 8 keeps P <= 256; -inf maps to 0
+    const float mu = (m_used == -INFINITY) ? 0.0f : m_used;
+    u32x4 pw[2];
     float psum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = (m_used == -INFINITY) ? 0.0f : exp2f(x[i] - m_used);
-      psum += p;
-      pb[i >> 3][i & 7] = (__bf16)p;
+    for (int i = 0; i < 16; i += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(x[i] - mu);
+      const float p1 = __builtin_amdgcn_exp2f(x[i + 1] - mu);
+      psum += p0 + p1;
+      pw[i >> 3][(i & 7) >> 1] = pack_bf16x2(p0, p1);
     }
     lsum += psum;
     // ---- O^T += V^T . P^T
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kk]);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const bf16x8 va = *reinterpret_cast<const bf16x8*>(
             reinterpret_cast<const uint8_t*>(vt) + vt_off(db * 32 + (lane & 31), 2 * kk + (lane >> 5)));
-        o[db] = mfma32(va, pb[kk], o[db]);
+        o[db] = mfma32(va, pb, o[db]);
       }
     }
     // ---- stage block j+1 into the other buffer (nobody has read it since
     // the barrier that ended block j-1)
-    if (j + 1 < nblk) stage(gb, (j + 1) & 1);
-    gb = ga;
+    if (j + 1 < nblk) stage(g_next, (j + 1) & 1);
     vm_c = vm_b;
     vm_b = vm_a;
     __syncthreads();
+  };
+  for (int j = 0; j < nblk; j += 2) {
+    block(j, ga, gb);
+    if (j + 1 < nblk) block(j + 1, gb, ga);
   }
 
   if (!active || h >= H) return;
@@ -304,10 +319,8 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     for (int g = 0; g < 4; ++g) {
       const int d0 = db * 32 + 8 * g + 4 * (lane >> 5);
       u32x2 pk;
-      pk.x = (uint32_t)f32_to_bf16(o[db][4 * g + 0] * inv) |
-             ((uint32_t)f32_to_bf16(o[db][4 * g + 1] * inv) << 16);
-      pk.y = (uint32_t)f32_to_bf16(o[db][4 * g + 2] * inv) |
-             ((uint32_t)f32_to_bf16(o[db][4 * g + 3] * inv) << 16);
+      pk.x = pack_bf16x2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv);
+      pk.y = pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
       *reinterpret_cast<u32x2*>(orow + d0) = pk;
     }
   }

@@ -61,6 +61,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair (hardware round-to-nearest-even), low = a.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2 h = __builtin_convertvector(f32x2{a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 // Order-preserving map of a finite fp32 to uint32 (larger float -> larger key);
 // -0.0 is mapped like +0.0.
 __device__ __forceinline__ uint32_t order_key(float f) {

@@ -21,7 +21,7 @@ namespace idxc {
 namespace {
 
 constexpr int kRowWaves = 8;          // queries per workgroup (one per wave)
-constexpr int kKeyTile = 64;          // keys per LDS tile (two 32-key N-blocks)
+constexpr int kKeyTile = 128;         // keys per LDS tile (four 32-key N-blocks)
 
 // Wave-level synchronisation point for LDS/global data written by other lanes
 // of the same wave (waits for outstanding memory operations).
@@ -157,15 +157,15 @@ __device__ void wave_compact(u32x2* __restrict__ buf, int& n, int k, uint32_t& t
 
 // ---------------------------------------------------------------------------
 // Row-stationary kernel: a workgroup owns 8 consecutive query rows (one per
-// wave) and streams all their causal keys through LDS in 64-key tiles, two
-// tiles ahead.
+// wave) and streams all their causal keys through LDS in 128-key tiles, one
+// tile ahead.
 //   MODE 0: write scores[b, i, 0..Lk) (score for s <= t, -inf beyond).
 //   MODE 1: append (order key, s) for keys at or above the row's threshold to
 //           cand[row*cap ..] (position order); the final count goes to
 //           cand_count[row].
 //
 // MODE 1 threshold. Rows longer than the candidate capacity first score a
-// stratified sample of their keys: up to 32 tiles of 64 consecutive keys
+// stratified sample of their keys: up to 16 tiles of 128 consecutive keys
 // spread evenly over [0, t_first] (t_first = the workgroup's first row), run
 // through the same pipeline before the key sweep; the tile count grows with
 // the row length so that about kSampleHits sampled keys land above the
@@ -181,7 +181,7 @@ __device__ void wave_compact(u32x2* __restrict__ buf, int& n, int k, uint32_t& t
 // of them, hence the whole top-k. At the end each row's buffer is compacted
 // to exactly its k best, so the selection kernel only has to sort them.
 // ---------------------------------------------------------------------------
-constexpr int kSampleTiles = 32;  // at most
+constexpr int kSampleTiles = 16;  // at most
 constexpr int kSampleKeys = kSampleTiles * kKeyTile;
 constexpr float kSampleSlack = 2.5f;
 // expected sampled keys at or above the threshold; the threshold's rank in the
@@ -247,9 +247,9 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
 
   const uint16_t* kbase = k_idx + (size_t)b * Lk * DI;
 
-  // --- cooperative tile load: global -> registers -> swizzled LDS. Two tiles
-  // are in flight in registers (pa: the tile two ahead, pb: the next one).
-  u32x4 pa[CPT], pb[CPT];
+  // --- cooperative tile load: global -> registers -> swizzled LDS, one tile
+  // ahead of the tile being scored
+  u32x4 pa[CPT];
   auto load_tile = [&](int s_begin, u32x4* dst) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
@@ -274,14 +274,14 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
       }
     }
   };
-  // scores of this wave's row against the 64 keys of LDS tile `buf`; lane l
-  // gets key l of the tile
-  auto tile_scores = [&](int buf) {
+  // scores of this wave's row against keys half*64 .. half*64+63 of LDS tile
+  // `buf`; lane l gets key half*64 + l
+  auto tile_scores = [&](int buf, int half) {
     const uint8_t* tl = tile_lds[buf];
     float sc[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const int r = nb * 32 + (lane & 31);
+      const int r = half * 64 + nb * 32 + (lane & 31);
       bf16x8 b_op[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -321,7 +321,7 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
     int nsamp = 0;
     if (MODE == 1 && pass == 0 && t_first + 1 > cap) {
       const float tiles = kSampleHits * (float)(t_first + 1) / (kSampleSlack * (float)k * kKeyTile);
-      nsamp = max(4, min(kSampleTiles, (int)ceilf(tiles)));
+      nsamp = max(2, min(kSampleTiles, (int)ceilf(tiles)));
     }
     const int nv = nsamp + ntiles;
     const int span = t_first + 1 - kKeyTile;
@@ -330,13 +330,12 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
     };
 
     load_tile(tile_start(0), pa);
-    if (nv > 1) load_tile(tile_start(1), pb);
     store_tile(0, pa);
     __syncthreads();
 
     for (int v = 0; v < nv; ++v) {
-      // pb holds tile v+1 (in flight); fetch tile v+2 into pa (tile v is in LDS)
-      if (v + 2 < nv) load_tile(tile_start(v + 2), pa);
+      // tile v is in LDS buffer v&1; fetch tile v+1 into registers
+      if (v + 1 < nv) load_tile(tile_start(v + 1), pa);
       if (MODE == 1 && v == nsamp && nsamp > 0 && compute_row) {
         // threshold = m-th largest sampled order key (binary search on bits)
         const int nkeys = nsamp * kKeyTile;
@@ -357,37 +356,50 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
       const int tile_s0 = tile_start(v);
       if (v < nsamp) {
         // sampled keys are all <= t_first <= t
-        if (compute_row) my_samp[v * kKeyTile + lane] = order_key(tile_scores(v & 1));
+        if (compute_row) {
+#pragma unroll
+          for (int half = 0; half < 2; ++half)
+            my_samp[v * kKeyTile + half * 64 + lane] = order_key(tile_scores(v & 1, half));
+        }
       } else if (compute_row && tile_s0 <= t) {
-        const float val = tile_scores(v & 1);
-        const int s = tile_s0 + lane;
-        if (MODE == 0) {
-          if (s < Lk) my_scores[s] = (s <= t) ? val : -INFINITY;
-        } else {
-          const uint32_t key = order_key(val);
-          bool pass_key = (s <= t) && key > tkey;
-          uint64_t m = ballot(pass_key);
-          int cnt = popc64(m);
-          if (cnt > 0) {
-            if (n_cand + cnt > cap) {
-              wave_compact(my_cand, n_cand, k, tkey, my_samp);
-              compacted = true;
-              pass_key = (s <= t) && key > tkey;
-              m = ballot(pass_key);
-              cnt = popc64(m);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int s = tile_s0 + half * 64 + lane;
+          if (half == 1 && tile_s0 + 64 > t) {
+            // second half wholly above this row
+            if (MODE == 0 && s < Lk) my_scores[s] = -INFINITY;
+            continue;
+          }
+          const float val = tile_scores(v & 1, half);
+          if (MODE == 0) {
+            if (s < Lk) my_scores[s] = (s <= t) ? val : -INFINITY;
+          } else {
+            const uint32_t key = order_key(val);
+            bool pass_key = (s <= t) && key > tkey;
+            uint64_t m = ballot(pass_key);
+            int cnt = popc64(m);
+            if (cnt > 0) {
+              if (n_cand + cnt > cap) {
+                wave_compact(my_cand, n_cand, k, tkey, my_samp);
+                compacted = true;
+                pass_key = (s <= t) && key > tkey;
+                m = ballot(pass_key);
+                cnt = popc64(m);
+              }
+              if (pass_key) my_cand[n_cand + lanes_below(m)] = u32x2{key, (uint32_t)s};
+              n_cand += cnt;
             }
-            if (pass_key) my_cand[n_cand + lanes_below(m)] = u32x2{key, (uint32_t)s};
-            n_cand += cnt;
           }
         }
       } else if (MODE == 0 && active) {
         // a tile wholly above this row's position (the block straddles a tile)
-        const int s = tile_s0 + lane;
-        if (s < Lk) my_scores[s] = -INFINITY;
-      }
-      if (v + 1 < nv) store_tile((v + 1) & 1, pb);
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) pb[c] = pa[c];
+        for (int half = 0; half < 2; ++half) {
+          const int s = tile_s0 + half * 64 + lane;
+          if (s < Lk) my_scores[s] = -INFINITY;
+        }
+      }
+      if (v + 1 < nv) store_tile((v + 1) & 1, pa);
       __syncthreads();
     }
 

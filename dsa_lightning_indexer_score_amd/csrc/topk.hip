@@ -258,6 +258,67 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks) {
   // ---- bitonic sort, descending, of the kk winners padded to a power of two
   int P = 1;
   while (P < kk) P <<= 1;
+  if (P == kThreads * 8) {
+    // register network: each thread holds 8 consecutive slots; strides 1-4
+    // stay in the thread, 8-256 cross lanes of the wave, only 512 and 1024
+    // go through LDS.
+    __syncthreads();
+    uint64_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int idx = tid * 8 + j;
+      v[j] = idx < kk ? sm.sortbuf[idx] : 0ull;
+    }
+    for (int size = 2; size <= P; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        if (stride >= 8) {
+          uint64_t p[8];
+          if (stride >= 8 * kWave) {
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sm.sortbuf[tid * 8 + j] = v[j];
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p[j] = sm.sortbuf[(tid * 8 + j) ^ stride];
+          } else {
+            const int lx = stride >> 3;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const uint32_t lo = __shfl_xor((uint32_t)v[j], lx, kWave);
+              const uint32_t hi = __shfl_xor((uint32_t)(v[j] >> 32), lx, kWave);
+              p[j] = ((uint64_t)hi << 32) | lo;
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int i = tid * 8 + j;
+            const bool take_max = ((i & stride) == 0) == ((i & size) == 0);
+            v[j] = take_max ? (v[j] > p[j] ? v[j] : p[j]) : (v[j] < p[j] ? v[j] : p[j]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            if ((j & stride) == 0) {
+              const int i = tid * 8 + j;
+              const uint64_t x = v[j], y = v[j + stride];
+              const bool desc = (i & size) == 0;
+              if ((x < y) == desc) {
+                v[j] = y;
+                v[j + stride] = x;
+              }
+            }
+          }
+        }
+      }
+    }
+    int32_t* orow = a.out + (size_t)row * k;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int idx = tid * 8 + j;
+      if (idx < k) orow[idx] = (idx < kk) ? (int32_t)(~(uint32_t)(v[j] & 0xFFFFFFFFull)) : -1;
+    }
+    return;
+  }
   for (int e = kk + tid; e < P; e += kThreads) sm.sortbuf[e] = 0ull;
   __syncthreads();
   for (int size = 2; size <= P; size <<= 1) {

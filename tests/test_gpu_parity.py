@@ -141,16 +141,15 @@ def test_indexer_topk_integer_exact(B, L, H_I, d_I, k, small_ws):
 
 def test_indexer_topk_threshold_rescan_exact():
     # A row whose sampled threshold is too high must still come out exact.
-    # With one workgroup of rows at q_pos0 = 7992 the stratified sample
-    # starts with keys [0, 64), [255, 319) and [511, 575); only those keys
-    # score high, so the sample suggests far more high keys than exist
-    # (192 < k) and the kernel has to sweep the row again without a threshold.
+    # The stratified sample of a long row starts with its first tile of keys
+    # ([0, 128)), and the threshold is about the 100th best sampled score;
+    # when only those 128 keys score high (128 < k), the sample suggests far
+    # more high keys than exist and the kernel has to sweep the row again
+    # without a threshold.
     L, q_pos0, k = 8000, 7992, 256
     q = torch.ones((1, 8, 1, 32), dtype=torch.bfloat16)
     kk = torch.ones((1, L, 32), dtype=torch.bfloat16)
-    kk[0, 0:64] = 4.0
-    kk[0, 255:319] = 4.0
-    kk[0, 511:575] = 4.0
+    kk[0, 0:128] = 4.0
     w = torch.ones((1, 8, 1), dtype=torch.bfloat16)
     ws = torch.empty(_min_ws(1, 8, k), dtype=torch.uint8, device="cuda")
     got = idxc.idxc_indexer_topk(cu(q), cu(kk), cu(w), k, q_pos0=q_pos0, workspace=ws)
