@@ -129,7 +129,7 @@ def attn_flops(cfg):
 # --------------------------------------------------------------------------- #
 # CPU oracle baseline on a bounded sample
 # --------------------------------------------------------------------------- #
-def cpu_baseline(cfg, n_rows=48):
+def cpu_baseline(cfg, n_rows=2048):
     """Time the oracle (as it stands) on n_rows query rows of one F layer and
     one S layer of the prefill stack, then compose the 47-layer stack time."""
     import numpy as np
