@@ -197,7 +197,7 @@ def main():
     layers, sets = build_stack(cfg12, N_SETS)
     log("prefill inputs ready (%d sets, %.1f s)" % (N_SETS, time.perf_counter() - t0))
     ws = torch.empty(idxc.idxc_workspace_bytes(cfg12.B, cfg12.Lq, cfg12.Lk, cfg12.q_pos0,
-                                               cfg12.H_I, cfg12.d_I, cfg12.k),
+                                               cfg12.H_I, cfg12.d_I, cfg12.k, cfg12.H, cfg12.D),
                      dtype=torch.uint8, device="cuda")
     cache = torch.empty((cfg12.B, cfg12.Lq, cfg12.k), dtype=torch.int32, device="cuda")
     call12 = idxc.StackCall(cfg12.pattern, layers, cfg12.k, cfg12.scale, cfg12.q_pos0,
@@ -232,7 +232,7 @@ def main():
         dlayers, dsets = build_stack(d12, N_SETS)
         log("decode inputs ready (%.1f s)" % (time.perf_counter() - t0))
         dws = torch.empty(idxc.idxc_workspace_bytes(d12.B, d12.Lq, d12.Lk, d12.q_pos0, d12.H_I,
-                                                    d12.d_I, d12.k),
+                                                    d12.d_I, d12.k, d12.H, d12.D),
                           dtype=torch.uint8, device="cuda")
         dcache = torch.empty((d12.B, d12.Lq, d12.k), dtype=torch.int32, device="cuda")
         dc12 = idxc.StackCall(d12.pattern, dlayers, d12.k, d12.scale, d12.q_pos0,

@@ -109,28 +109,42 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // must still take one more 64-key tile.
 int min_cap(int k) { return (k + 64 + 63) / 64 * 64; }
 
-// Default candidate capacity: room for the ~2.5k keys a sampled threshold
-// lets through, with margin.
+// Default candidate capacity: room for the ~2k keys a sampled threshold lets
+// through, with a margin of several standard deviations; also the number of
+// candidates the selection kernel stages per row.
 int default_cap(int k) {
-  int cap = 4 * k;
+  int cap = 3 * k;
   if (cap < k + 64) cap = k + 64;
-  if (cap < 8192) cap = 8192;
+  if (cap < 1024) cap = 1024;
   if (cap > kMaxStagePairs) cap = kMaxStagePairs;
   return (cap + 63) / 64 * 64;
 }
 
 struct Plan {
-  bool split;      // materialised scores + top-k (few rows)
+  bool split;      // per-chunk indexer top-k, then selection (few rows)
   size_t bytes;    // workspace needed at full speed
   size_t min_bytes;
 };
 
+// The few-row path writes per-chunk top-k segments that one workgroup per
+// row must be able to stage.
+bool split_topk_fits(const idxc_dims* d) {
+  const long long nch = indexer_split_chunks(d->Lk);
+  return nch <= kMaxSegments && nch * d->k <= kMaxStagePairs;
+}
+
+size_t split_part_bytes(const idxc_dims* d) {
+  const size_t rows = (size_t)d->B * d->Lq;
+  const size_t nch = (size_t)indexer_split_chunks(d->Lk);
+  return align_up(rows * nch * d->k * 8) + align_up(rows * nch * 4);
+}
+
 Plan plan_for(const idxc_dims* d, bool with_attn = false) {
   Plan p;
   const size_t rows = (size_t)d->B * d->Lq;
-  p.split = indexer_prefers_split(d->B, d->Lq, d->Lk);
+  p.split = indexer_prefers_split(d->B, d->Lq, d->Lk) && split_topk_fits(d);
   if (p.split) {
-    p.bytes = align_up(rows * (size_t)d->Lk * 4) + align_up(topk_part_bytes((int)rows, d->Lk, d->k));
+    p.bytes = split_part_bytes(d);
     p.min_bytes = p.bytes;
   } else {
     p.bytes = align_up(rows * 4) + rows * (size_t)default_cap(d->k) * 8;
@@ -197,11 +211,17 @@ hipError_t run_indexer_topk(const void* q_idx, const void* k_idx, const void* w,
   ta.k = d->k;
   ta.out = indices;
   if (plan_for(d).split) {
-    ia.scores = static_cast<float*>(ws);
-    hipError_t e = launch_indexer_scores(ia, st);
+    const int nch = indexer_split_chunks(d->Lk);
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    ia.cand = reinterpret_cast<decltype(ia.cand)>(base);
+    ia.cand_count = reinterpret_cast<int*>(base + align_up((size_t)rows * nch * d->k * 8));
+    hipError_t e = launch_indexer_split_topk(ia, st);
     if (e != hipSuccess) return e;
-    ta.scores = ia.scores;
-    set_parts(ta, static_cast<uint8_t*>(ws) + align_up((size_t)rows * d->Lk * 4), d);
+    ta.cand = ia.cand;
+    ta.cand_count = ia.cand_count;
+    ta.nseg = nch;
+    ta.seg_cap = d->k;
+    ta.stage_cap = nch * d->k;
     return launch_topk(ta, st);
   }
   const int cap = cap_for(d, ws_bytes);
@@ -214,7 +234,7 @@ hipError_t run_indexer_topk(const void* q_idx, const void* k_idx, const void* w,
   ta.cand_count = ia.cand_count;
   ta.nseg = 1;
   ta.seg_cap = cap;
-  ta.stage_cap = d->k;  // the candidate kernel leaves at most k per row
+  ta.stage_cap = cap;
   return launch_topk(ta, st);
 }
 
@@ -346,9 +366,6 @@ int idxc_indexer_topk(const void* q_idx, const void* k_idx, const void* w,
   REQUIRE_PTR(workspace, "workspace");
   REQUIRE_PTR(indices, "indices");
   const Plan p = plan_for(dims);
-  if (p.split && !topk_rows_supported(dims))
-    return fail(IDXC_ERR_UNSUPPORTED, "Lk = %d with k = %d exceeds the two-stage top-k", dims->Lk,
-                dims->k);
   if (workspace_bytes < p.min_bytes)
     return fail(IDXC_ERR_INVALID_ARG, "workspace of %zu bytes is below the minimum %zu",
                 workspace_bytes, p.min_bytes);
@@ -408,9 +425,6 @@ int idxc_layer_stack_forward(const char* pattern, int32_t n_layers, const idxc_l
     return fail(IDXC_ERR_INVALID_ARG, "debug_indices is not 16-byte aligned");
   if (!(scale == scale)) return fail(IDXC_ERR_INVALID_ARG, "scale is NaN");
   const Plan p = plan_for(dims, true);
-  if (p.split && !topk_rows_supported(dims))
-    return fail(IDXC_ERR_UNSUPPORTED, "Lk = %d with k = %d exceeds the two-stage top-k", dims->Lk,
-                dims->k);
   if (workspace_bytes < p.min_bytes)
     return fail(IDXC_ERR_INVALID_ARG, "workspace of %zu bytes is below the minimum %zu",
                 workspace_bytes, p.min_bytes);

@@ -15,6 +15,7 @@
 // chip against a running per-query threshold (candidate mode, see below).
 #include "common.hpp"
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace idxc {
 
@@ -178,12 +179,11 @@ __device__ void wave_compact(u32x2* __restrict__ buf, int& n, int k, uint32_t& t
 //    its top-k may have been filtered out, so the workgroup sweeps the keys
 //    again for that row without a threshold.
 // Otherwise the buffer holds every key at or above the threshold, at least k
-// of them, hence the whole top-k. At the end each row's buffer is compacted
-// to exactly its k best, so the selection kernel only has to sort them.
+// of them, hence the whole top-k; the selection kernel picks the exact k.
 // ---------------------------------------------------------------------------
 constexpr int kSampleTiles = 16;  // at most
 constexpr int kSampleKeys = kSampleTiles * kKeyTile;
-constexpr float kSampleSlack = 2.5f;
+constexpr float kSampleSlack = 2.0f;
 // expected sampled keys at or above the threshold; the threshold's rank in the
 // row then has a relative spread of about 1/sqrt(kSampleHits)
 constexpr float kSampleHits = 100.0f;
@@ -422,8 +422,6 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
   if (MODE == 0) {
     for (int s = ntiles * kKeyTile + lane; s < Lk; s += kWave) my_scores[s] = -INFINITY;
   } else {
-    // exactly the k best (the sample slice is free again)
-    if (n_cand > k) wave_compact(my_cand, n_cand, k, tkey, my_samp);
     if (lane == 0) cand_count[row] = n_cand;
   }
 }
@@ -513,6 +511,123 @@ void indexer_split_kernel(const uint16_t* __restrict__ q_idx,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Split-key kernel with chunk-local top-k (few query rows, e.g. decode): a
+// workgroup owns one query row and an 8192-key chunk (2048 keys per wave,
+// three 32-key blocks in flight per wave), keeps the chunk's order keys in
+// LDS and writes the chunk's exact top-k, in position order, as one
+// candidate segment; a selection launch over the row's segments finishes the
+// row. Every key of the row's top-k is in its chunk's top-k.
+// ---------------------------------------------------------------------------
+constexpr int kDecChunk = 8192;
+constexpr int kDecKeysPerWave = kDecChunk / kSplitWaves;
+
+template <int DI, int HB>
+__global__ __launch_bounds__(kSplitWaves * kWave, 2)
+void indexer_split_topk_kernel(const uint16_t* __restrict__ q_idx,
+                               const uint16_t* __restrict__ k_idx,
+                               const uint16_t* __restrict__ w, int B, int Lq, int Lk,
+                               int q_pos0, int H_I, int k, int nchunks,
+                               u32x2* __restrict__ part, int* __restrict__ part_count) {
+  constexpr int KS = DI / 16;
+  __shared__ __attribute__((aligned(16))) uint32_t skey[kDecChunk];
+  __shared__ SelectSmem sel;
+  const int chunk = blockIdx.x % nchunks;
+  const size_t row = blockIdx.x / nchunks;  // b * Lq + i
+  const int b = (int)(row / Lq);
+  const int i_row = (int)(row % Lq);
+  const int t = q_pos0 + i_row;
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int c0 = chunk * kDecChunk;
+  const int n = max(0, min(t + 1, c0 + kDecChunk) - c0);  // causal keys of this chunk
+
+  bf16x8 a_op[HB][KS];
+  float wv[HB][16];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int h = hb * 32 + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = ks * 2 + (lane >> 5);
+      a_op[hb][ks] = (h < H_I) ? *reinterpret_cast<const bf16x8*>(
+                                     q_idx + (row * H_I + h) * DI + c * 8)
+                               : bf16x8{};
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int hh = hb * 32 + acc_row(i, lane);
+      wv[hb][i] = (hh < H_I) ? bf16_to_f32(w[row * H_I + hh]) : 0.0f;
+    }
+  }
+
+  const uint16_t* kbase = k_idx + (size_t)b * Lk * DI;
+  const int e_begin = wave * kDecKeysPerWave;  // chunk-local
+  const int e_end = min(e_begin + kDecKeysPerWave, n);
+  const int nb = e_end > e_begin ? (e_end - e_begin + 31) / 32 : 0;
+
+  auto load_b = [&](int j, bf16x8* dst) {
+    const int s = c0 + e_begin + j * 32 + (lane & 31);
+    const bool ok = s < Lk;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = ks * 2 + (lane >> 5);
+      dst[ks] = ok ? *reinterpret_cast<const bf16x8*>(kbase + (size_t)s * DI + c * 8) : bf16x8{};
+    }
+  };
+  auto score_block = [&](int j, const bf16x8* bop) {
+    float part0 = 0.0f, part1 = 0.0f;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = mfma32(a_op[hb][ks], bop[ks], acc);
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        part0 = fmaf(wv[hb][i], relu_bits(acc[i]), part0);
+        part1 = fmaf(wv[hb][i + 1], relu_bits(acc[i + 1]), part1);
+      }
+    }
+    const float val = pair_sum(part0 + part1) + 0.0f;
+    const int e = e_begin + j * 32 + lane;
+    if (lane < 32 && e < e_end) skey[e] = order_key(val);
+  };
+
+  bf16x8 b0[KS], b1[KS], b2[KS];
+  if (nb > 0) load_b(0, b0);
+  if (nb > 1) load_b(1, b1);
+  if (nb > 2) load_b(2, b2);
+  for (int j = 0; j < nb; j += 3) {
+    score_block(j, b0);
+    if (j + 3 < nb) load_b(j + 3, b0);
+    if (j + 1 < nb) {
+      score_block(j + 1, b1);
+      if (j + 4 < nb) load_b(j + 4, b1);
+    }
+    if (j + 2 < nb) {
+      score_block(j + 2, b2);
+      if (j + 5 < nb) load_b(j + 5, b2);
+    }
+  }
+  __syncthreads();
+
+  u32x2* seg = part + row * (size_t)nchunks * k + (size_t)chunk * k;
+  const int kk = block_topk_collect<false>(skey, nullptr, c0, n, k, sel,
+                                           [&](int slot, uint32_t key, uint32_t pos) {
+                                             seg[slot] = u32x2{key, pos};
+                                           });
+  if (threadIdx.x == 0) part_count[row * nchunks + chunk] = kk;
+}
+
+template <int DI, int HB>
+hipError_t launch_split_topk(const IndexerArgs& a, hipStream_t st) {
+  const int nchunks = (a.Lk + kDecChunk - 1) / kDecChunk;
+  dim3 grid((unsigned)(nchunks * a.B * a.Lq)), block(kSplitWaves * kWave);
+  hipLaunchKernelGGL((indexer_split_topk_kernel<DI, HB>), grid, block, 0, st, a.q_idx, a.k_idx,
+                     a.w, a.B, a.Lq, a.Lk, a.q_pos0, a.H_I, a.k, nchunks, a.cand, a.cand_count);
+  return hipGetLastError();
+}
+
 template <int DI, int HB>
 hipError_t launch_rows(const IndexerArgs& a, int mode, hipStream_t st) {
   const int nqb = (a.Lq + kRowWaves - 1) / kRowWaves;
@@ -538,11 +653,19 @@ hipError_t launch_split(const IndexerArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// kind: 0 materialised rows, 1 candidate rows, 2 materialised split, 3 split
+// with chunk-local top-k
 template <int DI>
 hipError_t dispatch_hb(const IndexerArgs& a, int kind, hipStream_t st) {
   const int hb = (a.H_I + 31) / 32;
-  if (hb == 1) return kind == 2 ? launch_split<DI, 1>(a, st) : launch_rows<DI, 1>(a, kind, st);
-  return kind == 2 ? launch_split<DI, 2>(a, st) : launch_rows<DI, 2>(a, kind, st);
+  if (hb == 1) {
+    if (kind == 2) return launch_split<DI, 1>(a, st);
+    if (kind == 3) return launch_split_topk<DI, 1>(a, st);
+    return launch_rows<DI, 1>(a, kind, st);
+  }
+  if (kind == 2) return launch_split<DI, 2>(a, st);
+  if (kind == 3) return launch_split_topk<DI, 2>(a, st);
+  return launch_rows<DI, 2>(a, kind, st);
 }
 
 hipError_t dispatch(const IndexerArgs& a, int kind, hipStream_t st) {
@@ -569,6 +692,12 @@ hipError_t launch_indexer_scores(const IndexerArgs& a, hipStream_t st) {
 
 hipError_t launch_indexer_candidates(const IndexerArgs& a, hipStream_t st) {
   return dispatch(a, 1, st);
+}
+
+int indexer_split_chunks(int Lk) { return (Lk + kDecChunk - 1) / kDecChunk; }
+
+hipError_t launch_indexer_split_topk(const IndexerArgs& a, hipStream_t st) {
+  return dispatch(a, 3, st);
 }
 
 }  // namespace idxc

@@ -24,6 +24,10 @@ hipError_t launch_indexer_scores(const IndexerArgs& a, hipStream_t st);
 // the count in cand_count[row].
 hipError_t launch_indexer_candidates(const IndexerArgs& a, hipStream_t st);
 bool indexer_prefers_split(int B, int Lq, int Lk);
+// Few-row path: per (row, 8192-key chunk) exact top-k segments written to
+// cand (segments of k entries, counts in cand_count[row * chunks + chunk]).
+int indexer_split_chunks(int Lk);
+hipError_t launch_indexer_split_topk(const IndexerArgs& a, hipStream_t st);
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 

@@ -1,0 +1,218 @@
+// Block-wide exact top-k selection over keys staged in LDS (shared by the
+// selection kernels and the decode indexer). Internal to libidxc.
+//
+// Input: n order-preserving 32-bit keys skey[0..n) in increasing position
+// order, with positions spos[e] (explicit) or pos0 + e (implicit). Output:
+// the min(k, n) best entries under (key desc, position asc), emitted in
+// position order through emit(slot, key, position), slot = 0..min(k,n)-1.
+//
+// Method: the keys lie in [lo, lo + R); each pass histograms them into
+// kSelBins equal-width bins of that range, finds the bin holding the rem-th
+// largest key and narrows the range to it. It ends when the range is one key
+// (ties: keep the `rem` lowest positions of it) or when every key of the bin
+// is needed. An ordered pass (block prefix sums) then emits the winners.
+#pragma once
+
+#include "common.hpp"
+
+namespace idxc {
+
+constexpr int kSelThreads = 256;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kSelBins = 2048;
+constexpr int kSelPerThread = 8;  // ordered pass: consecutive entries per thread
+constexpr int kSelChunk = kSelThreads * kSelPerThread;
+
+struct SelectSmem {
+  uint32_t hist[kSelBins];
+  int scan[kSelWaves];
+  int bcast[4];
+  uint32_t kred[2 * kSelWaves];
+};
+
+// Block-wide exclusive prefix sum (kSelThreads threads); *total = block sum.
+__device__ __forceinline__ int sel_excl_scan(int v, int* scan, int* total) {
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int incl = wave_incl_scan(v);
+  if (lane == kWave - 1) scan[wave] = incl;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    const int s = scan[w];
+    if (w < wave) off += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + incl - v;
+}
+
+template <bool EXPLICIT_POS, typename Emit>
+__device__ int block_topk_collect(const uint32_t* skey, const uint32_t* spos, int pos0, int n,
+                                  int k, SelectSmem& sm, Emit emit) {
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  // ---- select the k-th best key (only needed when n > k). The keys lie in
+  // [lo, lo + R); each pass histograms them into kSelBins equal-width bins of
+  // that range, finds the bin holding the rem-th largest key and narrows the
+  // range to it. It ends when the range is one key (ties: keep the `rem`
+  // lowest positions of it) or when every key of the bin is needed.
+  uint32_t lo = 0u, hi = 0u;  // final key range; keys above hi are all kept
+  int rem = 0;
+  bool take_range = true;  // keep every key of [lo, hi]
+  const bool select_all = n <= k;
+  if (!select_all) {
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    for (int e = tid; e < n; e += kSelThreads) {
+      const uint32_t key = skey[e];
+      kmin = min(kmin, key);
+      kmax = max(kmax, key);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, kWave));
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, kWave));
+    }
+    if (lane_id() == 0) {
+      sm.kred[wave] = kmin;
+      sm.kred[kSelWaves + wave] = kmax;
+    }
+    __syncthreads();
+    kmin = sm.kred[0];
+    kmax = sm.kred[kSelWaves];
+#pragma unroll
+    for (int w = 1; w < kSelWaves; ++w) {
+      kmin = min(kmin, sm.kred[w]);
+      kmax = max(kmax, sm.kred[kSelWaves + w]);
+    }
+    lo = kmin;
+    hi = kmax;
+    rem = k;
+    take_range = false;
+    constexpr int BPT = kSelBins / kSelThreads;  // bins per thread
+    while (hi > lo) {
+      const uint64_t R = (uint64_t)hi - lo + 1ull;
+      for (int b = tid; b < kSelBins; b += kSelThreads) sm.hist[b] = 0u;
+      __syncthreads();
+      for (int e = tid; e < n; e += kSelThreads) {
+        const uint32_t key = skey[e];
+        if (key >= lo && key <= hi)
+          atomicAdd(&sm.hist[(uint32_t)(((uint64_t)(key - lo) * kSelBins) / R)], 1u);
+      }
+      __syncthreads();
+      // thread tid owns bins top - BPT*tid - (0..BPT-1), highest first
+      const int top = kSelBins - 1 - BPT * tid;
+      int cnts[BPT];
+      int local = 0;
+#pragma unroll
+      for (int q = 0; q < BPT; ++q) {
+        cnts[q] = (int)sm.hist[top - q];
+        local += cnts[q];
+      }
+      int total;
+      const int excl = sel_excl_scan(local, sm.scan, &total);
+      if (excl < rem && excl + local >= rem) {
+        int acc = excl;
+#pragma unroll
+        for (int q = 0; q < BPT; ++q) {
+          if (acc < rem && acc + cnts[q] >= rem) {
+            sm.bcast[0] = top - q;
+            sm.bcast[1] = acc;
+            sm.bcast[2] = cnts[q];
+          }
+          acc += cnts[q];
+        }
+      }
+      __syncthreads();
+      const uint64_t bstar = (uint64_t)sm.bcast[0];
+      rem -= sm.bcast[1];
+      const int cnt_b = sm.bcast[2];
+      __syncthreads();
+      // keys of bin b*: key - lo in [ceil(b* R / kSelBins), ceil((b*+1) R / kSelBins) - 1]
+      const uint32_t nlo = lo + (uint32_t)((bstar * R + kSelBins - 1) / kSelBins);
+      const uint32_t nhi = lo + (uint32_t)(((bstar + 1) * R + kSelBins - 1) / kSelBins) - 1u;
+      lo = nlo;
+      hi = nhi;
+      if (cnt_b == rem) {
+        take_range = true;
+        break;
+      }
+    }
+  }
+
+  // ---- ordered collection (position order; equal-to-T entries limited to
+  // the `rem` lowest positions)
+  int out_count = 0, eq_seen = 0;
+  for (int base = 0; base < n; base += kSelChunk) {
+    uint32_t keys[kSelPerThread], poss[kSelPerThread];
+    unsigned gt_bits = 0u, eq_bits = 0u;
+    const int e0 = base + tid * kSelPerThread;
+    if (e0 + kSelPerThread <= n) {
+      // whole group in range: two 16-byte LDS reads (lanes 32 bytes apart)
+      const u32x4 k0 = *reinterpret_cast<const u32x4*>(skey + e0);
+      const u32x4 k1 = *reinterpret_cast<const u32x4*>(skey + e0 + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        keys[j] = k0[j];
+        keys[4 + j] = k1[j];
+      }
+      if (!EXPLICIT_POS) {
+#pragma unroll
+        for (int j = 0; j < kSelPerThread; ++j) poss[j] = (uint32_t)(pos0 + e0 + j);
+      } else {
+        const u32x4 p0 = *reinterpret_cast<const u32x4*>(spos + e0);
+        const u32x4 p1 = *reinterpret_cast<const u32x4*>(spos + e0 + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          poss[j] = p0[j];
+          poss[4 + j] = p1[j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kSelPerThread; ++j) {
+        if (select_all || keys[j] > hi || (take_range && keys[j] >= lo)) gt_bits |= 1u << j;
+        else if (keys[j] >= lo) eq_bits |= 1u << j;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSelPerThread; ++j) {
+        const int e = e0 + j;
+        keys[j] = 0u;
+        poss[j] = 0u;
+        if (e < n) {
+          keys[j] = skey[e];
+          poss[j] = (!EXPLICIT_POS) ? (uint32_t)(pos0 + e) : spos[e];
+          if (select_all || keys[j] > hi || (take_range && keys[j] >= lo)) gt_bits |= 1u << j;
+          else if (keys[j] >= lo) eq_bits |= 1u << j;
+        }
+      }
+    }
+    int eq_total;
+    const int eq_excl = eq_seen + sel_excl_scan(__popc(eq_bits), sm.scan, &eq_total);
+    unsigned keep_bits = gt_bits;
+    int r = eq_excl;
+#pragma unroll
+    for (int j = 0; j < kSelPerThread; ++j) {
+      if (eq_bits & (1u << j)) {
+        if (r < rem) keep_bits |= 1u << j;
+        ++r;
+      }
+    }
+    int keep_total;
+    int pos = out_count + sel_excl_scan(__popc(keep_bits), sm.scan, &keep_total);
+#pragma unroll
+    for (int j = 0; j < kSelPerThread; ++j) {
+      if (keep_bits & (1u << j)) {
+        emit(pos, keys[j], poss[j]);
+        ++pos;
+      }
+    }
+    out_count += keep_total;
+    eq_seen += eq_total;
+  }
+  return out_count;  // == min(k, n)
+}
+
+}  // namespace idxc

@@ -6,11 +6,10 @@
 // their t+1 positions followed by -1.
 //
 // Scores become order-preserving 32-bit keys. A workgroup stages its input in
-// LDS once (loads batched so many are in flight), then a radix select (8 bits
-// per pass, per-wave LDS histograms) finds the key T of the k-th best entry
-// and how many entries equal to T are still needed; an ordered pass keeps
-// every key above T and the lowest-position entries equal to T; a bitonic sort
-// in LDS of 64-bit (key, ~position) words puts the k winners in order.
+// LDS once (loads batched so many are in flight), selects the exact top-k in
+// position order (select.hpp: range-narrowing radix select plus an ordered
+// pass), and a bitonic sort of 64-bit (key, ~position) words puts the k
+// winners in order.
 //
 // Inputs: a materialised score row (positions implicit), or candidate lists of
 // (order key, position) pairs in increasing position order, possibly split in
@@ -21,22 +20,18 @@
 // top-k is in its chunk's top-k, so the result is the same.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace idxc {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kPerThread = 8;                    // ordered pass: consecutive entries
-constexpr int kChunk = kThreads * kPerThread;
-constexpr int kBatch = 8;                        // staged loads in flight per thread
+constexpr int kThreads = kSelThreads;
+constexpr int kBatch = 8;  // staged loads in flight per thread
 
 struct Smem {
   uint64_t sortbuf[kMaxK];
-  uint32_t hist[kWaves * 256];
-  int scan[kWaves];
-  int bcast[4];
+  SelectSmem sel;
   int seg_off[kMaxSegments + 1];
 };
 
@@ -46,23 +41,52 @@ constexpr size_t kSmemBytes = (sizeof(Smem) + 15) / 16 * 16;
 enum SrcKind { kSrcRow = 0, kSrcCand = 1 };
 enum OutKind { kOutFinal = 0, kOutPart = 1 };
 
-// Block-wide exclusive prefix sum; *total gets the block total.
-__device__ __forceinline__ int block_excl_scan(int v, int* scan, int* total) {
-  const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
-  const int incl = wave_incl_scan(v);
-  if (lane == kWave - 1) scan[wave] = incl;
-  __syncthreads();
-  int off = 0, tot = 0;
+// Descending bitonic sort of 2048 64-bit words held 8 per thread (thread t
+// holds slots 8t..8t+7). Strides 1-4 stay in the thread, 8-256 cross lanes of
+// the wave, 512 and 1024 go through LDS. Fully unrolled.
+__device__ __forceinline__ void sort2048_regs(uint64_t (&v)[8], uint64_t* lds, int tid) {
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const int s = scan[w];
-    if (w < wave) off += s;
-    tot += s;
+  for (int size = 2; size <= 2048; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride >= 8) {
+        uint64_t p[8];
+        if (stride >= 8 * kWave) {
+          __syncthreads();
+#pragma unroll
+          for (int j = 0; j < 8; ++j) lds[tid * 8 + j] = v[j];
+          __syncthreads();
+#pragma unroll
+          for (int j = 0; j < 8; ++j) p[j] = lds[(tid * 8 + j) ^ stride];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t lo = __shfl_xor((uint32_t)v[j], stride >> 3, kWave);
+            const uint32_t hi = __shfl_xor((uint32_t)(v[j] >> 32), stride >> 3, kWave);
+            p[j] = ((uint64_t)hi << 32) | lo;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = tid * 8 + j;
+          const bool take_max = ((i & stride) == 0) == ((i & size) == 0);
+          v[j] = take_max ? (v[j] > p[j] ? v[j] : p[j]) : (v[j] < p[j] ? v[j] : p[j]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if ((j & stride) == 0) {
+            const bool desc = ((tid * 8 + j) & size) == 0;
+            const uint64_t x = v[j], y = v[j + stride];
+            if ((x < y) == desc) {
+              v[j] = y;
+              v[j + stride] = x;
+            }
+          }
+        }
+      }
+    }
   }
-  __syncthreads();
-  *total = tot;
-  return off + incl - v;
 }
 
 // One workgroup = one (row, chunk). SRC kSrcRow: positions [c0, c1) of a score
@@ -76,7 +100,6 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks) {
   uint32_t* spos = nullptr;  // SRC kSrcCand: positions after the keys
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
   const int k = a.k;
   const int row = blockIdx.x / nchunks;
   const int chunk = blockIdx.x % nchunks;
@@ -139,117 +162,14 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks) {
   }
   __syncthreads();
 
-  // ---- radix select of the k-th best key (only needed when n > k)
-  uint32_t prefix = 0u;
-  int rem = 0;
-  const bool select_all = n <= k;
-  if (!select_all) {
-    uint32_t pmask = 0u;
-    rem = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int b = tid; b < kWaves * 256; b += kThreads) sm.hist[b] = 0u;
-      __syncthreads();
-      uint32_t* wh = sm.hist + wave * 256;
-      for (int e = tid; e < n; e += kThreads) {
-        const uint32_t key = skey[e];
-        if ((key & pmask) == prefix) atomicAdd(&wh[(key >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      const int bin = 255 - tid;  // descending bins across threads
-      int cnt = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) cnt += (int)sm.hist[w * 256 + bin];
-      int total;
-      const int excl = block_excl_scan(cnt, sm.scan, &total);
-      if (excl < rem && excl + cnt >= rem) {
-        sm.bcast[0] = bin;
-        sm.bcast[1] = excl;
-      }
-      __syncthreads();
-      prefix |= ((uint32_t)sm.bcast[0]) << shift;
-      pmask |= 255u << shift;
-      rem -= sm.bcast[1];
-      __syncthreads();
-    }
-  }
-
-  // ---- ordered collection (position order; equal-to-T entries limited to
-  // the `rem` lowest positions)
   u32x2* part = nullptr;
   if (OUT == kOutPart) part = a.part + ((size_t)row * nchunks + chunk) * a.k;
-  int out_count = 0, eq_seen = 0;
-  for (int base = 0; base < n; base += kChunk) {
-    uint32_t keys[kPerThread], poss[kPerThread];
-    unsigned gt_bits = 0u, eq_bits = 0u;
-    const int e0 = base + tid * kPerThread;
-    if (e0 + kPerThread <= n) {
-      // whole group in range: two 16-byte LDS reads (lanes 32 bytes apart)
-      const u32x4 k0 = *reinterpret_cast<const u32x4*>(skey + e0);
-      const u32x4 k1 = *reinterpret_cast<const u32x4*>(skey + e0 + 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        keys[j] = k0[j];
-        keys[4 + j] = k1[j];
-      }
-      if (SRC == kSrcRow) {
-#pragma unroll
-        for (int j = 0; j < kPerThread; ++j) poss[j] = (uint32_t)(pos0 + e0 + j);
-      } else {
-        const u32x4 p0 = *reinterpret_cast<const u32x4*>(spos + e0);
-        const u32x4 p1 = *reinterpret_cast<const u32x4*>(spos + e0 + 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          poss[j] = p0[j];
-          poss[4 + j] = p1[j];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < kPerThread; ++j) {
-        if (select_all || keys[j] > prefix) gt_bits |= 1u << j;
-        else if (keys[j] == prefix) eq_bits |= 1u << j;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kPerThread; ++j) {
-        const int e = e0 + j;
-        keys[j] = 0u;
-        poss[j] = 0u;
-        if (e < n) {
-          keys[j] = skey[e];
-          poss[j] = (SRC == kSrcRow) ? (uint32_t)(pos0 + e) : spos[e];
-          if (select_all || keys[j] > prefix) gt_bits |= 1u << j;
-          else if (keys[j] == prefix) eq_bits |= 1u << j;
-        }
-      }
-    }
-    int eq_total;
-    const int eq_excl = eq_seen + block_excl_scan(__popc(eq_bits), sm.scan, &eq_total);
-    unsigned keep_bits = gt_bits;
-    int r = eq_excl;
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      if (eq_bits & (1u << j)) {
-        if (r < rem) keep_bits |= 1u << j;
-        ++r;
-      }
-    }
-    int keep_total;
-    int pos = out_count + block_excl_scan(__popc(keep_bits), sm.scan, &keep_total);
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      if (keep_bits & (1u << j)) {
-        if (OUT == kOutPart) {
-          part[pos] = u32x2{keys[j], poss[j]};
-        } else {
-          sm.sortbuf[pos] = (((uint64_t)keys[j]) << 32) | (uint64_t)(~poss[j]);
-        }
-        ++pos;
-      }
-    }
-    out_count += keep_total;
-    eq_seen += eq_total;
-  }
-  const int kk = out_count;  // == min(k, n)
+  uint64_t* sortbuf = sm.sortbuf;
+  const int kk = block_topk_collect<SRC == kSrcCand>(
+      skey, spos, pos0, n, k, sm.sel, [&](int slot, uint32_t key, uint32_t pos) {
+        if (OUT == kOutPart) part[slot] = u32x2{key, pos};
+        else sortbuf[slot] = (((uint64_t)key) << 32) | (uint64_t)(~pos);
+      });
   if (OUT == kOutPart) {
     if (tid == 0) a.part_count[row * nchunks + chunk] = kk;
     return;
@@ -259,9 +179,6 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks) {
   int P = 1;
   while (P < kk) P <<= 1;
   if (P == kThreads * 8) {
-    // register network: each thread holds 8 consecutive slots; strides 1-4
-    // stay in the thread, 8-256 cross lanes of the wave, only 512 and 1024
-    // go through LDS.
     __syncthreads();
     uint64_t v[8];
 #pragma unroll
@@ -269,48 +186,7 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks) {
       const int idx = tid * 8 + j;
       v[j] = idx < kk ? sm.sortbuf[idx] : 0ull;
     }
-    for (int size = 2; size <= P; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        if (stride >= 8) {
-          uint64_t p[8];
-          if (stride >= 8 * kWave) {
-            __syncthreads();
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sm.sortbuf[tid * 8 + j] = v[j];
-            __syncthreads();
-#pragma unroll
-            for (int j = 0; j < 8; ++j) p[j] = sm.sortbuf[(tid * 8 + j) ^ stride];
-          } else {
-            const int lx = stride >> 3;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const uint32_t lo = __shfl_xor((uint32_t)v[j], lx, kWave);
-              const uint32_t hi = __shfl_xor((uint32_t)(v[j] >> 32), lx, kWave);
-              p[j] = ((uint64_t)hi << 32) | lo;
-            }
-          }
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int i = tid * 8 + j;
-            const bool take_max = ((i & stride) == 0) == ((i & size) == 0);
-            v[j] = take_max ? (v[j] > p[j] ? v[j] : p[j]) : (v[j] < p[j] ? v[j] : p[j]);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            if ((j & stride) == 0) {
-              const int i = tid * 8 + j;
-              const uint64_t x = v[j], y = v[j + stride];
-              const bool desc = (i & size) == 0;
-              if ((x < y) == desc) {
-                v[j] = y;
-                v[j + stride] = x;
-              }
-            }
-          }
-        }
-      }
-    }
+    sort2048_regs(v, sm.sortbuf, tid);
     int32_t* orow = a.out + (size_t)row * k;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {

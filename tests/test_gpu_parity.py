@@ -175,6 +175,23 @@ def test_indexer_topk_long_rows_integer_exact():
     assert np.array_equal(got.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("B,Lq,Lk,q_pos0,k", [
+    (3, 1, 40000, 39999, 2048),   # decode rows, ragged last 8192-key chunk
+    (2, 4, 40000, 9000, 2048),    # rows that end in an early chunk
+    (1, 2, 20000, 1000, 2048),    # rows shorter than k: every position, then -1
+    (2, 1, 65536, 65535, 512),    # eight full chunks, small k
+])
+def test_indexer_topk_few_rows_integer_exact(B, Lq, Lk, q_pos0, k):
+    # few query rows over long keys: per-chunk top-k in the indexer, then a
+    # selection over the chunks' winners
+    _say("indexer_topk few rows B=%d Lq=%d Lk=%d q_pos0=%d k=%d" % (B, Lq, Lk, q_pos0, k))
+    q, kk, w = gen.indexer_inputs(B, Lq, Lk, 64, 128, kind="int", seed=43 + Lq, w_kind="quarter")
+    got = idxc.idxc_indexer_topk(cu(q), cu(kk), cu(w), k, q_pos0=q_pos0)
+    torch.cuda.synchronize()
+    want = oracle.topk(oracle.indexer_scores(f64(q), f64(kk), f64(w), q_pos0), k, q_pos0)
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
 def test_indexer_topk_random_overlap_and_determinism():
     B, L, H_I, d_I, k = 1, 1500, 64, 128, 256
     _say("indexer_topk normal L=%d k=%d" % (L, k))
