@@ -43,7 +43,10 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
-    ap.add_argument("--only", default="", help="prefill-12f | prefill-allf | decode (profiling)")
+    ap.add_argument("--only", default="",
+                    help="prefill-12f | prefill-allf | decode | pmc (profiling)")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CMD_F", "CMD_W"),
+                    help="write profiles/hbm_traffic.md from the two counter passes (no GPU)")
     return ap.parse_args()
 
 
@@ -77,18 +80,59 @@ def time_steps(fn, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
-def event_ms(fn, reps):
-    """Average device time of fn() on torch's current stream (HIP events)."""
+def kernel_pass(cfg, layers, ws, cache, steps):
+    """Run the stack layer by layer through the per-layer entry points (the
+    same launches, in the same order, as one stack call) with HIP events on
+    the launch stream around every F layer's indexer + top-k and every
+    attention launch. Returns (mean ms of one indexer + top-k, mean ms of one
+    attention launch, ms per step of the pass)."""
     import torch
+    import dsa_lightning_indexer_score_amd as idxc
     st = torch.cuda.current_stream()
-    fn()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(st)
-    for _ in range(reps):
-        fn()
-    b.record(st)
-    b.synchronize()
-    return a.elapsed_time(b) / reps
+
+    def one_step(events):
+        for l, L in enumerate(layers):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(st)
+            if cfg.pattern[l] == "F":
+                idxc.idxc_indexer_topk(L["q_idx"], L["k_idx"], L["w"], cfg.k, q_pos0=cfg.q_pos0,
+                                       workspace=ws, out=cache)
+            e[1].record(st)
+            idxc.idxc_sparse_attn(L["q"], L["k"], L["v"], cache, cfg.scale, workspace=ws,
+                                  out=L["out"])
+            e[2].record(st)
+            events.append((cfg.pattern[l] == "F", e))
+
+    one_step([])
+    events = []
+    for _ in range(steps):
+        one_step(events)
+    torch.cuda.synchronize()
+    idx = [e[0].elapsed_time(e[1]) for f, e in events if f]
+    att = [e[1].elapsed_time(e[2]) for f, e in events]
+    total = events[0][1][0].elapsed_time(events[-1][1][2])
+    return sum(idx) / len(idx), sum(att) / len(att), total / steps
+
+
+def hbm_traffic(kernel):
+    """Scaled HBM bytes per launch of `kernel` from the committed counter
+    summary, or None when the kernel's sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    for line in open(path):
+        if line.startswith("traffic-json: "):
+            rec = json.loads(line[len("traffic-json: "):]).get(kernel)
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest()[:16] != rec["sha"]:
+        return None
+    return rec["bytes"]
 
 
 # --------------------------------------------------------------------------- #
@@ -129,7 +173,7 @@ def attn_flops(cfg):
 # --------------------------------------------------------------------------- #
 # CPU oracle baseline on a bounded sample
 # --------------------------------------------------------------------------- #
-def cpu_baseline(cfg, n_rows=2048):
+def cpu_baseline(cfg, n_rows=4096):
     """Time the oracle (as it stands) on n_rows query rows of one F layer and
     one S layer of the prefill stack, then compose the 47-layer stack time."""
     import numpy as np
@@ -174,8 +218,136 @@ def cpu_baseline(cfg, n_rows=2048):
 
 
 # --------------------------------------------------------------------------- #
+# counter passes: rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -- python3 bench.py --only pmc
+# --------------------------------------------------------------------------- #
+CAL_BYTES = 1 << 30         # the calibration kernels read / write exactly this much
+TRAFFIC_SOURCES = {
+    "attention_prefill": ["attn.hip", "common.hpp", "kernels.hpp"],
+    "indexer_topk_prefill": ["indexer.hip", "topk.hip", "select.hpp", "common.hpp", "kernels.hpp",
+                             "api.hip"],
+    "indexer_topk_decode": ["indexer.hip", "topk.hip", "select.hpp", "common.hpp", "kernels.hpp",
+                            "api.hip"],
+}
+
+
+def pmc_launches():
+    """Launches for a counter pass: a fill that writes CAL_BYTES, an
+    elementwise negation that reads CAL_BYTES and writes CAL_BYTES, then one
+    F layer (indexer + top-k, then attention) of the prefill and of the
+    decode stack on their first input set, each bracketed by synchronisations."""
+    import torch
+    import idxc_inputs as gen
+    import dsa_lightning_indexer_score_amd as idxc
+    src = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    for cfg in (gen.C3_12F, gen.C4_12F):
+        L = gen.layer_inputs(cfg, 0, device="cuda")
+        ws = torch.empty(idxc.idxc_workspace_bytes(cfg.B, cfg.Lq, cfg.Lk, cfg.q_pos0, cfg.H_I,
+                                                   cfg.d_I, cfg.k, cfg.H, cfg.D),
+                         dtype=torch.uint8, device="cuda")
+        cache = torch.empty((cfg.B, cfg.Lq, cfg.k), dtype=torch.int32, device="cuda")
+        out = torch.empty_like(L["q"])
+        torch.cuda.synchronize()
+        idxc.idxc_indexer_topk(L["q_idx"], L["k_idx"], L["w"], cfg.k, q_pos0=cfg.q_pos0,
+                               workspace=ws, out=cache)
+        torch.cuda.synchronize()
+        idxc.idxc_sparse_attn(L["q"], L["k"], L["v"], cache, cfg.scale, workspace=ws, out=out)
+        torch.cuda.synchronize()
+        log("pmc launches of %s done" % cfg.name)
+        del L, ws, cache, out
+        torch.cuda.empty_cache()
+
+
+def pmc_summary(fetch_csv, write_csv, command_fetch, command_write):
+    """Write profiles/hbm_traffic.md from the two counter CSVs of --only pmc.
+
+    Counter values are KiB per dispatch. Each is scaled by the ratio of the
+    calibration kernels' known bytes to what the same counter reads for them
+    (FETCH_SIZE: the negation reads CAL_BYTES; WRITE_SIZE: the fill writes
+    CAL_BYTES)."""
+    import csv
+    import hashlib
+
+    def rows(path, counter):
+        out = []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]),
+                            float(r["Counter_Value"]) * 1024.0))
+        return sorted(out)
+
+    def short(name):
+        n = name.replace("(anonymous namespace)::", "").replace("void ", "")
+        return n.split("(")[0]
+
+    f, w = rows(fetch_csv, "FETCH_SIZE"), rows(write_csv, "WRITE_SIZE")
+    assert [(d, n) for d, n, _, _ in f] == [(d, n) for d, n, _, _ in w], "dispatch lists differ"
+    neg = [x for x in f if "neg_kernel" in x[1] or "NegFunctor" in x[1]]
+    fill = [x for x in w if "FillFunctor" in x[1]]
+    assert neg and fill, "calibration kernels not found"
+    cal_f = CAL_BYTES / neg[0][3]
+    cal_w = CAL_BYTES / fill[0][3]
+    idx = [i for i, x in enumerate(f) if short(x[1]).startswith("idxc::")]
+    lines = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+             "FETCH_SIZE pass: `%s`" % command_fetch, "",
+             "WRITE_SIZE pass: `%s`" % command_write, "",
+             "Calibration: torch.neg over %d bytes reads FETCH_SIZE %.0f KiB (factor %.4f); "
+             "torch.ones of %d bytes writes WRITE_SIZE %.0f KiB (factor %.4f)."
+             % (CAL_BYTES, neg[0][3] / 1024, cal_f, CAL_BYTES, fill[0][3] / 1024, cal_w), "",
+             "| dispatch | kernel | grid | FETCH KiB | WRITE KiB | scaled read MB | "
+             "scaled write MB |", "|---|---|---|---|---|---|---|"]
+    for i in idx:
+        d, n, g, fb = f[i]
+        wb = w[i][3]
+        lines.append("| %d | %s | %d | %.0f | %.0f | %.1f | %.1f |"
+                     % (d, short(n), g, fb / 1024, wb / 1024, fb * cal_f / 1e6, wb * cal_w / 1e6))
+    # the pmc launches run, in order: prefill indexer (+ top-k), prefill
+    # attention, decode indexer (+ top-k), decode attention
+    groups, cur = [], []
+    for i in idx:
+        nm = short(f[i][1])
+        if "attn" in nm and "merge" not in nm:
+            groups.append(("indexer", cur))
+            groups.append(("attention", [i]))
+            cur = []
+        elif "merge" in nm:
+            groups[-1][1].append(i)
+        else:
+            cur.append(i)
+    names = ["indexer_topk_prefill", "attention_prefill", "indexer_topk_decode",
+             "attention_decode"]
+    rec = {}
+    csrc = os.path.join("dsa_lightning_indexer_score_amd", "csrc")
+    for name, (_, members) in zip(names, groups):
+        srcs = [os.path.join(csrc, x) for x in TRAFFIC_SOURCES.get(name, ["attn.hip",
+                                                                          "common.hpp",
+                                                                          "kernels.hpp"])]
+        h = hashlib.sha256()
+        for x in srcs:
+            h.update(open(os.path.join(ROOT, x), "rb").read())
+        tot = sum(f[i][3] * cal_f + w[i][3] * cal_w for i in members)
+        rec[name] = {"sources": srcs, "sha": h.hexdigest()[:16], "bytes": round(tot),
+                     "kernels": [short(f[i][1]) for i in members]}
+    lines += ["", "Per launch (read + write, scaled); bench.py reports these as `traffic` "
+              "while the listed sources hash to `sha`:", "",
+              "traffic-json: " + json.dumps(rec, sort_keys=True), ""]
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    open(path, "w").write("\n".join(lines))
+    print("\n".join(lines))
+
+
+# --------------------------------------------------------------------------- #
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(decode shards by sequence and prefill by query rows with no collective "
@@ -188,41 +360,44 @@ def main():
     import dsa_lightning_indexer_score_amd as idxc
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     log("library %s on %s" % (idxc.idxc_version(), torch.cuda.get_device_name(0)))
+    if args.only == "pmc":
+        pmc_launches()
+        return
 
     res = {}
     extra = {}
     # ----------------------------------------------------------------- prefill
-    cfg12, cfgF = gen.C3_12F, gen.C3_ALLF
-    t0 = time.perf_counter()
-    layers, sets = build_stack(cfg12, N_SETS)
-    log("prefill inputs ready (%d sets, %.1f s)" % (N_SETS, time.perf_counter() - t0))
-    ws = torch.empty(idxc.idxc_workspace_bytes(cfg12.B, cfg12.Lq, cfg12.Lk, cfg12.q_pos0,
-                                               cfg12.H_I, cfg12.d_I, cfg12.k, cfg12.H, cfg12.D),
-                     dtype=torch.uint8, device="cuda")
-    cache = torch.empty((cfg12.B, cfg12.Lq, cfg12.k), dtype=torch.int32, device="cuda")
-    call12 = idxc.StackCall(cfg12.pattern, layers, cfg12.k, cfg12.scale, cfg12.q_pos0,
-                            index_cache=cache, workspace=ws)
-    callF = idxc.StackCall(cfgF.pattern, layers, cfgF.k, cfgF.scale, cfgF.q_pos0,
-                           index_cache=cache, workspace=ws)
-    if args.only in ("", "prefill-12f"):
-        s12 = time_steps(call12, args.steps, args.warmup)
-        assert call12.calls.value == 12
-        log("prefill 12-F: %.2f ms/step" % (s12 * 1e3))
-        res["prefill_12F"] = s12
-    if args.only in ("", "prefill-allf"):
-        sF = time_steps(callF, args.steps, args.warmup)
-        assert callF.calls.value == 47
-        log("prefill all-F: %.2f ms/step" % (sF * 1e3))
-        res["prefill_allF"] = sF
-    # per-layer breakdown with HIP events on the launch stream
-    L0 = sets[0]
-    idx_ms = event_ms(lambda: idxc.idxc_indexer_topk(L0["q_idx"], L0["k_idx"], L0["w"], cfg12.k,
-                                                     workspace=ws, out=cache), 3)
-    att_ms = event_ms(lambda: idxc.idxc_sparse_attn(L0["q"], L0["k"], L0["v"], cache,
-                                                    cfg12.scale, out=L0["out"]), 3)
-    log("prefill per layer: indexer+top-k %.3f ms, attention %.3f ms" % (idx_ms, att_ms))
-    del layers, sets, call12, callF, ws, cache, L0
-    torch.cuda.empty_cache()
+    idx_ms = att_ms = pass_ms = None
+    if args.only != "decode":
+        cfg12, cfgF = gen.C3_12F, gen.C3_ALLF
+        t0 = time.perf_counter()
+        layers, sets = build_stack(cfg12, N_SETS)
+        log("prefill inputs ready (%d sets, %.1f s)" % (N_SETS, time.perf_counter() - t0))
+        ws = torch.empty(idxc.idxc_workspace_bytes(cfg12.B, cfg12.Lq, cfg12.Lk, cfg12.q_pos0,
+                                                   cfg12.H_I, cfg12.d_I, cfg12.k, cfg12.H, cfg12.D),
+                         dtype=torch.uint8, device="cuda")
+        cache = torch.empty((cfg12.B, cfg12.Lq, cfg12.k), dtype=torch.int32, device="cuda")
+        call12 = idxc.StackCall(cfg12.pattern, layers, cfg12.k, cfg12.scale, cfg12.q_pos0,
+                                index_cache=cache, workspace=ws)
+        callF = idxc.StackCall(cfgF.pattern, layers, cfgF.k, cfgF.scale, cfgF.q_pos0,
+                               index_cache=cache, workspace=ws)
+        if args.only in ("", "prefill-12f"):
+            s12 = time_steps(call12, args.steps, args.warmup)
+            assert call12.calls.value == 12
+            log("prefill 12-F: %.2f ms/step" % (s12 * 1e3))
+            res["prefill_12F"] = s12
+        if args.only in ("", "prefill-allf"):
+            sF = time_steps(callF, args.steps, args.warmup)
+            assert callF.calls.value == 47
+            log("prefill all-F: %.2f ms/step" % (sF * 1e3))
+            res["prefill_allF"] = sF
+        # per-kernel durations: HIP events around every launch of a layer-by-layer
+        # pass over the same 12-F stack
+        idx_ms, att_ms, pass_ms = kernel_pass(cfg12, layers, ws, cache, args.steps)
+        log("prefill per layer: indexer+top-k %.3f ms, attention %.3f ms (layer-by-layer pass "
+            "%.2f ms/step)" % (idx_ms, att_ms, pass_ms))
+        del layers, sets, call12, callF, ws, cache
+        torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ decode
     dec = {}
@@ -241,53 +416,62 @@ def main():
                              index_cache=dcache, workspace=dws)
         dec["decode_12F"] = time_steps(dc12, args.decode_steps, args.warmup)
         dec["decode_allF"] = time_steps(dcF, args.decode_steps, args.warmup)
-        D0 = dsets[0]
-        dec_idx_ms = event_ms(lambda: idxc.idxc_indexer_topk(
-            D0["q_idx"], D0["k_idx"], D0["w"], d12.k, q_pos0=d12.q_pos0, workspace=dws,
-            out=dcache), 10)
-        dec_att_ms = event_ms(lambda: idxc.idxc_sparse_attn(D0["q"], D0["k"], D0["v"], dcache,
-                                                            d12.scale, out=D0["out"]), 10)
+        dec_idx_ms, dec_att_ms, dec_pass_ms = kernel_pass(d12, dlayers, dws, dcache,
+                                                          args.decode_steps)
         log("decode: 12-F %.3f ms/step, all-F %.3f ms/step; per layer indexer+top-k %.3f ms, "
             "attention %.3f ms" % (dec["decode_12F"] * 1e3, dec["decode_allF"] * 1e3,
                                    dec_idx_ms, dec_att_ms))
         extra["decode_per_layer_ms"] = {"indexer_topk": dec_idx_ms, "attention": dec_att_ms}
+        extra["decode_layer_by_layer_ms_per_step"] = dec_pass_ms
         extra["decode_indexer_hbm_gbs"] = indexer_bytes(d12) / (dec_idx_ms * 1e-3) / 1e9
         extra["decode_attention_gbs"] = attn_bytes(d12) / (dec_att_ms * 1e-3) / 1e9
-        del dlayers, dsets, dc12, dcF, dws, dcache, D0
+        del dlayers, dsets, dc12, dcF, dws, dcache
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ report
-    cfg = cfg12
+    cfg = gen.C3_12F
     s12 = res.get("prefill_12F")
     sF = res.get("prefill_allF")
     value = cfg.B * cfg.Lq / s12 if s12 else None
-    idx_tflops = indexer_flops(cfg) / (idx_ms * 1e-3) / 1e12
-    att_gbs = attn_bytes(cfg) / (att_ms * 1e-3) / 1e9
-    nF = cfg.pattern.count("F")
-    # dominant kernel of the headline workload by total time per step
-    idx_total, att_total = nF * idx_ms, cfg.n_layers * att_ms
-    roof_idx = {"kernel": "indexer_rows_kernel + topk_rows_kernel (fused indexer + top-k of one F "
-                          "layer, idxc_indexer_topk)",
-                "bound": "mfma", "achieved": idx_tflops, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": idx_tflops / PEAK_BF16_TFLOPS, "traffic": None,
-                "algorithmic": "%.4g flop per launch = causal pairs %d x 2*H_I*d_I"
-                               % (indexer_flops(cfg), causal_pairs(cfg.q_pos0, cfg.Lq)),
-                "launch_ms": idx_ms}
-    roof_att = {"kernel": "sparse_attn_kernel (one layer, idxc_sparse_attn)",
-                "bound": "hbm", "achieved": att_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": att_gbs / PEAK_HBM_GBS, "traffic": None,
-                "algorithmic": "%.4g B per launch = selected pairs x 2*D*2 (K+V rows) + Q + O "
-                               "+ indices" % attn_bytes(cfg),
-                "launch_ms": att_ms}
-    dominant, other = (roof_idx, roof_att) if idx_total >= att_total else (roof_att, roof_idx)
-    extra.update({
-        "prefill_allF_tokens_per_s": cfg.B * cfg.Lq / sF if sF else None,
-        "prefill_allF_ms_per_step": sF * 1e3 if sF else None,
-        "prefill_speedup_12F_vs_allF": (sF / s12) if (sF and s12) else None,
-        "prefill_per_layer_ms": {"indexer_topk": idx_ms, "attention": att_ms},
-        "indexer_mfma_frac": idx_tflops / PEAK_BF16_TFLOPS,
-        "other_roofline": other,
-    })
+    dominant = None
+    if idx_ms is not None:
+        idx_tflops = indexer_flops(cfg) / (idx_ms * 1e-3) / 1e12
+        att_gbs = attn_bytes(cfg) / (att_ms * 1e-3) / 1e9
+        nF = cfg.pattern.count("F")
+        # dominant kernel of the headline workload by total time per step
+        idx_total, att_total = nF * idx_ms, cfg.n_layers * att_ms
+        att_tflops = attn_flops(cfg) / (att_ms * 1e-3) / 1e12
+        roof_idx = {"kernel": "indexer_rows_kernel + topk_kernel (fused indexer + top-k of one F "
+                              "layer, idxc_indexer_topk)",
+                    "bound": "mfma", "achieved": idx_tflops, "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": idx_tflops / PEAK_BF16_TFLOPS,
+                    "traffic": hbm_traffic("indexer_topk_prefill"),
+                    "algorithmic": "%.4g flop per launch = causal pairs %d x 2*H_I*d_I"
+                                   % (indexer_flops(cfg), causal_pairs(cfg.q_pos0, cfg.Lq)),
+                    "launch_ms": idx_ms}
+        # QK^T and PV over the gathered rows are dense bf16 MFMA contractions; the
+        # gathered K/V rows (2*D*2 bytes per selected pair) come mostly from L2 and
+        # the last-level cache (one layer's K and V are 16 MB), not from HBM
+        roof_att = {"kernel": "sparse_attn_kernel (one layer, idxc_sparse_attn)",
+                    "bound": "mfma", "achieved": att_tflops, "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": att_tflops / PEAK_BF16_TFLOPS,
+                    "traffic": hbm_traffic("attention_prefill"),
+                    "algorithmic": "%.4g flop per launch = selected pairs %d x 4*H*D"
+                                   % (attn_flops(cfg), cfg.B * selected_pairs(cfg.q_pos0, cfg.Lq,
+                                                                               cfg.k)),
+                    "gathered_GBs": att_gbs,
+                    "gathered_bytes": attn_bytes(cfg),
+                    "launch_ms": att_ms}
+        dominant, other = (roof_idx, roof_att) if idx_total >= att_total else (roof_att, roof_idx)
+        extra.update({
+            "prefill_allF_tokens_per_s": cfg.B * cfg.Lq / sF if sF else None,
+            "prefill_allF_ms_per_step": sF * 1e3 if sF else None,
+            "prefill_speedup_12F_vs_allF": (sF / s12) if (sF and s12) else None,
+            "prefill_per_layer_ms": {"indexer_topk": idx_ms, "attention": att_ms},
+            "prefill_layer_by_layer_ms_per_step": pass_ms,
+            "indexer_mfma_frac": idx_tflops / PEAK_BF16_TFLOPS,
+            "other_roofline": other,
+        })
     if dec:
         extra.update({
             "decode_12F_tokens_per_s": gen.C4_12F.B / dec["decode_12F"],
