@@ -9,15 +9,15 @@
 // Work unit = (query row, slice of its index list). A unit's 32-key blocks of
 // K and V rows are gathered once into LDS and shared by the waves that own
 // the unit's head blocks (32 heads each), so every gathered row feeds all
-// heads of the query. With two head blocks, one wave gathers K and the other
-// V, two blocks ahead in registers. Scores are computed transposed,
-// S^T = K_sel . Q^T, on 32x32x16 MFMAs: a lane holds 16 keys of one head, so
-// the online-softmax max/sum stays in registers apart from one lane-half
-// swap, and rescaling the output accumulators (O^T, heads on N) is a per-lane
-// multiply. The running maximum is only moved (and the accumulators rescaled)
-// when a block raises it by more than 2^8 in the exp2 domain, which keeps
-// every P below 256. V rows are transposed on the way into LDS so that the
-// P.V MFMA reads contiguous keys.
+// heads of the query. The waves split each block's gather (whole rows, 16
+// bytes per lane), two blocks ahead in registers. Scores are computed
+// transposed, S^T = K_sel . Q^T, on 32x32x16 MFMAs: a lane holds 16 keys of
+// one head, so the online-softmax max/sum stays in registers apart from one
+// lane-half swap, and rescaling the output accumulators (O^T, heads on N) is
+// a per-lane multiply. The running maximum is only moved (and the
+// accumulators rescaled) when a block raises it by more than 2^8 in the exp2
+// domain, which keeps every P below 256. V rows stay row-major in LDS; the
+// P.V MFMA takes its V^T operand through transposing LDS reads.
 //
 // A unit covering only a slice of the list writes a partial result (bf16
 // output normalised by its own sum, plus that sum and the max); a second
@@ -30,99 +30,41 @@ namespace idxc {
 namespace {
 
 constexpr int kAttnWaves = 4;
-constexpr int kVtRow = 40;          // bf16 per transposed-V row: 32 keys + 8 pad (80 B)
 constexpr float kLazyLog2 = 8.0f;   // rescale threshold (exp2 domain)
 constexpr int kMaxAttnSplits = 32;
 
-// Position of key-quad qd (keys 4qd..4qd+3 of a 32-key block) inside a
-// transposed-V row, so that the 8 keys one lane needs for a P.V k-step are
-// contiguous (they follow the row order of the S^T accumulator layout).
-__device__ __forceinline__ int vt_quad_pos(int qd) {
-  return (qd & 4) | ((qd & 1) << 1) | ((qd >> 1) & 1);
-}
-
-// Byte offset of 16-byte chunk ch (0..3) of transposed-V row d. Rows are
-// 80 bytes apart, so 16 consecutive rows hit 16 different bank groups (the
-// P.V operand reads); the chunk is XOR-ed with (d / 16) % 4 so that the rows
-// 8 apart written by one instruction of the transpose spread over 8 bank
-// groups instead of 2.
-__device__ __forceinline__ int vt_off(int d, int ch) {
-  return d * (kVtRow * 2) + ((ch ^ ((d >> 4) & 3)) << 4);
-}
-
-// Gathered rows of one 32-key block in registers. A K-gathering wave holds
-// r[ks] = (slot l%32, 16 B chunk 2ks + l/32); a V-gathering wave holds, for
-// each of its D/64 (key quad, chunk) pairs, 4 rows x 16 B. Both need D/16
-// registers of 16 B; a wave that gathers both uses 2*D/16.
-template <int D, int NR>
-struct Gather {
-  u32x4 r[NR];
+// One gathered 32-key block in LDS: whole K rows SK bytes apart, then whole V
+// rows SV bytes apart. The padding spreads the MFMA operand reads over the
+// banks: the K reads take 16 rows at one column (rows 16 bytes apart modulo
+// 256), the transposed V reads take 4 consecutive rows at one 64-byte column
+// range (rows 64 bytes apart modulo 256).
+// A gather instruction moves KPI whole rows (16 bytes per lane, NCH lanes per
+// row); lane l gathers rows (l / NCH) * NI + r of the block. The block's 32
+// indices are loaded once (one per lane) and spread with lane shuffles.
+template <int D>
+struct Blk {
+  static constexpr int NCH = D / 8;
+  static constexpr int KPI = kWave / NCH;
+  static constexpr int NI = 32 / KPI;
+  static constexpr int SK = 2 * D + 16;
+  static constexpr int SV = 2 * D + 64;
+  static constexpr int KB = 32 * SK;
+  static constexpr int BYTES = 32 * SK + 32 * SV;
 };
 
-template <int D, int NR>
-__device__ __forceinline__ void gather_k(Gather<D, NR>& g, const uint16_t* __restrict__ kb,
-                                         int srow) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-    g.r[ks] = *reinterpret_cast<const u32x4*>(kb + (size_t)srow * D + (ks * 2 + (lane >> 5)) * 8);
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// (i % 4) of the 4 bf16 addressed by lanes 4j + i/4, j = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  auto lp = (__attribute__((address_space(3))) s16x4*)(const_cast<uint8_t*>(p));
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp));
 }
 
-template <int D, int NR, int OFF>
-__device__ __forceinline__ void gather_v(Gather<D, NR>& g, const uint16_t* __restrict__ vb,
-                                         int srow) {
-  constexpr int NCHV = D / 8;
-  const int lane = lane_id();
-#pragma unroll
-  for (int vp = 0; vp < D / 64; ++vp) {
-    const int pi = lane + kWave * vp;
-    const int qd = pi / NCHV;
-    const int c = pi % NCHV;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int rr = __shfl(srow, 4 * qd + r, kWave);
-      g.r[OFF + vp * 4 + r] = *reinterpret_cast<const u32x4*>(vb + (size_t)rr * D + c * 8);
-    }
-  }
-}
-
-template <int D, int NR>
-__device__ __forceinline__ void stage_k(const Gather<D, NR>& g, uint8_t* kl) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-    *reinterpret_cast<u32x4*>(kl + ks * 1024 + lane * 16) = g.r[ks];
-}
-
-template <int D, int NR, int OFF>
-__device__ __forceinline__ void stage_v(const Gather<D, NR>& g, uint16_t* vt) {
-  constexpr int NCHV = D / 8;
-  const int lane = lane_id();
-#pragma unroll
-  for (int vp = 0; vp < D / 64; ++vp) {
-    const int pi = lane + kWave * vp;
-    const int qd = pi / NCHV;
-    const int c = pi % NCHV;
-    const int pq = vt_quad_pos(qd);  // 8-byte slot within the 64 data bytes
-    const u32x4* rows = &g.r[OFF + vp * 4];
-    uint8_t* vtb = reinterpret_cast<uint8_t*>(vt);
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int wd = jj >> 1;
-      const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
-      u32x2 pk;
-      pk.x = __builtin_amdgcn_perm(rows[1][wd], rows[0][wd], sel);
-      pk.y = __builtin_amdgcn_perm(rows[3][wd], rows[2][wd], sel);
-      *reinterpret_cast<u32x2*>(vtb + vt_off(c * 8 + jj, pq >> 1) + (pq & 1) * 8) = pk;
-    }
-  }
-}
-
-// LDS bytes of one unit's buffer: K operand slabs + transposed V.
-template <int D>
-constexpr int unit_lds_bytes() {
-  return (D / 16) * 1024 + D * kVtRow * 2;
-}
+template <int NRW>
+struct Gather {
+  u32x4 k[NRW];
+  u32x4 v[NRW];
+};
 
 template <int D, int HB>
 __global__ __launch_bounds__(kAttnWaves * kWave, (D == 128 && HB == 1) ? 1 : 2)
@@ -131,10 +73,11 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
                         int B, int Lq, int Lk, int H, int k, int nsplit, float sl2,
                         uint16_t* __restrict__ out, uint16_t* __restrict__ part_o,
                         float* __restrict__ part_ml) {
+  using BL = Blk<D>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int UPW = kAttnWaves / HB;  // units per workgroup
-  constexpr int UB = unit_lds_bytes<D>();
+  constexpr int NRW = BL::NI / HB;      // gather instructions per wave and matrix
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
 
   const int wave = threadIdx.x / kWave;
@@ -170,34 +113,32 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
 
-  // gather row of this lane's slot (l % 32) of block j; *vmask = valid slots
-  auto slot_index = [&](int j, uint32_t* vmask) {
-    const int e = kbeg + j * 32 + (lane & 31);
-    const int idx = (active && e < kend) ? irow[e] : -1;
-    const bool valid = idx >= 0 && idx < Lk;
-    *vmask = (uint32_t)(ballot(valid) & 0xFFFFFFFFull);
-    return valid ? idx : 0;
+  // The waves of a unit split the gather: wave hb moves rows r0 .. r0+NRW-1
+  // of every row group, K and V alike.
+  const int gkey0 = (lane / BL::NCH) * BL::NI + (HB == 1 ? 0 : hb * NRW);
+  const int gch = lane % BL::NCH;
+  // rows to gather, from the resolved index of key (lane % 32) (lanes l and
+  // l + 32 hold the same key)
+  auto gather = [&](Gather<NRW>& g, int row_of_lane) {
+#pragma unroll
+    for (int r = 0; r < NRW; ++r) {
+      const int row = __shfl(row_of_lane, gkey0 + r, kWave);
+      g.k[r] = *reinterpret_cast<const u32x4*>(kb + (size_t)row * D + gch * 8);
+      g.v[r] = *reinterpret_cast<const u32x4*>(vb + (size_t)row * D + gch * 8);
+    }
   };
-
-  // with two head blocks, wave hb=0 gathers K and wave hb=1 gathers V
-  constexpr int NR = (HB == 1) ? 2 * KS : KS;
-  constexpr int VOFF = (HB == 1) ? KS : 0;
-  Gather<D, NR> ga, gb;  // ga: block j+2 (in flight), gb: block j+1
-  uint32_t vm_a = 0, vm_b = 0, vm_c = 0;
-  uint8_t* base = dyn + ul * 2 * UB;
-
-  auto gather = [&](Gather<D, NR>& g, int srow) {
-    if (HB == 1 || hb == 0) gather_k<D, NR>(g, kb, srow);
-    if (HB == 1 || hb == 1) gather_v<D, NR, VOFF>(g, vb, srow);
+  uint8_t* base = dyn + ul * 2 * BL::BYTES;
+  auto stage = [&](const Gather<NRW>& g, int buf) {
+    uint8_t* kl = base + buf * BL::BYTES;
+    uint8_t* vl = kl + BL::KB;
+#pragma unroll
+    for (int r = 0; r < NRW; ++r) {
+      *reinterpret_cast<u32x4*>(kl + (gkey0 + r) * BL::SK + gch * 16) = g.k[r];
+      *reinterpret_cast<u32x4*>(vl + (gkey0 + r) * BL::SV + gch * 16) = g.v[r];
+    }
   };
-  auto stage = [&](const Gather<D, NR>& g, int buf) {
-    uint8_t* kl = base + buf * UB;
-    uint16_t* vt = reinterpret_cast<uint16_t*>(kl + KS * 1024);
-    if (HB == 1 || hb == 0) stage_k<D, NR>(g, kl);
-    if (HB == 1 || hb == 1) stage_v<D, NR, VOFF>(g, vt);
-  };
-
-  // raw index-list entries, loaded two blocks before their gather is issued
+  // index of key (lane % 32) of block j; invalid entries gather row 0 and are
+  // masked out of the softmax
   auto raw_index = [&](int j) {
     const int e = kbeg + j * 32 + (lane & 31);
     return (active && j < nblk && e < kend) ? irow[e] : -1;
@@ -207,35 +148,35 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     *vmask = (uint32_t)(ballot(valid) & 0xFFFFFFFFull);
     return valid ? idx : 0;
   };
+
+  Gather<NRW> ga, gb;  // ga: block j+2 (in flight), gb: block j+1
+  uint32_t vm_a = 0, vm_b = 0, vm_c = 0;
   int ix2 = raw_index(2), ix3 = raw_index(3);
-  {
-    const int r0 = slot_index(0, &vm_c);
-    gather(ga, r0);
-    if (nblk > 1) {
-      const int r1 = slot_index(1, &vm_b);
-      gather(gb, r1);
-    }
-    stage(ga, 0);
-  }
+  gather(ga, resolve(raw_index(0), &vm_c));
+  if (nblk > 1) gather(gb, resolve(raw_index(1), &vm_b));
+  stage(ga, 0);
   __syncthreads();
+
+  // V^T operand rows for this lane: key 16kk + 8t + 4(l/32) + (l%16)/4 at
+  // column 64db + 32((l/16)%2) + 8(l%4) bytes (t selects operand half)
+  const int vt_lane = (4 * (lane >> 5) + ((lane & 15) >> 2)) * BL::SV + 32 * ((lane >> 4) & 1) +
+                      8 * (lane & 3);
 
   // One 32-key block. g_far receives block j+2, g_next (block j+1) is staged
   // at the end; the loop alternates the two register sets.
-  auto block = [&](int j, Gather<D, NR>& g_far, Gather<D, NR>& g_next) {
-    if (j + 2 < nblk) {
-      const int r2 = resolve(ix2, &vm_a);
-      gather(g_far, r2);
-    }
+  auto block = [&](int j, Gather<NRW>& g_far, Gather<NRW>& g_next) {
+    if (j + 2 < nblk) gather(g_far, resolve(ix2, &vm_a));
     ix2 = ix3;
     ix3 = raw_index(j + 4);
-    const uint8_t* kl = base + (j & 1) * UB;
-    const uint16_t* vt = reinterpret_cast<const uint16_t*>(kl + KS * 1024);
+    const uint8_t* kl = base + (j & 1) * BL::BYTES;
+    const uint8_t* vl = kl + BL::KB;
 
     // ---- S^T = K . Q^T for this wave's 32 heads
     f32x16 s = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + ks * 1024 + lane * 16);
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + (lane & 31) * BL::SK +
+                                                         (ks * 2 + (lane >> 5)) * 16);
       s = mfma32(ka, qb[ks], s);
     }
     // ---- online softmax in the exp2 domain with a lazily moved maximum
@@ -277,14 +218,17 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
       pw[i >> 3][(i & 7) >> 1] = pack_bf16x2(p0, p1);
     }
     lsum += psum;
-    // ---- O^T += V^T . P^T
+    // ---- O^T += V^T . P^T; P^T's k index 8(l/32) + jj is key
+    // 16kk + 8(jj/4) + 4(l/32) + jj%4, which the transposed reads match
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kk]);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(
-            reinterpret_cast<const uint8_t*>(vt) + vt_off(db * 32 + (lane & 31), 2 * kk + (lane >> 5)));
+        const uint8_t* p0 = vl + vt_lane + 16 * kk * BL::SV + 64 * db;
+        const u32x2 lo = lds_read_tr16(p0);
+        const u32x2 hi = lds_read_tr16(p0 + 8 * BL::SV);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
         o[db] = mfma32(va, pb, o[db]);
       }
     }
@@ -379,7 +323,12 @@ hipError_t launch(const AttnArgs& a, int nsplit, hipStream_t st) {
   constexpr int UPW = kAttnWaves / HB;
   const long long units = (long long)a.B * a.Lq * nsplit;
   const unsigned grid = (unsigned)((units + UPW - 1) / UPW);
-  const size_t shmem = (size_t)UPW * 2 * unit_lds_bytes<D>();
+  const size_t shmem = (size_t)UPW * 2 * Blk<D>::BYTES;
+  if (shmem > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_attn_kernel<D, HB>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (e != hipSuccess) return e;
+  }
   const float sl2 = a.scale * 1.4426950408889634f;
   uint16_t* po = nsplit > 1 ? reinterpret_cast<uint16_t*>(a.workspace) : nullptr;
   float* pml = nsplit > 1 ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.workspace) +
