@@ -96,7 +96,7 @@ def kernel_pass(cfg, layers, ws, cache, steps):
             e[0].record(st)
             if cfg.pattern[l] == "F":
                 idxc.idxc_indexer_topk(L["q_idx"], L["k_idx"], L["w"], cfg.k, q_pos0=cfg.q_pos0,
-                                       workspace=ws, out=cache)
+                                       workspace=ws, out=cache, order="position")
             e[1].record(st)
             idxc.idxc_sparse_attn(L["q"], L["k"], L["v"], cache, cfg.scale, workspace=ws,
                                   out=L["out"])
@@ -254,7 +254,7 @@ def pmc_launches():
         out = torch.empty_like(L["q"])
         torch.cuda.synchronize()
         idxc.idxc_indexer_topk(L["q_idx"], L["k_idx"], L["w"], cfg.k, q_pos0=cfg.q_pos0,
-                               workspace=ws, out=cache)
+                               workspace=ws, out=cache, order="position")
         torch.cuda.synchronize()
         idxc.idxc_sparse_attn(L["q"], L["k"], L["v"], cache, cfg.scale, workspace=ws, out=out)
         torch.cuda.synchronize()

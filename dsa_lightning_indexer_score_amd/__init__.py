@@ -87,7 +87,17 @@ def idxc_topk_workspace_bytes(B, Lq, Lk, q_pos0, k) -> int:
     return n.value
 
 
-def idxc_topk(scores, k: int, q_pos0: int = 0, workspace=None, out=None, stream=None):
+_ORDERS = {"score": _lib.IDXC_ORDER_SCORE, "position": _lib.IDXC_ORDER_POSITION}
+
+
+def _order(order) -> int:
+    if order not in _ORDERS:
+        raise ValueError("order must be 'score' or 'position', not %r" % (order,))
+    return _ORDERS[order]
+
+
+def idxc_topk(scores, k: int, q_pos0: int = 0, workspace=None, out=None, stream=None,
+              order: str = "score"):
     lib = _lib.load()
     B, Lq, Lk = scores.shape
     d = make_dims(B, Lq, Lk, q_pos0, k=k)
@@ -98,7 +108,7 @@ def idxc_topk(scores, k: int, q_pos0: int = 0, workspace=None, out=None, stream=
         out = torch.empty((B, Lq, k), dtype=torch.int32, device=scores.device)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _lib.check(lib.idxc_topk(_ptr(scores, "scores", torch.float32), ctypes.byref(d),
-                             _ptr(workspace, "workspace"), nbytes,
+                             _order(order), _ptr(workspace, "workspace"), nbytes,
                              _ptr(out, "indices", torch.int32), _stream(stream)))
     return out
 
@@ -116,7 +126,7 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 
 
 def idxc_indexer_topk(q_idx, k_idx, w, k: int, q_pos0: int = 0, workspace=None, out=None,
-                      stream=None):
+                      stream=None, order: str = "score"):
     lib = _lib.load()
     d = _idx_dims(q_idx, k_idx, q_pos0, k)
     if workspace is None:
@@ -127,7 +137,7 @@ def idxc_indexer_topk(q_idx, k_idx, w, k: int, q_pos0: int = 0, workspace=None, 
     _lib.check(lib.idxc_indexer_topk(_ptr(q_idx, "q_idx", torch.bfloat16),
                                      _ptr(k_idx, "k_idx", torch.bfloat16),
                                      _ptr(w, "w", torch.bfloat16), ctypes.byref(d),
-                                     _ptr(workspace, "workspace"),
+                                     _order(order), _ptr(workspace, "workspace"),
                                      workspace.numel() * workspace.element_size(),
                                      _ptr(out, "indices", torch.int32), _stream(stream)))
     return out

@@ -16,6 +16,8 @@ IDXC_ERR_INVALID_ARG = 1
 IDXC_ERR_PATTERN = 2
 IDXC_ERR_UNSUPPORTED = 3
 IDXC_ERR_HIP = 4
+IDXC_ORDER_SCORE = 0
+IDXC_ORDER_POSITION = 1
 
 STATUS_NAMES = {
     IDXC_OK: "IDXC_OK",
@@ -70,10 +72,11 @@ def load() -> ctypes.CDLL:
         "idxc_validate_pattern": ([ctypes.c_char_p, i32, P(i32)], ctypes.c_int),
         "idxc_schedule": ([ctypes.c_char_p, i32, P(i32)], ctypes.c_int),
         "idxc_indexer_scores": ([vp, vp, vp, P(IdxcDims), vp, vp], ctypes.c_int),
-        "idxc_topk": ([vp, P(IdxcDims), vp, sz, vp, vp], ctypes.c_int),
+        "idxc_topk": ([vp, P(IdxcDims), ctypes.c_int32, vp, sz, vp, vp], ctypes.c_int),
         "idxc_topk_workspace_bytes": ([P(IdxcDims), P(sz)], ctypes.c_int),
         "idxc_workspace_bytes": ([P(IdxcDims), P(sz)], ctypes.c_int),
-        "idxc_indexer_topk": ([vp, vp, vp, P(IdxcDims), vp, sz, vp, vp], ctypes.c_int),
+        "idxc_indexer_topk": ([vp, vp, vp, P(IdxcDims), ctypes.c_int32, vp, sz, vp, vp],
+                              ctypes.c_int),
         "idxc_sparse_attn": ([vp, vp, vp, vp, P(IdxcDims), ctypes.c_float, vp, sz, vp, vp],
                              ctypes.c_int),
         "idxc_sparse_attn_workspace_bytes": ([P(IdxcDims), P(sz)], ctypes.c_int),

@@ -190,7 +190,7 @@ bool topk_rows_supported(const idxc_dims* d) {
 // Indexer + top-k for one layer into `indices`, using the workspace.
 hipError_t run_indexer_topk(const void* q_idx, const void* k_idx, const void* w,
                             const idxc_dims* d, void* ws, size_t ws_bytes, int32_t* indices,
-                            hipStream_t st) {
+                            bool pos_order, hipStream_t st) {
   IndexerArgs ia{};
   ia.q_idx = static_cast<const uint16_t*>(q_idx);
   ia.k_idx = static_cast<const uint16_t*>(k_idx);
@@ -210,6 +210,7 @@ hipError_t run_indexer_topk(const void* q_idx, const void* k_idx, const void* w,
   ta.rows = rows;
   ta.k = d->k;
   ta.out = indices;
+  ta.pos_order = pos_order ? 1 : 0;
   if (plan_for(d).split) {
     const int nch = indexer_split_chunks(d->Lk);
     uint8_t* base = static_cast<uint8_t*>(ws);
@@ -327,10 +328,12 @@ int idxc_topk_workspace_bytes(const idxc_dims* dims, size_t* bytes) {
   return ok();
 }
 
-int idxc_topk(const float* scores, const idxc_dims* dims, void* workspace, size_t workspace_bytes,
-              int32_t* indices, void* hip_stream) {
+int idxc_topk(const float* scores, const idxc_dims* dims, int32_t order, void* workspace,
+              size_t workspace_bytes, int32_t* indices, void* hip_stream) {
   int r = check_dims(dims, 4);
   if (r != IDXC_OK) return r;
+  if (order != IDXC_ORDER_SCORE && order != IDXC_ORDER_POSITION)
+    return fail(IDXC_ERR_INVALID_ARG, "order = %d is not an IDXC_ORDER_* value", order);
   REQUIRE_PTR(scores, "scores");
   REQUIRE_PTR(indices, "indices");
   if (!topk_rows_supported(dims))
@@ -351,15 +354,18 @@ int idxc_topk(const float* scores, const idxc_dims* dims, void* workspace, size_
   ta.rows = dims->B * dims->Lq;
   ta.k = dims->k;
   ta.out = indices;
+  ta.pos_order = order == IDXC_ORDER_POSITION ? 1 : 0;
   set_parts(ta, static_cast<uint8_t*>(workspace), dims);
   return hip_status(launch_topk(ta, static_cast<hipStream_t>(hip_stream)), "topk launch");
 }
 
 int idxc_indexer_topk(const void* q_idx, const void* k_idx, const void* w,
-                      const idxc_dims* dims, void* workspace, size_t workspace_bytes,
-                      int32_t* indices, void* hip_stream) {
+                      const idxc_dims* dims, int32_t order, void* workspace,
+                      size_t workspace_bytes, int32_t* indices, void* hip_stream) {
   int r = check_dims(dims, 1 | 4);
   if (r != IDXC_OK) return r;
+  if (order != IDXC_ORDER_SCORE && order != IDXC_ORDER_POSITION)
+    return fail(IDXC_ERR_INVALID_ARG, "order = %d is not an IDXC_ORDER_* value", order);
   REQUIRE_PTR(q_idx, "q_idx");
   REQUIRE_PTR(k_idx, "k_idx");
   REQUIRE_PTR(w, "w");
@@ -370,6 +376,7 @@ int idxc_indexer_topk(const void* q_idx, const void* k_idx, const void* w,
     return fail(IDXC_ERR_INVALID_ARG, "workspace of %zu bytes is below the minimum %zu",
                 workspace_bytes, p.min_bytes);
   return hip_status(run_indexer_topk(q_idx, k_idx, w, dims, workspace, workspace_bytes, indices,
+                                     order == IDXC_ORDER_POSITION,
                                      static_cast<hipStream_t>(hip_stream)),
                     "indexer_topk launch");
 }
@@ -455,8 +462,10 @@ int idxc_layer_stack_forward(const char* pattern, int32_t n_layers, const idxc_l
   for (int l = 0; l < n_layers; ++l) {
     const idxc_layer& L = layers[l];
     if (pattern[l] == 'F') {
+      // the cache keeps each row's top-k set in position order: attention
+      // does not depend on the order, and its gathers then sweep the keys
       hipError_t e = run_indexer_topk(L.q_idx, L.k_idx, L.w, dims, workspace, workspace_bytes,
-                                      index_cache, st);
+                                      index_cache, true, st);
       if (e != hipSuccess) {
         *indexer_calls = calls;
         return hip_status(e, "stack indexer launch");

@@ -49,6 +49,9 @@ struct TopkArgs {
   int* part_count;
   int rows, k;
   int32_t* out;  // [rows, k]
+  // 0: score order (higher score, then lower position); 1: increasing
+  // position order (the selected set is the same)
+  int pos_order;
 };
 
 // Number of stage-1 chunks for materialised rows of length Lk (1 = single pass).

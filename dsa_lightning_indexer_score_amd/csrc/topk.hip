@@ -9,7 +9,9 @@
 // LDS once (loads batched so many are in flight), selects the exact top-k in
 // position order (select.hpp: range-narrowing radix select plus an ordered
 // pass), and a bitonic sort of 64-bit (key, ~position) words puts the k
-// winners in order.
+// winners in score order; the index cache of a layer stack keeps them in
+// position order instead (gathers then sweep the keys in order), which needs
+// no sort.
 //
 // Inputs: a materialised score row (positions implicit), or candidate lists of
 // (order key, position) pairs in increasing position order, possibly split in
@@ -165,13 +167,20 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks) {
   u32x2* part = nullptr;
   if (OUT == kOutPart) part = a.part + ((size_t)row * nchunks + chunk) * a.k;
   uint64_t* sortbuf = sm.sortbuf;
+  int32_t* orow = a.out + (size_t)row * k;
+  const bool pos_order = OUT == kOutFinal && a.pos_order;
   const int kk = block_topk_collect<SRC == kSrcCand>(
       skey, spos, pos0, n, k, sm.sel, [&](int slot, uint32_t key, uint32_t pos) {
         if (OUT == kOutPart) part[slot] = u32x2{key, pos};
+        else if (pos_order) orow[slot] = (int32_t)pos;
         else sortbuf[slot] = (((uint64_t)key) << 32) | (uint64_t)(~pos);
       });
   if (OUT == kOutPart) {
     if (tid == 0) a.part_count[row * nchunks + chunk] = kk;
+    return;
+  }
+  if (pos_order) {  // winners are emitted in position order: no sort
+    for (int j = kk + tid; j < k; j += kThreads) orow[j] = -1;
     return;
   }
 
@@ -187,7 +196,6 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks) {
       v[j] = idx < kk ? sm.sortbuf[idx] : 0ull;
     }
     sort2048_regs(v, sm.sortbuf, tid);
-    int32_t* orow = a.out + (size_t)row * k;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int idx = tid * 8 + j;
@@ -213,7 +221,6 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks) {
     }
   }
 
-  int32_t* orow = a.out + (size_t)row * k;
   for (int j = tid; j < k; j += kThreads) {
     orow[j] = (j < kk) ? (int32_t)(~(uint32_t)(sm.sortbuf[j] & 0xFFFFFFFFull)) : -1;
   }

@@ -116,14 +116,23 @@ int idxc_schedule(const char* pattern, int32_t n_layers, int32_t* source);
 int idxc_indexer_scores(const void* q_idx, const void* k_idx, const void* w,
                         const idxc_dims* dims, float* scores, void* hip_stream);
 
+/* Order of the positions in an output index list. The selected set is the
+ * same in both: the min(k, t+1) best positions under (score desc, position
+ * asc), followed by -1 entries.
+ *   IDXC_ORDER_SCORE:    sorted by (score desc, position asc);
+ *   IDXC_ORDER_POSITION: increasing position (what a layer stack's index
+ *                        cache holds; attention does not depend on order). */
+enum { IDXC_ORDER_SCORE = 0, IDXC_ORDER_POSITION = 1 };
+
 /* Per-query top-k of materialised scores ([W] I_l = TopK(s_l, k)). Row (b,i)
  * reads scores[b,i,0..t] only (t = q_pos0 + i) and writes indices[b,i,0..k-1]:
- * the min(k, t+1) best positions sorted by (score desc, position asc), then
- * -1. Uses B, Lq, Lk, q_pos0, k. Bit-exact and deterministic. Rows longer
+ * the min(k, t+1) best positions in the given order (IDXC_ORDER_*, anything
+ * else is IDXC_ERR_INVALID_ARG), then -1. Uses B, Lq, Lk, q_pos0, k.
+ * Bit-exact and deterministic. Rows longer
  * than 8192 are selected in two stages through a device workspace of at
  * least idxc_topk_workspace_bytes() bytes (NULL/0 is fine when that is 0);
  * Lk > 8192 * floor(16384 / k) returns IDXC_ERR_UNSUPPORTED. */
-int idxc_topk(const float* scores, const idxc_dims* dims, void* workspace,
+int idxc_topk(const float* scores, const idxc_dims* dims, int32_t order, void* workspace,
               size_t workspace_bytes, int32_t* indices, void* hip_stream);
 
 /* Workspace bytes idxc_topk needs for these sizes (0 when Lk <= 8192).
@@ -136,15 +145,15 @@ int idxc_topk_workspace_bytes(const idxc_dims* dims, size_t* bytes);
 int idxc_workspace_bytes(const idxc_dims* dims, size_t* bytes);
 
 /* Fused indexer + top-k: same result as idxc_indexer_scores followed by
- * idxc_topk, without writing the score matrix. Scores are filtered on chip
+ * idxc_topk with the same order, without writing the score matrix. Scores are filtered on chip
  * against a running per-query threshold; only candidates that can still be
  * in the top-k are kept, in a caller-provided workspace. Smaller workspaces
  * (down to 256*ceil(4*B*Lq/256) + 8*B*Lq*64*ceil((k+64)/64) bytes) are
  * accepted and only cost speed.
  * Returns IDXC_ERR_INVALID_ARG if the workspace is smaller than that. */
 int idxc_indexer_topk(const void* q_idx, const void* k_idx, const void* w,
-                      const idxc_dims* dims, void* workspace, size_t workspace_bytes,
-                      int32_t* indices, void* hip_stream);
+                      const idxc_dims* dims, int32_t order, void* workspace,
+                      size_t workspace_bytes, int32_t* indices, void* hip_stream);
 
 /* Gathered sparse attention ([J] "背景 & 问题提出": core attention only over
  * the k selected tokens). For each (b,i,h): softmax over the valid entries of
@@ -170,10 +179,13 @@ int idxc_sparse_attn_workspace_bytes(const idxc_dims* dims, size_t* bytes);
  * top-k of layers[l] overwrites index_cache [B,Lq,k] and *indexer_calls is
  * incremented; then sparse attention of layers[l] reads index_cache and
  * writes layers[l].out. S layers launch no indexer work. Afterwards
- * index_cache holds the last F layer's indices. *indexer_calls (HOST
+ * index_cache holds the last F layer's indices, in IDXC_ORDER_POSITION
+ * (attention does not depend on the order, and position order lets the K/V
+ * gathers of the rows that run together sweep the keys together).
+ * *indexer_calls (HOST
  * pointer) receives the number of indexer launches (= number of F layers).
  * debug_indices, if not NULL, is a DEVICE buffer [n_layers, B, Lq, k] that
- * receives each layer's indices (for tests). workspace as for
+ * receives each layer's cache contents (for tests). workspace as for
  * idxc_indexer_topk, plus room for attention partials; idxc_workspace_bytes
  * with H and D set gives the full-speed size. */
 int idxc_layer_stack_forward(const char* pattern, int32_t n_layers,

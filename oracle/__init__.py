@@ -9,8 +9,8 @@ closed forms, brute force or library special cases; none is "parity unpinned".
 """
 from .indexcache import (PAD, validate_pattern, nearest_full, indexer_scores,
                          topk_row, topk, sparse_attention, schedule, layer_stack,
-                         overlap, jaccard, mean_overlap, greedy_pattern)
+                         overlap, jaccard, mean_overlap, greedy_pattern, position_order)
 
 __all__ = ["PAD", "validate_pattern", "nearest_full", "indexer_scores", "topk_row",
            "topk", "sparse_attention", "schedule", "layer_stack", "overlap",
-           "jaccard", "mean_overlap", "greedy_pattern"]
+           "jaccard", "mean_overlap", "greedy_pattern", "position_order"]

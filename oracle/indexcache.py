@@ -236,6 +236,16 @@ def layer_stack(pattern: str, layers: Sequence[Dict[str, np.ndarray]], k: int,
 # --------------------------------------------------------------------------- #
 # Metrics  ([W] Overlap(l, j) = |I_l ∩ I_j| / k; [S] "Step 1" Jaccard)
 # --------------------------------------------------------------------------- #
+def position_order(indices: np.ndarray) -> np.ndarray:
+    """The same top-k sets with each row's valid positions in increasing order
+    and the PAD entries last: the order in which a layer stack's index cache
+    holds them (the selection, a set, is unchanged; attention over the set
+    does not depend on its order)."""
+    ix = np.asarray(indices)
+    key = np.where(ix == PAD, np.iinfo(np.int64).max, ix.astype(np.int64))
+    return np.take_along_axis(ix, np.argsort(key, axis=-1, kind="stable"), axis=-1)
+
+
 def _valid_set(row: np.ndarray) -> set:
     return set(int(x) for x in np.asarray(row).ravel() if int(x) != PAD)
 

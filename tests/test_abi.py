@@ -95,11 +95,14 @@ def test_indexer_scores_argument_errors(lib):
 
 
 def test_topk_argument_errors(lib):
-    f = lib.idxc_topk
+    f = lambda s, d, ws, nb, out, st, order=0: lib.idxc_topk(s, d, order, ws, nb, out, st)
     assert f(P(), ctypes.byref(_dims(k=0)), None, 0, P(), None) == _lib.IDXC_ERR_INVALID_ARG
     assert f(P(), ctypes.byref(_dims(k=4096)), None, 0, P(), None) == _lib.IDXC_ERR_UNSUPPORTED
     assert f(None, ctypes.byref(_dims()), None, 0, P(), None) == _lib.IDXC_ERR_INVALID_ARG
     assert f(P(), ctypes.byref(_dims()), None, 0, P(FAKE + 4), None) == _lib.IDXC_ERR_INVALID_ARG
+    for bad in (-1, 2, 7):
+        assert f(P(), ctypes.byref(_dims()), None, 0, P(), None, bad) == _lib.IDXC_ERR_INVALID_ARG
+        assert "order" in lib.idxc_last_error().decode()
     # long rows need the two-stage workspace; too long rows are unsupported
     long_rows = _dims(Lq=1, Lk=65536, q_pos0=65535, k=2048)
     n = ctypes.c_size_t(0)
@@ -136,8 +139,12 @@ def test_workspace_and_fused_errors(lib):
     assert lib.idxc_workspace_bytes(ctypes.byref(_dims()), ctypes.byref(n)) == 0
     assert n.value >= 64 * (8 * (16 + 64) + 4)
     f = lib.idxc_indexer_topk
-    assert f(P(), P(), P(), ctypes.byref(_dims()), P(), 16, P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), P(), P(), ctypes.byref(_dims()), 0, P(), 16, P(), None) == \
+        _lib.IDXC_ERR_INVALID_ARG
     assert "workspace" in lib.idxc_last_error().decode()
+    assert f(P(), P(), P(), ctypes.byref(_dims()), 3, P(), 1 << 30, P(), None) == \
+        _lib.IDXC_ERR_INVALID_ARG
+    assert "order" in lib.idxc_last_error().decode()
 
 
 def test_stack_errors_before_launch(lib):

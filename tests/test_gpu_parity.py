@@ -107,9 +107,11 @@ def test_topk_exact(kind, B, Lq, Lk, q_pos0, k):
     _say("topk %s B=%d Lq=%d Lk=%d q_pos0=%d k=%d" % (kind, B, Lq, Lk, q_pos0, k))
     s = gen.score_rows(B, Lq, Lk, kind=kind, seed=3)
     got = idxc.idxc_topk(cu(s), k, q_pos0=q_pos0)
+    got_pos = idxc.idxc_topk(cu(s), k, q_pos0=q_pos0, order="position")
     torch.cuda.synchronize()
     want = oracle.topk(s.numpy(), k, q_pos0)
     assert np.array_equal(got.cpu().numpy(), want)
+    assert np.array_equal(got_pos.cpu().numpy(), oracle.position_order(want))
 
 
 # --------------------------------------------------------------------------- #
@@ -211,12 +213,14 @@ def test_fused_equals_materialised_and_decode_equals_last_row():
     B, L, H_I, d_I, k = 2, 700, 64, 128, 64
     q, kk, w = gen.indexer_inputs(B, L, L, H_I, d_I, kind="int", seed=8, w_kind="neg-quarter")
     fused = idxc.idxc_indexer_topk(cu(q), cu(kk), cu(w), k)
+    fused_pos = idxc.idxc_indexer_topk(cu(q), cu(kk), cu(w), k, order="position")
     two = idxc.idxc_topk(idxc.idxc_indexer_scores(cu(q), cu(kk), cu(w)), k)
     dec = idxc.idxc_indexer_topk(cu(q[:, L - 1:]), cu(kk), cu(w[:, L - 1:]), k, q_pos0=L - 1)
     chunk = idxc.idxc_indexer_topk(cu(q[:, 256:512]), cu(kk[:, :512]), cu(w[:, 256:512]), k,
                                    q_pos0=256)
     torch.cuda.synchronize()
     assert torch.equal(fused, two)
+    assert np.array_equal(fused_pos.cpu().numpy(), oracle.position_order(fused.cpu().numpy()))
     assert torch.equal(dec[:, 0], fused[:, L - 1])
     assert torch.equal(chunk, fused[:, 256:512])
 
@@ -291,12 +295,36 @@ def test_stack_tiny_fssf_exact():
     assert res["indexer_calls"] == ref["calls"] == 2
     dbg = res["debug_indices"].cpu().numpy()
     for l in range(cfg.n_layers):
-        assert np.array_equal(dbg[l], ref["indices"][l]), l
+        # the cache holds the oracle's top-k set in position order
+        assert np.array_equal(dbg[l], oracle.position_order(ref["indices"][l])), l
         err = np.abs(res["out"][l].float().cpu().numpy() - ref["out"][l]).max()
         assert err <= ATOL, (l, err)
     assert np.array_equal(dbg[1], dbg[0]) and np.array_equal(dbg[2], dbg[0])
     assert not np.array_equal(dbg[3], dbg[0])
-    assert np.array_equal(res["index_cache"].cpu().numpy(), ref["indices"][3])
+    assert np.array_equal(res["index_cache"].cpu().numpy(),
+                          oracle.position_order(ref["indices"][3]))
+
+
+@pytest.mark.parametrize("B,Lq,Lk,q_pos0,k", [
+    (1, 3000, 3000, 0, 256),       # many rows: candidate path
+    (2, 1, 20000, 19999, 2048),    # decode rows: per-chunk top-k, two segments+
+])
+def test_stack_cache_is_oracle_set_in_position_order(B, Lq, Lk, q_pos0, k):
+    import dataclasses
+    cfg = dataclasses.replace(gen.C1, name="cache", n_layers=2, pattern="FS", B=B, Lq=Lq,
+                              Lk=Lk, q_pos0=q_pos0, H_I=64, d_I=128, k=k, H=4, D=64)
+    _say("stack cache order B=%d Lq=%d Lk=%d k=%d" % (B, Lq, Lk, k))
+    layers = _layers(cfg)
+    dev_layers = [{n: cu(t) for n, t in L.items()} for L in layers]
+    res = idxc.idxc_layer_stack_forward(cfg.pattern, dev_layers, cfg.k, cfg.scale,
+                                        q_pos0=cfg.q_pos0, debug_indices=True)
+    torch.cuda.synchronize()
+    L0 = layers[0]
+    want = oracle.topk(oracle.indexer_scores(f64(L0["q_idx"]), f64(L0["k_idx"]), f64(L0["w"]),
+                                             q_pos0), k, q_pos0)
+    dbg = res["debug_indices"].cpu().numpy()
+    assert np.array_equal(dbg[0], oracle.position_order(want))
+    assert np.array_equal(dbg[1], dbg[0])
 
 
 def test_stack_s_layers_ignore_indexer_inputs():
@@ -336,6 +364,7 @@ def test_stack_random_small_overlap():
     L3 = layers[3]
     want2 = oracle.topk(oracle.indexer_scores(f64(layers[2]["q_idx"]), f64(layers[2]["k_idx"]),
                                               f64(layers[2]["w"]), 0), cfg.k, 0)
+    want2 = oracle.position_order(want2)
     same = [t for t in range(cfg.Lq) if np.array_equal(dbg[3][0, t], want2[0, t])]
     assert len(same) >= 0.5 * cfg.Lq
     rows = np.array(same[:: max(1, len(same) // 64)])

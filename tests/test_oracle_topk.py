@@ -102,3 +102,17 @@ def test_short_rows_return_all_positions():
     for t in range(5):
         assert sorted(idx[0, t, : t + 1].tolist()) == list(range(t + 1))
         assert (idx[0, t, t + 1:] == -1).all()
+
+
+def test_position_order_keeps_the_set_and_sorts_positions():
+    ix = np.array([[5, 2, 9, -1], [3, -1, -1, -1], [7, 0, 1, 4]])
+    want = np.array([[2, 5, 9, -1], [3, -1, -1, -1], [0, 1, 4, 7]])
+    assert np.array_equal(oracle.position_order(ix), want)
+    rng = np.random.default_rng(3)
+    sc = rng.standard_normal((1, 40, 40))
+    top = oracle.topk(sc, 8, 0)
+    po = oracle.position_order(top)
+    for a, b in zip(top[0], po[0]):
+        v = b[b >= 0]
+        assert set(a[a >= 0]) == set(v) and np.all(np.diff(v) > 0)
+        assert np.all(b[len(v):] == -1)
