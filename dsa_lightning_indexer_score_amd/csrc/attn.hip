@@ -181,21 +181,16 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     }
     // ---- online softmax in the exp2 domain with a lazily moved maximum
     float x[16];
-    float mloc = -INFINITY;
-    if (vm_c == 0xFFFFFFFFu) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        x[i] = s[i] * sl2;
-        mloc = fmaxf(mloc, x[i]);
-      }
-    } else {
+    for (int i = 0; i < 16; ++i) x[i] = s[i] * sl2;
+    if (__builtin_expect(vm_c != 0xFFFFFFFFu, 0)) {  // wave-uniform: padded entries
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const bool ok = (vm_c >> acc_row(i, lane)) & 1u;
-        x[i] = ok ? s[i] * sl2 : -INFINITY;
-        mloc = fmaxf(mloc, x[i]);
-      }
+      for (int i = 0; i < 16; ++i)
+        if (!((vm_c >> acc_row(i, lane)) & 1u)) x[i] = -INFINITY;
     }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, x[i]);
     const float mblk = pair_max(mloc);
     const bool move = mblk > m_used + kLazyLog2;
     if (ballot(move)) {

@@ -224,7 +224,9 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
 
   // --- query operands (A: heads x d) and head weights, held in registers
   bf16x8 a_op[HB][KS];
-  float wv[HB][16];
+  // head weights as bf16 pairs (even head in the low half): bf16 -> fp32 is
+  // a shift or a mask, and the pairs halve the registers held
+  uint32_t wp[HB][8];
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     const int h = hb * 32 + (lane & 31);
@@ -241,68 +243,94 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int hh = hb * 32 + acc_row(i, lane);
-      wv[hb][i] = (active && hh < H_I) ? bf16_to_f32(w[row * H_I + hh]) : 0.0f;
+      const uint32_t wb = (active && hh < H_I) ? (uint32_t)w[row * H_I + hh] : 0u;
+      if (i & 1) wp[hb][i >> 1] |= wb << 16;
+      else wp[hb][i >> 1] = wb;
     }
   }
 
   const uint16_t* kbase = k_idx + (size_t)b * Lk * DI;
 
-  // --- cooperative tile load: global -> registers -> swizzled LDS, one tile
-  // ahead of the tile being scored
-  u32x4 pa[CPT];
-  auto load_tile = [&](int s_begin, u32x4* dst) {
+  // --- cooperative tile load, global -> LDS directly (16 bytes per lane),
+  // one tile ahead of the tile being scored. LDS chunk position p of key row
+  // r holds the row's 16-byte chunk p ^ (r % NCH) (XOR swizzle: the MFMA
+  // operand reads of 16 rows at one chunk hit 16 different bank groups); a
+  // lane picks the chunk that belongs at its position. Keys past Lk load row
+  // Lk - 1: they are never kept (every kept key is <= t < Lk).
+  static_assert(TILE_CHUNKS % THREADS == 0, "tile chunks must fill the workgroup");
+  auto load_tile = [&](int s_begin, int buf) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int chunk = threadIdx.x + c * THREADS;
-      const int s = s_begin + chunk / NCH;
-      if (chunk < TILE_CHUNKS && s < Lk) {
-        dst[c] = *reinterpret_cast<const u32x4*>(kbase + (size_t)s * DI + (chunk % NCH) * 8);
-      } else {
-        dst[c] = u32x4{0u, 0u, 0u, 0u};
-      }
+      const int r = chunk / NCH;
+      const int p = chunk % NCH;
+      const int s = min(s_begin + r, Lk - 1);
+      const uint16_t* src = kbase + (size_t)s * DI + (p ^ (r % NCH)) * 8;
+      uint8_t* dst = &tile_lds[buf][(wave * kWave + c * THREADS) * 16];  // wave-uniform
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16,
+                                       0, 0);
     }
   };
-  auto store_tile = [&](int buf, const u32x4* src) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int chunk = threadIdx.x + c * THREADS;
-      if (chunk < TILE_CHUNKS) {
-        const int r = chunk / NCH;
-        const int cc = chunk % NCH;
-        *reinterpret_cast<u32x4*>(&tile_lds[buf][r * ROW_BYTES + ((cc ^ (r % NCH)) * 16)]) =
-            src[c];
-      }
-    }
+  // the tile's loads have landed in LDS for every wave
+  auto tile_ready = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   };
-  // scores of this wave's row against keys half*64 .. half*64+63 of LDS tile
-  // `buf`; lane l gets key half*64 + l
-  auto tile_scores = [&](int buf, int half) {
+  // Scores of this wave's row against the keys of LDS tile `buf`: vals[h]
+  // gets key h*64 + lane for h = 0 and, if `both`, h = 1. The tile's 32-key
+  // blocks are software-pipelined: the MFMAs of block j+1 are issued before
+  // the ReLU / head-weight reduction of block j, so this wave's vector work
+  // overlaps its own matrix work (the waves of a workgroup run in step
+  // between the per-tile barriers and cannot cover each other).
+  auto tile_vals = [&](int buf, bool both, float (&vals)[2]) {
     const uint8_t* tl = tile_lds[buf];
-    float sc[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int r = half * 64 + nb * 32 + (lane & 31);
+    f32x16 acc[2][HB];
+    float sc[4];
+    auto issue = [&](int j) {
+      const int r = j * 32 + (lane & 31);
       bf16x8 b_op[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int c = ks * 2 + (lane >> 5);
         b_op[ks] = *reinterpret_cast<const bf16x8*>(&tl[r * ROW_BYTES + ((c ^ (r % NCH)) * 16)]);
       }
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) acc[j & 1][hb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+          acc[j & 1][hb] = mfma32(a_op[hb][ks], b_op[ks], acc[j & 1][hb]);
+      }
+    };
+    auto reduce = [&](int j) {
       float part0 = 0.0f, part1 = 0.0f;
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma32(a_op[hb][ks], b_op[ks], acc);
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-          part0 = fmaf(wv[hb][i], relu_bits(acc[i]), part0);
-          part1 = fmaf(wv[hb][i + 1], relu_bits(acc[i + 1]), part1);
+          const uint32_t pw = wp[hb][i >> 1];
+          part0 = fmaf(__uint_as_float(pw << 16), relu_bits(acc[j & 1][hb][i]), part0);
+          part1 = fmaf(__uint_as_float(pw & 0xFFFF0000u), relu_bits(acc[j & 1][hb][i + 1]),
+                       part1);
         }
       }
-      sc[nb] = pair_sum(part0 + part1);
+      sc[j] = pair_sum(part0 + part1);
+    };
+    issue(0);
+    issue(1);
+    reduce(0);
+    if (both) {
+      issue(2);
+      reduce(1);
+      issue(3);
+      reduce(2);
+      reduce(3);
+      vals[1] = ((lane < 32) ? sc[2] : sc[3]) + 0.0f;
+    } else {
+      reduce(1);
     }
-    return ((lane < 32) ? sc[0] : sc[1]) + 0.0f;
+    vals[0] = ((lane < 32) ? sc[0] : sc[1]) + 0.0f;
   };
 
   // --- candidate state (MODE 1)
@@ -329,13 +357,13 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
       return v < nsamp ? (int)(((long long)v * span) / (nsamp - 1)) : (v - nsamp) * kKeyTile;
     };
 
-    load_tile(tile_start(0), pa);
-    store_tile(0, pa);
-    __syncthreads();
+    load_tile(tile_start(0), 0);
+    tile_ready();
 
     for (int v = 0; v < nv; ++v) {
-      // tile v is in LDS buffer v&1; fetch tile v+1 into registers
-      if (v + 1 < nv) load_tile(tile_start(v + 1), pa);
+      // tile v is in LDS buffer v&1; tile v+1 streams into the other buffer
+      // (last read in tile v-1, before the barrier that ended it)
+      if (v + 1 < nv) load_tile(tile_start(v + 1), (v + 1) & 1);
       if (MODE == 1 && v == nsamp && nsamp > 0 && compute_row) {
         // threshold = m-th largest sampled order key (binary search on bits)
         const int nkeys = nsamp * kKeyTile;
@@ -357,20 +385,25 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
       if (v < nsamp) {
         // sampled keys are all <= t_first <= t
         if (compute_row) {
+          float vals[2];
+          tile_vals(v & 1, true, vals);
 #pragma unroll
           for (int half = 0; half < 2; ++half)
-            my_samp[v * kKeyTile + half * 64 + lane] = order_key(tile_scores(v & 1, half));
+            my_samp[v * kKeyTile + half * 64 + lane] = order_key(vals[half]);
         }
       } else if (compute_row && tile_s0 <= t) {
+        // the second half is skipped when it lies wholly above this row
+        const bool both = tile_s0 + 64 <= t;
+        float vals[2];
+        tile_vals(v & 1, both, vals);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int s = tile_s0 + half * 64 + lane;
-          if (half == 1 && tile_s0 + 64 > t) {
-            // second half wholly above this row
+          if (half == 1 && !both) {
             if (MODE == 0 && s < Lk) my_scores[s] = -INFINITY;
             continue;
           }
-          const float val = tile_scores(v & 1, half);
+          const float val = vals[half];
           if (MODE == 0) {
             if (s < Lk) my_scores[s] = (s <= t) ? val : -INFINITY;
           } else {
@@ -399,8 +432,7 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
           if (s < Lk) my_scores[s] = -INFINITY;
         }
       }
-      if (v + 1 < nv) store_tile((v + 1) & 1, pa);
-      __syncthreads();
+      tile_ready();
     }
 
     if (MODE == 0 || nsamp == 0) break;
