@@ -153,7 +153,7 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   uint32_t vm_a = 0, vm_b = 0, vm_c = 0;
   int ix2 = raw_index(2), ix3 = raw_index(3);
   gather(ga, resolve(raw_index(0), &vm_c));
-  if (nblk > 1) gather(gb, resolve(raw_index(1), &vm_b));
+  gather(gb, resolve(raw_index(1), &vm_b));
   stage(ga, 0);
   __syncthreads();
 
@@ -165,7 +165,10 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   // One 32-key block. g_far receives block j+2, g_next (block j+1) is staged
   // at the end; the loop alternates the two register sets.
   auto block = [&](int j, Gather<NRW>& g_far, Gather<NRW>& g_next) {
-    if (j + 2 < nblk) gather(g_far, resolve(ix2, &vm_a));
+    // issued unconditionally (blocks past the end gather row 0, masked out):
+    // a conditional load here would make the compiler drain every
+    // outstanding load before the staging below, removing the prefetch
+    gather(g_far, resolve(ix2, &vm_a));
     ix2 = ix3;
     ix3 = raw_index(j + 4);
     const uint8_t* kl = base + (j & 1) * BL::BYTES;
@@ -229,7 +232,7 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     }
     // ---- stage block j+1 into the other buffer (nobody has read it since
     // the barrier that ended block j-1)
-    if (j + 1 < nblk) stage(g_next, (j + 1) & 1);
+    stage(g_next, (j + 1) & 1);  // past the last block: a buffer nobody reads
     vm_c = vm_b;
     vm_b = vm_a;
     __syncthreads();
