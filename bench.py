@@ -171,6 +171,67 @@ def attn_flops(cfg):
 
 
 # --------------------------------------------------------------------------- #
+# long-context indexer + top-k (query chunks) and the standalone top-k
+# --------------------------------------------------------------------------- #
+def events_ms(fn, reps=1):
+    """Mean device time of fn() over reps calls on torch's current stream (the
+    stream the library launches on), after one untimed call."""
+    import torch
+    st = torch.cuda.current_stream()
+    fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(st)
+    for _ in range(reps):
+        fn()
+    b.record(st)
+    b.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def long_context(L, chunk, H_I=64, d_I=128, k=2048, seed=0):
+    """Fused indexer + top-k of one layer at L tokens, processed in query
+    chunks of `chunk` rows against all preceding keys (chunk c: q_pos0 =
+    c*chunk, keys [0, (c+1)*chunk)); scores never reach HBM."""
+    import torch
+    import idxc_inputs as gen
+    import dsa_lightning_indexer_score_amd as idxc
+    q, kk, w = gen.indexer_inputs(1, L, L, H_I, d_I, kind="normal", seed=seed, device="cuda")
+    ws = torch.empty(idxc.idxc_workspace_bytes(1, chunk, L, L - chunk, H_I, d_I, k),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((1, chunk, k), dtype=torch.int32, device="cuda")
+    n = L // chunk
+
+    def one_pass():
+        for c in range(n):
+            idxc.idxc_indexer_topk(q[:, c * chunk:(c + 1) * chunk], kk[:, :(c + 1) * chunk],
+                                   w[:, c * chunk:(c + 1) * chunk], k, q_pos0=c * chunk,
+                                   workspace=ws, out=out)
+    ms = events_ms(one_pass, 1)
+    flops = causal_pairs(0, L) * 2 * H_I * d_I
+    return {"L": L, "chunk": chunk, "chunks": n, "ms": ms, "tokens_per_s": L / (ms * 1e-3),
+            "indexer_flops": flops, "TFLOPs": flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
+def standalone_topk(B, Lq, Lk, q_pos0, k, seed=0):
+    """idxc_topk on materialised fp32 scores; algorithmic bytes = valid scores
+    read (4 B each) + indices written (4 B each)."""
+    import torch
+    import dsa_lightning_indexer_score_amd as idxc
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    s = torch.randn((B, Lq, Lk), generator=g, device="cuda")
+    ws_n = idxc.idxc_topk_workspace_bytes(B, Lq, Lk, q_pos0, k)
+    ws = torch.empty((max(ws_n, 256),), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, Lq, k), dtype=torch.int32, device="cuda")
+    ms = events_ms(lambda: idxc.idxc_topk(s, k, q_pos0=q_pos0, workspace=ws, out=out), 5)
+    nbytes = B * causal_pairs(q_pos0, Lq) * 4 + B * Lq * k * 4
+    del s
+    return {"shape": [B, Lq, Lk], "k": k, "ms": ms, "GBs": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
+# --------------------------------------------------------------------------- #
 # CPU oracle baseline on a bounded sample
 # --------------------------------------------------------------------------- #
 def cpu_baseline(cfg, n_rows=4096):
@@ -428,6 +489,21 @@ def main():
         del dlayers, dsets, dc12, dcF, dws, dcache
         torch.cuda.empty_cache()
 
+    # ------------------------------------------------- long context, top-k
+    if not args.skip_decode and args.only == "":
+        import idxc_inputs as gen
+        lc = long_context(gen.C5_L, gen.C5_CHUNK)
+        log("long context L=%d in %d chunks: %.1f ms, %.0f TFLOP/s indexer"
+            % (lc["L"], lc["chunks"], lc["ms"], lc["TFLOPs"]))
+        extra["long_context_indexer_topk"] = lc
+        torch.cuda.empty_cache()
+        tk = {"decode_rows": standalone_topk(64, 1, 65536, 65535, 2048),
+              "prefill_rows": standalone_topk(1, 8192, 8192, 0, 2048)}
+        log("standalone top-k: %.0f GB/s (64 x 65536), %.0f GB/s (8192 x 8192 causal)"
+            % (tk["decode_rows"]["GBs"], tk["prefill_rows"]["GBs"]))
+        extra["standalone_topk"] = tk
+        torch.cuda.empty_cache()
+
     # ------------------------------------------------------------------ report
     cfg = gen.C3_12F
     s12 = res.get("prefill_12F")
@@ -463,7 +539,13 @@ def main():
                     "gathered_bytes": attn_bytes(cfg),
                     "launch_ms": att_ms}
         dominant, other = (roof_idx, roof_att) if idx_total >= att_total else (roof_att, roof_idx)
+        # idealised stack: every F layer's indexer and every layer's attention
+        # at the bf16 MFMA peak
+        t_roof = (nF * indexer_flops(cfg) + cfg.n_layers * attn_flops(cfg)) / (
+            PEAK_BF16_TFLOPS * 1e12) * 1e3
         extra.update({
+            "stack_roofline_ms_12F": t_roof,
+            "stack_roofline_frac_12F": (t_roof / (s12 * 1e3)) if s12 else None,
             "prefill_allF_tokens_per_s": cfg.B * cfg.Lq / sF if sF else None,
             "prefill_allF_ms_per_step": sF * 1e3 if sF else None,
             "prefill_speedup_12F_vs_allF": (sF / s12) if (sF and s12) else None,

@@ -15,7 +15,7 @@ from . import _lib
 from ._lib import IdxcDims, IdxcError, IdxcLayer
 
 __all__ = ["idxc_version", "idxc_validate_pattern", "idxc_schedule", "idxc_indexer_scores",
-           "idxc_topk", "idxc_topk_workspace_bytes", "idxc_workspace_bytes", "idxc_indexer_topk", "idxc_sparse_attn", "idxc_sparse_attn_workspace_bytes",
+           "idxc_topk", "idxc_topk_workspace_bytes", "idxc_workspace_bytes", "idxc_indexer_topk", "idxc_sparse_attn", "idxc_sparse_attn_workspace_bytes", "idxc_overlap",
            "idxc_layer_stack_forward", "make_dims", "IdxcError", "StackCall"]
 
 
@@ -213,6 +213,25 @@ def idxc_layer_stack_forward(pattern: str, layers: Sequence[Dict[str, torch.Tens
                                             _stream(stream)))
     return dict(out=outs, indexer_calls=calls.value, index_cache=index_cache,
                 debug_indices=dbg)
+
+
+def idxc_overlap(a, b, Lk: int, stream=None):
+    """Per-row |A ∩ B|, overlap |A ∩ B| / |A| and Jaccard |A ∩ B| / |A ∪ B| of two
+    [B, Lq, k] int32 index tensors (valid entries as sets, -1 ignored).
+    Returns (inter int32 [B, Lq], overlap fp32 [B, Lq], jaccard fp32 [B, Lq])."""
+    lib = _lib.load()
+    if a.shape != b.shape or a.dim() != 3:
+        raise ValueError("a and b must be [B, Lq, k] tensors of one shape")
+    B, Lq, k = a.shape
+    d = make_dims(B, Lq, Lk, Lk - Lq, k=k)
+    dev = a.device
+    inter = torch.empty((B, Lq), dtype=torch.int32, device=dev)
+    ov = torch.empty((B, Lq), dtype=torch.float32, device=dev)
+    jac = torch.empty((B, Lq), dtype=torch.float32, device=dev)
+    _lib.check(lib.idxc_overlap(_ptr(a, "a", torch.int32), _ptr(b, "b", torch.int32),
+                                ctypes.byref(d), _ptr(inter, "inter"), _ptr(ov, "overlap"),
+                                _ptr(jac, "jaccard"), _stream(stream)))
+    return inter, ov, jac
 
 
 class StackCall:

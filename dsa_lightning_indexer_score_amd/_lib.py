@@ -32,7 +32,7 @@ EXPORTED = (
     "idxc_last_error", "idxc_version", "idxc_validate_pattern", "idxc_schedule",
     "idxc_indexer_scores", "idxc_topk", "idxc_topk_workspace_bytes", "idxc_workspace_bytes",
     "idxc_indexer_topk", "idxc_sparse_attn", "idxc_sparse_attn_workspace_bytes",
-    "idxc_layer_stack_forward",
+    "idxc_layer_stack_forward", "idxc_overlap",
 )
 
 
@@ -83,6 +83,7 @@ def load() -> ctypes.CDLL:
         "idxc_layer_stack_forward": ([ctypes.c_char_p, i32, P(IdxcLayer), P(IdxcDims),
                                       ctypes.c_float, vp, vp, sz, P(i32), vp, vp],
                                      ctypes.c_int),
+        "idxc_overlap": ([vp, vp, P(IdxcDims), vp, vp, vp, vp], ctypes.c_int),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)

@@ -55,6 +55,8 @@ constexpr int kMaxLk = 1 << 24;
 
 // Common size checks. need: bit 0 = indexer fields, bit 1 = attention fields,
 // bit 2 = k.
+constexpr int kMaxOverlapLk = 262144;  // two LDS bitmaps of Lk bits (64 KB)
+
 int check_dims(const idxc_dims* d, int need) {
   if (d == nullptr) return fail(IDXC_ERR_INVALID_ARG, "dims is NULL");
   if (d->B < 1 || d->Lq < 1 || d->Lk < 1)
@@ -414,6 +416,23 @@ int idxc_sparse_attn(const void* q, const void* k, const void* v, const int32_t*
   return hip_status(launch_sparse_attn(attn_args(q, k, v, indices, dims, scale, out, ws),
                                        static_cast<hipStream_t>(hip_stream)),
                     "sparse_attn launch");
+}
+
+int idxc_overlap(const int32_t* a, const int32_t* b, const idxc_dims* dims, int32_t* inter,
+                 float* overlap, float* jaccard, void* hip_stream) {
+  int r = check_dims(dims, 4);
+  if (r != IDXC_OK) return r;
+  auto aligned4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+  if (a == nullptr || b == nullptr) return fail(IDXC_ERR_INVALID_ARG, "a and b must not be NULL");
+  const void* ptrs[5] = {a, b, inter, overlap, jaccard};
+  for (const void* p : ptrs)
+    if (p != nullptr && !aligned4(p)) return fail(IDXC_ERR_INVALID_ARG, "pointer not 4-byte aligned");
+  if (overlap_lds_bytes(dims->Lk) > overlap_lds_bytes(kMaxOverlapLk))
+    return fail(IDXC_ERR_UNSUPPORTED, "Lk = %d above %d for idxc_overlap", dims->Lk, kMaxOverlapLk);
+  if (inter == nullptr && overlap == nullptr && jaccard == nullptr) return ok();
+  return hip_status(launch_overlap(a, b, dims->B * dims->Lq, dims->k, dims->Lk, inter, overlap,
+                                   jaccard, static_cast<hipStream_t>(hip_stream)),
+                    "overlap launch");
 }
 
 int idxc_layer_stack_forward(const char* pattern, int32_t n_layers, const idxc_layer* layers,

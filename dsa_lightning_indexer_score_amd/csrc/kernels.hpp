@@ -77,4 +77,10 @@ int attn_splits(int B, int Lq, int k);
 size_t attn_part_o_bytes(int B, int Lq, int H, int D, int nsplit);
 size_t attn_workspace_bytes(int B, int Lq, int H, int D, int k);
 
+// Cross-layer agreement of two [rows, k] index tensors (per-row |A ∩ B|,
+// overlap, Jaccard; any output may be null).
+size_t overlap_lds_bytes(int Lk);
+hipError_t launch_overlap(const int32_t* a, const int32_t* b, int rows, int k, int Lk,
+                          int32_t* inter, float* overlap, float* jaccard, hipStream_t st);
+
 }  // namespace idxc

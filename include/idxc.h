@@ -194,6 +194,19 @@ int idxc_layer_stack_forward(const char* pattern, int32_t n_layers,
                              size_t workspace_bytes, int32_t* indexer_calls,
                              int32_t* debug_indices, void* hip_stream);
 
+/* Cross-layer agreement of two index tensors a, b [B,Lq,k] int32 (DEVICE;
+ * entries are positions in [0, Lk) or -1, in any order; other values are
+ * ignored). Per row, over the valid entries taken as sets: inter = |A ∩ B|,
+ * overlap = |A ∩ B| / |A| (1 if both sets are empty, 0 if only A is) and
+ * jaccard = |A ∩ B| / |A ∪ B| (1 if both are empty), the measures
+ * "IndexCache：跨层复用稀疏注意力的索引" uses for how much adjacent layers'
+ * top-k selections agree (with |A| = k, overlap = |A ∩ B| / k). Outputs are
+ * DEVICE buffers of B*Lq entries; any may be NULL. Uses B, Lq, Lk, k.
+ * Lk above 262144 returns IDXC_ERR_UNSUPPORTED (two bitmaps of Lk bits live
+ * in LDS). Asynchronous on hip_stream. */
+int idxc_overlap(const int32_t* a, const int32_t* b, const idxc_dims* dims, int32_t* inter,
+                 float* overlap, float* jaccard, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

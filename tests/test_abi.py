@@ -170,3 +170,16 @@ def test_stack_errors_before_launch(lib):
     assert f(*args(b"FSSS", 4)) == _lib.IDXC_ERR_INVALID_ARG
     assert "layers[2].q" in lib.idxc_last_error().decode()
     assert calls.value == -7  # nothing ran
+
+
+def test_overlap_argument_errors(lib):
+    f = lib.idxc_overlap
+    d = ctypes.byref(_dims(Lq=8, Lk=64, k=16))
+    assert f(None, P(), d, P(), None, None, None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), P(FAKE + 2), d, P(), None, None, None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), P(), ctypes.byref(_dims(k=0)), P(), None, None, None) == \
+        _lib.IDXC_ERR_INVALID_ARG
+    big = ctypes.byref(_dims(Lq=1, Lk=262145, q_pos0=262144, k=16))
+    assert f(P(), P(), big, P(), None, None, None) == _lib.IDXC_ERR_UNSUPPORTED
+    # nothing requested: no launch
+    assert f(P(), P(), d, None, None, None, None) == _lib.IDXC_OK

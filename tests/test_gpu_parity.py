@@ -372,3 +372,59 @@ def test_stack_random_small_overlap():
                                   want2[:, rows], cfg.scale)
     err = np.abs(res["out"][3].float().cpu().numpy()[:, rows] - ref).max()
     assert err <= ATOL
+
+
+# --------------------------------------------------------------------------- #
+# cross-layer agreement of index sets
+# --------------------------------------------------------------------------- #
+def _set_stats(a, b):
+    inter = np.zeros(a.shape[:-1], dtype=np.int64)
+    ov = np.zeros(a.shape[:-1])
+    jac = np.zeros(a.shape[:-1])
+    for ix in np.ndindex(*a.shape[:-1]):
+        A = set(int(x) for x in a[ix] if x >= 0)
+        Bs = set(int(x) for x in b[ix] if x >= 0)
+        inter[ix] = len(A & Bs)
+        ov[ix] = oracle.overlap(a[ix], b[ix])
+        jac[ix] = oracle.jaccard(a[ix], b[ix])
+    return inter, ov, jac
+
+
+def test_overlap_matches_oracle_on_random_sets():
+    rng = np.random.default_rng(11)
+    B, Lq, k, Lk = 2, 300, 64, 5000
+    a = rng.integers(0, 200, size=(B, Lq, k)).astype(np.int32)   # many duplicates
+    b = rng.integers(0, 200, size=(B, Lq, k)).astype(np.int32)
+    a[rng.random(a.shape) < 0.2] = -1
+    b[rng.random(b.shape) < 0.2] = -1
+    a[0, 0] = -1                      # empty A, nonempty B
+    a[0, 1] = -1
+    b[0, 1] = -1                      # both empty
+    b[1, 5] = a[1, 5][::-1]           # same set, other order
+    b[1, 6] = np.where(a[1, 6] >= 0, a[1, 6] + 4000, -1)   # disjoint
+    inter, ov, jac = idxc.idxc_overlap(cu(torch.from_numpy(a)), cu(torch.from_numpy(b)), Lk)
+    torch.cuda.synchronize()
+    wi, wo, wj = _set_stats(a, b)
+    assert np.array_equal(inter.cpu().numpy(), wi)
+    assert np.allclose(ov.cpu().numpy(), wo, rtol=0, atol=1e-6)
+    assert np.allclose(jac.cpu().numpy(), wj, rtol=0, atol=1e-6)
+    assert ov[0, 0].item() == 0.0 and ov[0, 1].item() == 1.0 and jac[0, 1].item() == 1.0
+    assert ov[1, 5].item() == 1.0 and jac[1, 6].item() == 0.0
+
+
+def test_overlap_of_adjacent_layer_selections():
+    # two layers' top-k selections (as an index cache holds them) against the
+    # oracle's own selections
+    B, L, k = 1, 1200, 128
+    q0, k0, w0 = gen.indexer_inputs(B, L, L, 64, 128, kind="normal", seed=21, idx_std=128 ** -0.5)
+    q1, k1, w1 = gen.indexer_inputs(B, L, L, 64, 128, kind="normal", seed=22, idx_std=128 ** -0.5)
+    a = idxc.idxc_indexer_topk(cu(q0), cu(k0), cu(w0), k, order="position")
+    b = idxc.idxc_indexer_topk(cu(q1), cu(k1), cu(w1), k)
+    inter, ov, jac = idxc.idxc_overlap(a, b, L)
+    torch.cuda.synchronize()
+    wi, wo, wj = _set_stats(a.cpu().numpy(), b.cpu().numpy())
+    assert np.array_equal(inter.cpu().numpy(), wi)
+    assert np.allclose(ov.cpu().numpy(), wo, rtol=0, atol=1e-6)
+    assert np.allclose(jac.cpu().numpy(), wj, rtol=0, atol=1e-6)
+    # rows with t + 1 <= k select every position in both layers
+    assert np.all(ov.cpu().numpy()[0, :k] == 1.0)
