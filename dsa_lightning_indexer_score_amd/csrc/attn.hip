@@ -182,10 +182,12 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
                                                          (ks * 2 + (lane >> 5)) * 16);
       s = mfma32(ka, qb[ks], s);
     }
-    // ---- online softmax in the exp2 domain with a lazily moved maximum
+    // ---- online softmax in the exp2 domain with a lazily moved maximum. The
+    // scale (> 0) commutes with the maximum, so the raw scores' maximum is
+    // scaled once and each exponent is one fma, s * sl2 - m.
     float x[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = s[i] * sl2;
+    for (int i = 0; i < 16; ++i) x[i] = s[i];
     if (__builtin_expect(vm_c != 0xFFFFFFFFu, 0)) {  // wave-uniform: padded entries
 #pragma unroll
       for (int i = 0; i < 16; ++i)
@@ -194,7 +196,7 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     float mloc = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, x[i]);
-    const float mblk = pair_max(mloc);
+    const float mblk = pair_max(mloc) * sl2;
     const bool move = mblk > m_used + kLazyLog2;
     if (ballot(move)) {
       const float mnew = move ? mblk : m_used;
@@ -204,14 +206,14 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
       m_used = mnew;
     }
-    // x - m_used <= 8 keeps P <= 256; -inf maps to 0
+    // x * sl2 - m_used <= 8 keeps P <= 256; -inf maps to 0
     const float mu = (m_used == -INFINITY) ? 0.0f : m_used;
     u32x4 pw[2];
     float psum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(x[i] - mu);
-      const float p1 = __builtin_amdgcn_exp2f(x[i + 1] - mu);
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(x[i], sl2, -mu));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(x[i + 1], sl2, -mu));
       psum += p0 + p1;
       pw[i >> 3][(i & 7) >> 1] = pack_bf16x2(p0, p1);
     }
