@@ -644,7 +644,7 @@ void indexer_split_topk_kernel(const uint16_t* __restrict__ q_idx,
   __syncthreads();
 
   u32x2* seg = part + row * (size_t)nchunks * k + (size_t)chunk * k;
-  const int kk = block_topk_collect<false>(skey, nullptr, c0, n, k, sel,
+  const int kk = block_topk_collect(skey, n, k, sel, [&](int e) { return c0 + e; },
                                            [&](int slot, uint32_t key, uint32_t pos) {
                                              seg[slot] = u32x2{key, pos};
                                            });

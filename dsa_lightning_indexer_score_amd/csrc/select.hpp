@@ -2,9 +2,10 @@
 // selection kernels and the decode indexer). Internal to libidxc.
 //
 // Input: n order-preserving 32-bit keys skey[0..n) in increasing position
-// order, with positions spos[e] (explicit) or pos0 + e (implicit). Output:
-// the min(k, n) best entries under (key desc, position asc), emitted in
-// position order through emit(slot, key, position), slot = 0..min(k,n)-1.
+// order; pos_of(e) gives the position of entry e and is called only for the
+// winners. Output: the min(k, n) best entries under (key desc, position
+// asc), emitted in position order through emit(slot, key, position),
+// slot = 0..min(k,n)-1.
 //
 // Method: the keys lie in [lo, lo + R); each pass histograms them into
 // kSelBins equal-width bins of that range, finds the bin holding the rem-th
@@ -49,9 +50,9 @@ __device__ __forceinline__ int sel_excl_scan(int v, int* scan, int* total) {
   return off + incl - v;
 }
 
-template <bool EXPLICIT_POS, typename Emit>
-__device__ int block_topk_collect(const uint32_t* skey, const uint32_t* spos, int pos0, int n,
-                                  int k, SelectSmem& sm, Emit emit) {
+template <typename PosOf, typename Emit>
+__device__ int block_topk_collect(const uint32_t* skey, int n, int k, SelectSmem& sm,
+                                  PosOf pos_of, Emit emit) {
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   // ---- select the k-th best key (only needed when n > k). The keys lie in
@@ -146,7 +147,7 @@ __device__ int block_topk_collect(const uint32_t* skey, const uint32_t* spos, in
   // the `rem` lowest positions)
   int out_count = 0, eq_seen = 0;
   for (int base = 0; base < n; base += kSelChunk) {
-    uint32_t keys[kSelPerThread], poss[kSelPerThread];
+    uint32_t keys[kSelPerThread];
     unsigned gt_bits = 0u, eq_bits = 0u;
     const int e0 = base + tid * kSelPerThread;
     if (e0 + kSelPerThread <= n) {
@@ -158,18 +159,6 @@ __device__ int block_topk_collect(const uint32_t* skey, const uint32_t* spos, in
         keys[j] = k0[j];
         keys[4 + j] = k1[j];
       }
-      if (!EXPLICIT_POS) {
-#pragma unroll
-        for (int j = 0; j < kSelPerThread; ++j) poss[j] = (uint32_t)(pos0 + e0 + j);
-      } else {
-        const u32x4 p0 = *reinterpret_cast<const u32x4*>(spos + e0);
-        const u32x4 p1 = *reinterpret_cast<const u32x4*>(spos + e0 + 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          poss[j] = p0[j];
-          poss[4 + j] = p1[j];
-        }
-      }
 #pragma unroll
       for (int j = 0; j < kSelPerThread; ++j) {
         if (select_all || keys[j] > hi || (take_range && keys[j] >= lo)) gt_bits |= 1u << j;
@@ -180,10 +169,8 @@ __device__ int block_topk_collect(const uint32_t* skey, const uint32_t* spos, in
       for (int j = 0; j < kSelPerThread; ++j) {
         const int e = e0 + j;
         keys[j] = 0u;
-        poss[j] = 0u;
         if (e < n) {
           keys[j] = skey[e];
-          poss[j] = (!EXPLICIT_POS) ? (uint32_t)(pos0 + e) : spos[e];
           if (select_all || keys[j] > hi || (take_range && keys[j] >= lo)) gt_bits |= 1u << j;
           else if (keys[j] >= lo) eq_bits |= 1u << j;
         }
@@ -205,7 +192,7 @@ __device__ int block_topk_collect(const uint32_t* skey, const uint32_t* spos, in
 #pragma unroll
     for (int j = 0; j < kSelPerThread; ++j) {
       if (keep_bits & (1u << j)) {
-        emit(pos, keys[j], poss[j]);
+        emit(pos, keys[j], (uint32_t)pos_of(e0 + j));
         ++pos;
       }
     }

@@ -31,16 +31,19 @@ namespace {
 constexpr int kThreads = kSelThreads;
 constexpr int kBatch = 8;  // staged loads in flight per thread
 
+// LDS: selection scratch and segment offsets, then the staged keys, then
+// (multi-segment candidate lists only) the staged positions, then (score
+// order only) the sort buffer. Position-order output needs no sort buffer,
+// and single-segment lists read their winners' positions back from memory,
+// so the common candidate case stages keys alone.
 struct Smem {
-  uint64_t sortbuf[kMaxK];
   SelectSmem sel;
   int seg_off[kMaxSegments + 1];
 };
-
-// LDS bytes before the staged input (keeps the stage 16-byte aligned).
 constexpr size_t kSmemBytes = (sizeof(Smem) + 15) / 16 * 16;
+constexpr size_t kSortBytes = (size_t)kMaxK * 8;
 
-enum SrcKind { kSrcRow = 0, kSrcCand = 1 };
+enum SrcKind { kSrcRow = 0, kSrcCand = 1, kSrcCand1 = 2 };
 enum OutKind { kOutFinal = 0, kOutPart = 1 };
 
 // Descending bitonic sort of 2048 64-bit words held 8 per thread (thread t
@@ -92,14 +95,17 @@ __device__ __forceinline__ void sort2048_regs(uint64_t (&v)[8], uint64_t* lds, i
 }
 
 // One workgroup = one (row, chunk). SRC kSrcRow: positions [c0, c1) of a score
-// row. SRC kSrcCand: the concatenation of nseg segments of a row.
+// row. SRC kSrcCand: the concatenation of nseg segments of a row (positions
+// staged too). SRC kSrcCand1: one segment (positions read back for winners).
+// The sort buffer sits at byte sort_off of the dynamic LDS.
 template <int SRC, int OUT>
 __global__ __launch_bounds__(kThreads)
-void topk_kernel(TopkArgs a, int chunk_len, int nchunks) {
+void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int sort_off) {
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   Smem& sm = *reinterpret_cast<Smem*>(dyn);
   uint32_t* skey = reinterpret_cast<uint32_t*>(dyn + kSmemBytes);
   uint32_t* spos = nullptr;  // SRC kSrcCand: positions after the keys
+  uint64_t* sortbuf = reinterpret_cast<uint64_t*>(dyn + sort_off);
 
   const int tid = threadIdx.x;
   const int k = a.k;
@@ -126,6 +132,22 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks) {
       for (int j = 0; j < kBatch; ++j) {
         const int e = base + j * kThreads + tid;
         if (e < n) skey[e] = order_key(v[j]);
+      }
+    }
+  } else if (SRC == kSrcCand1) {
+    n = a.cand_count[row];
+    const u32x2* src = a.cand + (size_t)row * a.seg_cap;
+    for (int base = 0; base < n; base += kThreads * kBatch) {
+      uint32_t v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int e = base + j * kThreads + tid;
+        v[j] = e < n ? src[e].x : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int e = base + j * kThreads + tid;
+        if (e < n) skey[e] = v[j];
       }
     }
   } else {
@@ -166,11 +188,16 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks) {
 
   u32x2* part = nullptr;
   if (OUT == kOutPart) part = a.part + ((size_t)row * nchunks + chunk) * a.k;
-  uint64_t* sortbuf = sm.sortbuf;
   int32_t* orow = a.out + (size_t)row * k;
   const bool pos_order = OUT == kOutFinal && a.pos_order;
-  const int kk = block_topk_collect<SRC == kSrcCand>(
-      skey, spos, pos0, n, k, sm.sel, [&](int slot, uint32_t key, uint32_t pos) {
+  const u32x2* cand1 = (SRC == kSrcCand1) ? a.cand + (size_t)row * a.seg_cap : nullptr;
+  auto pos_of = [&](int e) -> uint32_t {
+    if (SRC == kSrcRow) return (uint32_t)(pos0 + e);
+    if (SRC == kSrcCand) return spos[e];
+    return cand1[e].y;
+  };
+  const int kk = block_topk_collect(
+      skey, n, k, sm.sel, pos_of, [&](int slot, uint32_t key, uint32_t pos) {
         if (OUT == kOutPart) part[slot] = u32x2{key, pos};
         else if (pos_order) orow[slot] = (int32_t)pos;
         else sortbuf[slot] = (((uint64_t)key) << 32) | (uint64_t)(~pos);
@@ -193,9 +220,9 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int idx = tid * 8 + j;
-      v[j] = idx < kk ? sm.sortbuf[idx] : 0ull;
+      v[j] = idx < kk ? sortbuf[idx] : 0ull;
     }
-    sort2048_regs(v, sm.sortbuf, tid);
+    sort2048_regs(v, sortbuf, tid);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int idx = tid * 8 + j;
@@ -203,18 +230,18 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks) {
     }
     return;
   }
-  for (int e = kk + tid; e < P; e += kThreads) sm.sortbuf[e] = 0ull;
+  for (int e = kk + tid; e < P; e += kThreads) sortbuf[e] = 0ull;
   __syncthreads();
   for (int size = 2; size <= P; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int i = tid; i < (P >> 1); i += kThreads) {
         const int lo = 2 * i - (i & (stride - 1));
         const int hi = lo + stride;
-        const uint64_t x = sm.sortbuf[lo], y = sm.sortbuf[hi];
+        const uint64_t x = sortbuf[lo], y = sortbuf[hi];
         const bool desc = (lo & size) == 0;
         if ((x < y) == desc) {
-          sm.sortbuf[lo] = y;
-          sm.sortbuf[hi] = x;
+          sortbuf[lo] = y;
+          sortbuf[hi] = x;
         }
       }
       __syncthreads();
@@ -222,14 +249,18 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks) {
   }
 
   for (int j = tid; j < k; j += kThreads) {
-    orow[j] = (j < kk) ? (int32_t)(~(uint32_t)(sm.sortbuf[j] & 0xFFFFFFFFull)) : -1;
+    orow[j] = (j < kk) ? (int32_t)(~(uint32_t)(sortbuf[j] & 0xFFFFFFFFull)) : -1;
   }
 }
 
+// stage_bytes: the staged input; the sort buffer follows it unless the output
+// is in position order (or is a stage-1 part)
 template <int SRC, int OUT>
 hipError_t launch_one(const TopkArgs& a, int chunk_len, int nchunks, size_t stage_bytes,
                       hipStream_t st) {
-  const size_t shmem = kSmemBytes + stage_bytes;
+  const size_t sort_off = kSmemBytes + (stage_bytes + 15) / 16 * 16;
+  const bool need_sort = OUT == kOutFinal && !a.pos_order;
+  const size_t shmem = sort_off + (need_sort ? kSortBytes : 0);
   auto fn = topk_kernel<SRC, OUT>;
   if (shmem > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
@@ -237,7 +268,7 @@ hipError_t launch_one(const TopkArgs& a, int chunk_len, int nchunks, size_t stag
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(fn, dim3((unsigned)(a.rows * nchunks)), dim3(kThreads), shmem, st, a,
-                     chunk_len, nchunks);
+                     chunk_len, nchunks, (int)sort_off);
   return hipGetLastError();
 }
 
@@ -254,11 +285,13 @@ size_t topk_part_bytes(int rows, int Lk, int k) {
 hipError_t launch_topk(const TopkArgs& a0, hipStream_t st) {
   TopkArgs a = a0;
   if (a.cand) {
-    // candidate lists (one or more position-ordered segments per row); keys
-    // then positions, each area a multiple of 16 bytes
+    // candidate lists (one or more position-ordered segments per row); keys,
+    // then positions when there are several segments, each area a multiple
+    // of 16 bytes
     a.stage_cap = (a.stage_cap + 3) / 4 * 4;
-    const size_t stage = (size_t)a.stage_cap * 8;
-    return launch_one<kSrcCand, kOutFinal>(a, 0, 1, stage, st);
+    if (a.nseg == 1)
+      return launch_one<kSrcCand1, kOutFinal>(a, 0, 1, (size_t)a.stage_cap * 4, st);
+    return launch_one<kSrcCand, kOutFinal>(a, 0, 1, (size_t)a.stage_cap * 8, st);
   }
   const int nch = topk_row_chunks(a.Lk);
   if (nch <= 1) {
