@@ -271,51 +271,59 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
 }
 
 // Combine the nsplit partial results of each (row, head): weights
-// l_s * 2^(m_s - max m) over the slices, applied to the normalised partials.
-// One workgroup per row: the weights go through LDS, the partial outputs are
-// read 8 bf16 at a time.
+// l_s * 2^(m_s - max m) over the slices, normalised, applied to the
+// normalised partials. One workgroup per (row, group of kMergeHeads heads):
+// 32 lanes per head compute its slice weights together (shuffle reductions),
+// then each thread combines 4 consecutive outputs over the slices.
+constexpr int kMergeHeads = 8;
+
 __global__ __launch_bounds__(256)
 void attn_merge_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ part_ml,
-                       int H, int D, int nsplit, uint16_t* __restrict__ out) {
-  __shared__ float wgt[kMaxAttnSplits * 64];
-  __shared__ float inv[64];
-  const int row = blockIdx.x;
+                       int H, int D, int nsplit, int hgroups, uint16_t* __restrict__ out) {
+  __shared__ float wgt[kMergeHeads][kMaxAttnSplits];
+  const int row = blockIdx.x / hgroups;
+  const int hg = blockIdx.x % hgroups;
+  const int tid = threadIdx.x;
   const size_t u0 = (size_t)row * nsplit;
-  for (int h = threadIdx.x; h < H; h += blockDim.x) {
-    float mmax = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) mmax = fmaxf(mmax, part_ml[((u0 + s) * H + h) * 2]);
-    float wsum = 0.0f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float ms = part_ml[((u0 + s) * H + h) * 2];
-      const float ls = part_ml[((u0 + s) * H + h) * 2 + 1];
-      const float wv = (ms == -INFINITY || ls <= 0.0f) ? 0.0f : ls * exp2f(ms - mmax);
-      wgt[s * 64 + h] = wv;
-      wsum += wv;
+  {
+    const int hl = tid >> 5, sl = tid & 31;
+    const int h = hg * kMergeHeads + hl;
+    float m = -INFINITY, l = 0.0f;
+    if (h < H && sl < nsplit) {
+      m = part_ml[((u0 + sl) * H + h) * 2];
+      l = part_ml[((u0 + sl) * H + h) * 2 + 1];
     }
-    inv[h] = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+    float mmax = m;
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, off, 32));
+    const float wv = (m == -INFINITY || l <= 0.0f) ? 0.0f : l * exp2f(m - mmax);
+    float wsum = wv;
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off, 32);
+    wgt[hl][sl] = wsum > 0.0f ? wv / wsum : 0.0f;
   }
   __syncthreads();
-  const int nvec = H * D / 8;
-  for (int e8 = threadIdx.x; e8 < nvec; e8 += blockDim.x) {
-    const int h = (e8 * 8) / D;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < nsplit; ++s) {
-      const float wv = wgt[s * 64 + h];
-      const u32x4 v = *reinterpret_cast<const u32x4*>(part_o + (u0 + s) * H * D + (size_t)e8 * 8);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[2 * j] += wv * __uint_as_float(v[j] << 16);
-        acc[2 * j + 1] += wv * __uint_as_float(v[j] & 0xFFFF0000u);
-      }
-    }
-    u32x4 o;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      o[j] = (uint32_t)f32_to_bf16(acc[2 * j] * inv[h]) |
-             ((uint32_t)f32_to_bf16(acc[2 * j + 1] * inv[h]) << 16);
-    }
-    *reinterpret_cast<u32x4*>(out + (size_t)row * H * D + (size_t)e8 * 8) = o;
+  const int e = tid * 4;  // 4 consecutive outputs of head hl
+  const int hl = e / D;
+  const int d = e % D;
+  const int h = hg * kMergeHeads + hl;
+  if (hl >= kMergeHeads || h >= H) return;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const uint16_t* src = part_o + (u0 * H + h) * D + d;
+  const size_t stride = (size_t)H * D;  // next slice
+#pragma unroll 4
+  for (int s = 0; s < nsplit; ++s) {
+    const float wv = wgt[hl][s];
+    const u32x2 v = *reinterpret_cast<const u32x2*>(src + s * stride);
+    acc[0] += wv * __uint_as_float(v[0] << 16);
+    acc[1] += wv * __uint_as_float(v[0] & 0xFFFF0000u);
+    acc[2] += wv * __uint_as_float(v[1] << 16);
+    acc[3] += wv * __uint_as_float(v[1] & 0xFFFF0000u);
   }
+  u32x2 o;
+  o[0] = pack_bf16x2(acc[0], acc[1]);
+  o[1] = pack_bf16x2(acc[2], acc[3]);
+  *reinterpret_cast<u32x2*>(out + ((size_t)row * H + h) * D + d) = o;
 }
 
 template <int D, int HB>
@@ -339,8 +347,9 @@ hipError_t launch(const AttnArgs& a, int nsplit, hipStream_t st) {
                      a.out, po, pml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)(a.B * a.Lq)), dim3(256), 0, st, po, pml,
-                     a.H, a.D, nsplit, a.out);
+  const int hgroups = (a.H + kMergeHeads - 1) / kMergeHeads;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)(a.B * a.Lq * hgroups)), dim3(256), 0, st,
+                     po, pml, a.H, a.D, nsplit, hgroups, a.out);
   return hipGetLastError();
 }
 
@@ -352,10 +361,11 @@ size_t attn_part_o_bytes(int B, int Lq, int H, int D, int nsplit) {
 }
 
 int attn_splits(int B, int Lq, int k) {
-  // Enough units to fill the chip (about 1024), at least 128 keys each.
+  // About 512 units (two per CU: each runs a few key blocks, so fewer, longer
+  // units pipeline better than filling every slot), at least 128 keys each.
   const long long rows = (long long)B * Lq;
   int ns = 1;
-  while (rows * ns < 1024 && ns * 2 * 128 <= k && ns < kMaxAttnSplits) ns *= 2;
+  while (rows * ns < 512 && ns * 2 * 128 <= k && ns < kMaxAttnSplits) ns *= 2;
   return ns;
 }
 
