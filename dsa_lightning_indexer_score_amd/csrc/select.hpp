@@ -18,21 +18,24 @@
 
 namespace idxc {
 
-constexpr int kSelThreads = 256;
-constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kSelThreads = 256;  // default workgroup size
 constexpr int kSelBins = 2048;
 constexpr int kSelPerThread = 8;  // ordered pass: consecutive entries per thread
-constexpr int kSelChunk = kSelThreads * kSelPerThread;
 
-struct SelectSmem {
+// Scratch of a selection by an NT-thread workgroup.
+template <int NT = kSelThreads>
+struct SelectSmemT {
   uint32_t hist[kSelBins];
-  int scan[kSelWaves];
+  int scan[NT / kWave];
   int bcast[4];
-  uint32_t kred[2 * kSelWaves];
+  uint32_t kred[2 * (NT / kWave)];
 };
+using SelectSmem = SelectSmemT<>;
 
-// Block-wide exclusive prefix sum (kSelThreads threads); *total = block sum.
+// Block-wide exclusive prefix sum (NT threads); *total = block sum.
+template <int NT>
 __device__ __forceinline__ int sel_excl_scan(int v, int* scan, int* total) {
+  constexpr int kSelWaves = NT / kWave;
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int incl = wave_incl_scan(v);
@@ -50,9 +53,13 @@ __device__ __forceinline__ int sel_excl_scan(int v, int* scan, int* total) {
   return off + incl - v;
 }
 
-template <typename PosOf, typename Emit>
-__device__ int block_topk_collect(const uint32_t* skey, int n, int k, SelectSmem& sm,
+template <int NT = kSelThreads, typename PosOf, typename Emit>
+__device__ int block_topk_collect(const uint32_t* skey, int n, int k, SelectSmemT<NT>& sm,
                                   PosOf pos_of, Emit emit) {
+  constexpr int kSelThreads = NT;
+  constexpr int kSelWaves = NT / kWave;
+  constexpr int kSelChunk = NT * kSelPerThread;
+  static_assert(kSelBins % NT == 0, "bins split evenly over the threads");
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   // ---- select the k-th best key (only needed when n > k). The keys lie in
@@ -113,7 +120,7 @@ __device__ int block_topk_collect(const uint32_t* skey, int n, int k, SelectSmem
         local += cnts[q];
       }
       int total;
-      const int excl = sel_excl_scan(local, sm.scan, &total);
+      const int excl = sel_excl_scan<NT>(local, sm.scan, &total);
       if (excl < rem && excl + local >= rem) {
         int acc = excl;
 #pragma unroll
@@ -177,7 +184,7 @@ __device__ int block_topk_collect(const uint32_t* skey, int n, int k, SelectSmem
       }
     }
     int eq_total;
-    const int eq_excl = eq_seen + sel_excl_scan(__popc(eq_bits), sm.scan, &eq_total);
+    const int eq_excl = eq_seen + sel_excl_scan<NT>(__popc(eq_bits), sm.scan, &eq_total);
     unsigned keep_bits = gt_bits;
     int r = eq_excl;
 #pragma unroll
@@ -188,7 +195,7 @@ __device__ int block_topk_collect(const uint32_t* skey, int n, int k, SelectSmem
       }
     }
     int keep_total;
-    int pos = out_count + sel_excl_scan(__popc(keep_bits), sm.scan, &keep_total);
+    int pos = out_count + sel_excl_scan<NT>(__popc(keep_bits), sm.scan, &keep_total);
 #pragma unroll
     for (int j = 0; j < kSelPerThread; ++j) {
       if (keep_bits & (1u << j)) {

@@ -29,6 +29,9 @@ namespace idxc {
 namespace {
 
 constexpr int kThreads = kSelThreads;
+// multi-segment selections (few rows, up to 16384 candidates each) use wider
+// workgroups: there are few of them, so latency per row is what counts
+constexpr int kThreadsWide = 1024;
 constexpr int kBatch = 8;  // staged loads in flight per thread
 
 // LDS: selection scratch and segment offsets, then the staged keys, then
@@ -36,11 +39,15 @@ constexpr int kBatch = 8;  // staged loads in flight per thread
 // order only) the sort buffer. Position-order output needs no sort buffer,
 // and single-segment lists read their winners' positions back from memory,
 // so the common candidate case stages keys alone.
+template <int NT>
 struct Smem {
-  SelectSmem sel;
+  SelectSmemT<NT> sel;
   int seg_off[kMaxSegments + 1];
 };
-constexpr size_t kSmemBytes = (sizeof(Smem) + 15) / 16 * 16;
+template <int NT>
+constexpr size_t smem_bytes() {
+  return (sizeof(Smem<NT>) + 15) / 16 * 16;
+}
 constexpr size_t kSortBytes = (size_t)kMaxK * 8;
 
 enum SrcKind { kSrcRow = 0, kSrcCand = 1, kSrcCand1 = 2 };
@@ -98,12 +105,12 @@ __device__ __forceinline__ void sort2048_regs(uint64_t (&v)[8], uint64_t* lds, i
 // row. SRC kSrcCand: the concatenation of nseg segments of a row (positions
 // staged too). SRC kSrcCand1: one segment (positions read back for winners).
 // The sort buffer sits at byte sort_off of the dynamic LDS.
-template <int SRC, int OUT>
-__global__ __launch_bounds__(kThreads)
+template <int SRC, int OUT, int NT>
+__global__ __launch_bounds__(NT)
 void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int sort_off) {
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
-  Smem& sm = *reinterpret_cast<Smem*>(dyn);
-  uint32_t* skey = reinterpret_cast<uint32_t*>(dyn + kSmemBytes);
+  Smem<NT>& sm = *reinterpret_cast<Smem<NT>*>(dyn);
+  uint32_t* skey = reinterpret_cast<uint32_t*>(dyn + smem_bytes<NT>());
   uint32_t* spos = nullptr;  // SRC kSrcCand: positions after the keys
   uint64_t* sortbuf = reinterpret_cast<uint64_t*>(dyn + sort_off);
 
@@ -121,32 +128,32 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int sort_off) {
     pos0 = chunk * chunk_len;
     n = max(0, min(len, pos0 + chunk_len) - pos0);
     const float* src = a.scores + (size_t)row * a.Lk + pos0;
-    for (int base = 0; base < n; base += kThreads * kBatch) {
+    for (int base = 0; base < n; base += NT * kBatch) {
       float v[kBatch];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        const int e = base + j * kThreads + tid;
+        const int e = base + j * NT + tid;
         v[j] = e < n ? src[e] : 0.0f;
       }
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        const int e = base + j * kThreads + tid;
+        const int e = base + j * NT + tid;
         if (e < n) skey[e] = order_key(v[j]);
       }
     }
   } else if (SRC == kSrcCand1) {
     n = a.cand_count[row];
     const u32x2* src = a.cand + (size_t)row * a.seg_cap;
-    for (int base = 0; base < n; base += kThreads * kBatch) {
+    for (int base = 0; base < n; base += NT * kBatch) {
       uint32_t v[kBatch];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        const int e = base + j * kThreads + tid;
+        const int e = base + j * NT + tid;
         v[j] = e < n ? src[e].x : 0u;
       }
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        const int e = base + j * kThreads + tid;
+        const int e = base + j * NT + tid;
         if (e < n) skey[e] = v[j];
       }
     }
@@ -166,16 +173,16 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int sort_off) {
       const int off = sm.seg_off[s];
       const int cnt = sm.seg_off[s + 1] - off;
       const u32x2* src = a.cand + ((size_t)row * a.nseg + s) * a.seg_cap;
-      for (int base = 0; base < cnt; base += kThreads * kBatch) {
+      for (int base = 0; base < cnt; base += NT * kBatch) {
         u32x2 v[kBatch];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-          const int e = base + j * kThreads + tid;
+          const int e = base + j * NT + tid;
           v[j] = e < cnt ? src[e] : u32x2{0u, 0u};
         }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-          const int e = base + j * kThreads + tid;
+          const int e = base + j * NT + tid;
           if (e < cnt) {
             skey[off + e] = v[j].x;
             spos[off + e] = v[j].y;
@@ -196,7 +203,7 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int sort_off) {
     if (SRC == kSrcCand) return spos[e];
     return cand1[e].y;
   };
-  const int kk = block_topk_collect(
+  const int kk = block_topk_collect<NT>(
       skey, n, k, sm.sel, pos_of, [&](int slot, uint32_t key, uint32_t pos) {
         if (OUT == kOutPart) part[slot] = u32x2{key, pos};
         else if (pos_order) orow[slot] = (int32_t)pos;
@@ -207,14 +214,14 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int sort_off) {
     return;
   }
   if (pos_order) {  // winners are emitted in position order: no sort
-    for (int j = kk + tid; j < k; j += kThreads) orow[j] = -1;
+    for (int j = kk + tid; j < k; j += NT) orow[j] = -1;
     return;
   }
 
   // ---- bitonic sort, descending, of the kk winners padded to a power of two
   int P = 1;
   while (P < kk) P <<= 1;
-  if (P == kThreads * 8) {
+  if (NT == kThreads && P == NT * 8) {
     __syncthreads();
     uint64_t v[8];
 #pragma unroll
@@ -230,11 +237,11 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int sort_off) {
     }
     return;
   }
-  for (int e = kk + tid; e < P; e += kThreads) sortbuf[e] = 0ull;
+  for (int e = kk + tid; e < P; e += NT) sortbuf[e] = 0ull;
   __syncthreads();
   for (int size = 2; size <= P; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < (P >> 1); i += kThreads) {
+      for (int i = tid; i < (P >> 1); i += NT) {
         const int lo = 2 * i - (i & (stride - 1));
         const int hi = lo + stride;
         const uint64_t x = sortbuf[lo], y = sortbuf[hi];
@@ -248,26 +255,26 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int sort_off) {
     }
   }
 
-  for (int j = tid; j < k; j += kThreads) {
+  for (int j = tid; j < k; j += NT) {
     orow[j] = (j < kk) ? (int32_t)(~(uint32_t)(sortbuf[j] & 0xFFFFFFFFull)) : -1;
   }
 }
 
 // stage_bytes: the staged input; the sort buffer follows it unless the output
 // is in position order (or is a stage-1 part)
-template <int SRC, int OUT>
+template <int SRC, int OUT, int NT = kThreads>
 hipError_t launch_one(const TopkArgs& a, int chunk_len, int nchunks, size_t stage_bytes,
                       hipStream_t st) {
-  const size_t sort_off = kSmemBytes + (stage_bytes + 15) / 16 * 16;
+  const size_t sort_off = smem_bytes<NT>() + (stage_bytes + 15) / 16 * 16;
   const bool need_sort = OUT == kOutFinal && !a.pos_order;
   const size_t shmem = sort_off + (need_sort ? kSortBytes : 0);
-  auto fn = topk_kernel<SRC, OUT>;
+  auto fn = topk_kernel<SRC, OUT, NT>;
   if (shmem > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(fn, dim3((unsigned)(a.rows * nchunks)), dim3(kThreads), shmem, st, a,
+  hipLaunchKernelGGL(fn, dim3((unsigned)(a.rows * nchunks)), dim3(NT), shmem, st, a,
                      chunk_len, nchunks, (int)sort_off);
   return hipGetLastError();
 }
@@ -291,7 +298,7 @@ hipError_t launch_topk(const TopkArgs& a0, hipStream_t st) {
     a.stage_cap = (a.stage_cap + 3) / 4 * 4;
     if (a.nseg == 1)
       return launch_one<kSrcCand1, kOutFinal>(a, 0, 1, (size_t)a.stage_cap * 4, st);
-    return launch_one<kSrcCand, kOutFinal>(a, 0, 1, (size_t)a.stage_cap * 8, st);
+    return launch_one<kSrcCand, kOutFinal, kThreadsWide>(a, 0, 1, (size_t)a.stage_cap * 8, st);
   }
   const int nch = topk_row_chunks(a.Lk);
   if (nch <= 1) {
@@ -306,7 +313,7 @@ hipError_t launch_topk(const TopkArgs& a0, hipStream_t st) {
   b.nseg = nch;
   b.seg_cap = a.k;
   b.stage_cap = (nch * a.k + 3) / 4 * 4;
-  return launch_one<kSrcCand, kOutFinal>(b, 0, 1, (size_t)b.stage_cap * 8, st);
+  return launch_one<kSrcCand, kOutFinal, kThreadsWide>(b, 0, 1, (size_t)b.stage_cap * 8, st);
 }
 
 }  // namespace idxc
