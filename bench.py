@@ -477,6 +477,20 @@ def main():
                              index_cache=dcache, workspace=dws)
         dec["decode_12F"] = time_steps(dc12, args.decode_steps, args.warmup)
         dec["decode_allF"] = time_steps(dcF, args.decode_steps, args.warmup)
+        # the same decode steps replayed from captured HIP graphs (no host
+        # launch work inside a step)
+        graphs = {}
+        for name, call in (("12F", dc12), ("allF", dcF)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                call()
+            graphs[name] = g
+        torch.cuda.synchronize()
+        for name, g in graphs.items():
+            dec["graph_" + name] = time_steps(g.replay, args.decode_steps, args.warmup)
+        log("decode from graphs: 12-F %.3f ms/step, all-F %.3f ms/step"
+            % (dec["graph_12F"] * 1e3, dec["graph_allF"] * 1e3))
+        del graphs
         dec_idx_ms, dec_att_ms, dec_pass_ms = kernel_pass(d12, dlayers, dws, dcache,
                                                           args.decode_steps)
         log("decode: 12-F %.3f ms/step, all-F %.3f ms/step; per layer indexer+top-k %.3f ms, "
@@ -561,6 +575,10 @@ def main():
             "decode_speedup_12F_vs_allF": dec["decode_allF"] / dec["decode_12F"],
             "decode_12F_ms_per_step": dec["decode_12F"] * 1e3,
             "decode_allF_ms_per_step": dec["decode_allF"] * 1e3,
+            "decode_graph_12F_tokens_per_s": gen.C4_12F.B / dec["graph_12F"],
+            "decode_graph_allF_tokens_per_s": gen.C4_ALLF.B / dec["graph_allF"],
+            "decode_graph_12F_ms_per_step": dec["graph_12F"] * 1e3,
+            "decode_graph_allF_ms_per_step": dec["graph_allF"] * 1e3,
         })
     cpu = None
     if not args.skip_cpu:

@@ -428,3 +428,40 @@ def test_overlap_of_adjacent_layer_selections():
     assert np.allclose(jac.cpu().numpy(), wj, rtol=0, atol=1e-6)
     # rows with t + 1 <= k select every position in both layers
     assert np.all(ov.cpu().numpy()[0, :k] == 1.0)
+
+
+# --------------------------------------------------------------------------- #
+# the stack captured in a HIP graph
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("shape", ["decode", "prefill"])
+def test_stack_graph_replays_match_eager(shape):
+    import dataclasses
+    if shape == "decode":   # split indexer, two-stage selection, split attention + merge
+        cfg = dataclasses.replace(gen.C4_12F, name="g-decode", n_layers=3, pattern="FSF", B=4,
+                                  Lk=20000, q_pos0=19999)
+    else:                   # candidate indexer, selection, attention
+        cfg = dataclasses.replace(gen.C2, name="g-prefill", n_layers=3, pattern="FSF", Lq=1500,
+                                  Lk=1500, k=256)
+    _say("stack graph %s" % cfg.name)
+    layers = [{n: cu(t) for n, t in L.items()} for L in _layers(cfg)]
+    for L in layers:
+        L["out"] = torch.empty_like(L["q"])
+    call = idxc.StackCall(cfg.pattern, layers, cfg.k, cfg.scale, cfg.q_pos0)
+    call()
+    torch.cuda.synchronize()
+    want = [L["out"].clone() for L in layers]
+    want_cache = call.index_cache.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for L in layers:
+            L["out"].fill_(7.0)        # eager work between replays
+        call.index_cache.fill_(-5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(call.index_cache, want_cache), rep
+        for l, L in enumerate(layers):
+            assert torch.equal(L["out"], want[l]), (rep, l)
