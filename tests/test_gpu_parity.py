@@ -465,3 +465,99 @@ def test_stack_graph_replays_match_eager(shape):
         assert torch.equal(call.index_cache, want_cache), rep
         for l, L in enumerate(layers):
             assert torch.equal(L["out"], want[l]), (rep, l)
+
+
+# --------------------------------------------------------------------------- #
+# full sizes, in the launch configurations the benchmark times, checked on
+# sampled rows the oracle computes one by one
+# --------------------------------------------------------------------------- #
+def _oracle_rows(q_idx, k_idx, w, rows_t, k):
+    """Oracle top-k of single query rows: q_idx [1,n,H_I,d_I] / w [1,n,H_I] on
+    the host hold the sampled rows, rows_t their positions; k_idx [1,Lk,d_I]."""
+    kf = f64(k_idx)
+    out = []
+    for j, t in enumerate(rows_t):
+        sc = oracle.indexer_scores(f64(q_idx[:, j:j + 1]), kf, f64(w[:, j:j + 1]), int(t))
+        out.append(oracle.topk(sc, k, int(t))[0, 0])
+    return np.stack(out)
+
+
+def _check_selection(got_rows, want_rows):
+    ovs = [oracle.overlap(g, w) for g, w in zip(got_rows, want_rows)]
+    _say("sampled rows: overlap mean %.5f min %.5f" % (np.mean(ovs), np.min(ovs)))
+    assert np.mean(ovs) >= MIN_OVERLAP and np.min(ovs) >= 0.98
+
+
+def test_full_size_prefill_layer_sampled_rows():
+    cfg = gen.C3_12F   # L = 32768, H_I = H = 64, d_I = D = 128, k = 2048
+    _say("full size prefill layer L=%d" % cfg.Lq)
+    L = gen.layer_inputs(cfg, 0, device="cuda")
+    got = idxc.idxc_indexer_topk(L["q_idx"], L["k_idx"], L["w"], cfg.k, order="position")
+    out = idxc.idxc_sparse_attn(L["q"], L["k"], L["v"], got, cfg.scale)
+    torch.cuda.synchronize()
+    rows = [0, 1, 2046, 2047, 2048, 8191, 16384, 24577, 32766, 32767]
+    want = _oracle_rows(L["q_idx"][:, rows].cpu(), L["k_idx"].cpu(), L["w"][:, rows].cpu(), rows,
+                        cfg.k)
+    got_rows = got[0, rows].cpu().numpy()
+    _check_selection(got_rows, want)
+    assert np.array_equal(got_rows[0], oracle.position_order(want[0:1])[0])  # t = 0
+    ref = oracle.sparse_attention(f64(L["q"][:, rows].cpu()), f64(L["k"].cpu()),
+                                  f64(L["v"].cpu()), got[:, rows].cpu().numpy(), cfg.scale)
+    err = np.abs(out[:, rows].float().cpu().numpy() - ref).max()
+    _say("attention max-abs %.3e" % err)
+    assert err <= ATOL
+
+
+def test_full_size_decode_layer_sampled_rows():
+    cfg = gen.C4_12F   # 64 sequences x 65536 cached tokens, one query each
+    _say("full size decode layer B=%d Lk=%d" % (cfg.B, cfg.Lk))
+    L = gen.layer_inputs(cfg, 0, device="cuda")
+    got = idxc.idxc_indexer_topk(L["q_idx"], L["k_idx"], L["w"], cfg.k, q_pos0=cfg.q_pos0)
+    out = idxc.idxc_sparse_attn(L["q"], L["k"], L["v"], got, cfg.scale)
+    torch.cuda.synchronize()
+    seqs = [0, 37, 63]
+    want = np.stack([_oracle_rows(L["q_idx"][b:b + 1].cpu(), L["k_idx"][b:b + 1].cpu(),
+                                  L["w"][b:b + 1].cpu(), [cfg.q_pos0], cfg.k)[0] for b in seqs])
+    _check_selection(got[seqs, 0].cpu().numpy(), want)
+    for b in seqs:
+        ref = oracle.sparse_attention(f64(L["q"][b:b + 1].cpu()), f64(L["k"][b:b + 1].cpu()),
+                                      f64(L["v"][b:b + 1].cpu()), got[b:b + 1].cpu().numpy(),
+                                      cfg.scale)
+        err = np.abs(out[b:b + 1].float().cpu().numpy() - ref).max()
+        assert err <= ATOL, (b, err)
+
+
+def test_full_size_single_layer_stack_sampled_rows():
+    cfg = gen.C2       # one F layer at L = 8192 through the stack entry point
+    _say("full size single-layer stack L=%d" % cfg.Lq)
+    L = gen.layer_inputs(cfg, 0, device="cuda")
+    L["out"] = torch.empty_like(L["q"])
+    res = idxc.idxc_layer_stack_forward(cfg.pattern, [L], cfg.k, cfg.scale)
+    torch.cuda.synchronize()
+    assert res["indexer_calls"] == 1
+    rows = [0, 100, 2047, 2048, 4000, 8190, 8191]
+    want = _oracle_rows(L["q_idx"][:, rows].cpu(), L["k_idx"].cpu(), L["w"][:, rows].cpu(), rows,
+                        cfg.k)
+    cache = res["index_cache"][0, rows].cpu().numpy()
+    _check_selection(cache, want)
+    for r in cache:   # the cache holds each set in position order
+        v = r[r >= 0]
+        assert np.all(np.diff(v) > 0) and np.all(r[len(v):] == -1)
+    ref = oracle.sparse_attention(f64(L["q"][:, rows].cpu()), f64(L["k"].cpu()), f64(L["v"].cpu()),
+                                  res["index_cache"][:, rows].cpu().numpy(), cfg.scale)
+    err = np.abs(res["out"][0][:, rows].float().cpu().numpy() - ref).max()
+    assert err <= ATOL
+
+
+def test_full_size_long_context_last_chunk_sampled_rows():
+    # the last 4096-query chunk of a 196608-token context against all keys
+    L_all, chunk, k = gen.C5_L, gen.C5_CHUNK, 2048
+    q_pos0 = L_all - chunk
+    _say("long-context chunk q_pos0=%d Lk=%d" % (q_pos0, L_all))
+    q, kk, w = gen.indexer_inputs(1, chunk, L_all, 64, 128, kind="normal", seed=5, device="cuda")
+    got = idxc.idxc_indexer_topk(q, kk, w, k, q_pos0=q_pos0)
+    torch.cuda.synchronize()
+    rows = [0, 2000, chunk - 1]
+    want = _oracle_rows(q[:, rows].cpu(), kk.cpu(), w[:, rows].cpu(), [q_pos0 + r for r in rows],
+                        k)
+    _check_selection(got[0, rows].cpu().numpy(), want)
