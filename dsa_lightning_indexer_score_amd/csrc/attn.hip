@@ -80,7 +80,7 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   constexpr int NRW = BL::NI / HB;      // gather instructions per wave and matrix
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
 
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = lane_id();
   const int ul = wave / HB;  // unit slot in this workgroup
   const int hb = wave % HB;
@@ -119,12 +119,19 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   const int gch = lane % BL::NCH;
   // rows to gather, from the resolved index of key (lane % 32) (lanes l and
   // l + 32 hold the same key)
+  // (32-bit byte offsets from the batch's K and V bases: Lk <= 2^24 keeps
+  // them below 2^32)
+  const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(kb);
+  const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(vb);
   auto gather = [&](Gather<NRW>& g, int row_of_lane) {
+    uint32_t off[NRW];
+#pragma unroll
+    for (int r = 0; r < NRW; ++r) off[r] = (uint32_t)__shfl(row_of_lane, gkey0 + r, kWave);
 #pragma unroll
     for (int r = 0; r < NRW; ++r) {
-      const int row = __shfl(row_of_lane, gkey0 + r, kWave);
-      g.k[r] = *reinterpret_cast<const u32x4*>(kb + (size_t)row * D + gch * 8);
-      g.v[r] = *reinterpret_cast<const u32x4*>(vb + (size_t)row * D + gch * 8);
+      const uint32_t o = off[r] * (uint32_t)(2 * D) + (uint32_t)gch * 16u;
+      g.k[r] = *reinterpret_cast<const u32x4*>(kb8 + o);
+      g.v[r] = *reinterpret_cast<const u32x4*>(vb8 + o);
     }
   };
   uint8_t* base = dyn + ul * 2 * BL::BYTES;
@@ -141,7 +148,9 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   // masked out of the softmax
   auto raw_index = [&](int j) {
     const int e = kbeg + j * 32 + (lane & 31);
-    return (active && j < nblk && e < kend) ? irow[e] : -1;
+    const bool in = active && j < nblk && e < kend;
+    const int v = irow[in ? e : 0];  // unconditional load (entry 0 always exists)
+    return in ? v : -1;
   };
   auto resolve = [&](int idx, uint32_t* vmask) {
     const bool valid = idx >= 0 && idx < Lk;
@@ -208,16 +217,22 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     }
     // x * sl2 - m_used <= 8 keeps P <= 256; -inf maps to 0
     const float mu = (m_used == -INFINITY) ? 0.0f : m_used;
+    // The row sum accumulates the bf16-rounded weights that the P.V product
+    // uses (two-way dot products with 1), in two chains.
     u32x4 pw[2];
-    float psum = 0.0f;
+    float psum0 = 0.0f, psum1 = 0.0f;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
       const float p0 = __builtin_amdgcn_exp2f(fmaf(x[i], sl2, -mu));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(x[i + 1], sl2, -mu));
-      psum += p0 + p1;
-      pw[i >> 3][(i & 7) >> 1] = pack_bf16x2(p0, p1);
+      const uint32_t pk = pack_bf16x2(p0, p1);
+      pw[i >> 3][(i & 7) >> 1] = pk;
+      if (i & 2) psum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, psum1, false);
+      else psum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, psum0, false);
     }
-    lsum += psum;
+    lsum += psum0 + psum1;
     // ---- O^T += V^T . P^T; P^T's k index 8(l/32) + jj is key
     // 16kk + 8(jj/4) + 4(l/32) + jj%4, which the transposed reads match
 #pragma unroll
