@@ -16,7 +16,8 @@ from ._lib import IdxcDims, IdxcError, IdxcLayer
 
 __all__ = ["idxc_version", "idxc_validate_pattern", "idxc_schedule", "idxc_indexer_scores",
            "idxc_topk", "idxc_topk_workspace_bytes", "idxc_workspace_bytes", "idxc_indexer_topk", "idxc_sparse_attn", "idxc_sparse_attn_workspace_bytes", "idxc_overlap",
-           "idxc_layer_stack_forward", "make_dims", "IdxcError", "StackCall"]
+           "idxc_layer_stack_forward", "idxc_overlap_matrix", "idxc_greedy_pattern",
+           "idxc_overlap_proxy_loss", "make_dims", "IdxcError", "StackCall"]
 
 
 def _stream(stream=None) -> ctypes.c_void_p:
@@ -232,6 +233,67 @@ def idxc_overlap(a, b, Lk: int, stream=None):
                                 ctypes.byref(d), _ptr(inter, "inter"), _ptr(ov, "overlap"),
                                 _ptr(jac, "jaccard"), _stream(stream)))
     return inter, ov, jac
+
+
+def idxc_overlap_matrix(sel, Lk: int, workspace=None, stream=None):
+    """Mean overlap of every pair of layers: sel is an int32 [n_layers, B, Lq, k]
+    tensor (for instance every layer's own top-k); returns fp32 [n_layers,
+    n_layers] on the device with M[a, b] = mean over rows of |A ∩ B| / |A|."""
+    lib = _lib.load()
+    if sel.dim() != 4:
+        raise ValueError("sel must be an [n_layers, B, Lq, k] tensor")
+    n, B, Lq, k = sel.shape
+    d = make_dims(B, Lq, Lk, Lk - Lq, k=k)
+    need = int(lib.idxc_overlap_matrix_workspace_bytes(n))
+    if workspace is None:
+        workspace = _workspace(max(need, 16), sel.device)
+    m = torch.empty((n, n), dtype=torch.float32, device=sel.device)
+    _lib.check(lib.idxc_overlap_matrix(_ptr(sel, "sel", torch.int32), n, ctypes.byref(d),
+                                       _ptr(workspace, "workspace"),
+                                       workspace.numel() * workspace.element_size(),
+                                       _ptr(m, "matrix"), _stream(stream)))
+    return m
+
+
+def idxc_greedy_pattern(n_layers: int, removals: int, loss):
+    """Greedy F->S search of the C driver; loss(pattern: str) -> float is
+    called for every trial. Returns (pattern, number of loss calls)."""
+    lib = _lib.load()
+    errors = []
+
+    def call(pattern, _user):
+        try:
+            return float(loss(pattern.decode("ascii")))
+        except Exception as e:  # surfaced after the C call returns
+            errors.append(e)
+            return float("nan")
+
+    fn = _lib.LOSS_FN(call)
+    buf = ctypes.create_string_buffer(n_layers + 1)
+    evals = ctypes.c_int64(0)
+    code = lib.idxc_greedy_pattern(n_layers, removals, fn, None, buf, ctypes.byref(evals))
+    if errors:
+        raise errors[0]
+    _lib.check(code)
+    return buf.value.decode("ascii"), int(evals.value)
+
+
+def idxc_overlap_proxy_loss(pattern: str, matrix) -> float:
+    """(1 / n) * sum over S layers l of (1 - M[l, f(l)]) for a host copy of an
+    idxc_overlap_matrix result (numpy array or tensor, [n, n])."""
+    lib = _lib.load()
+    if isinstance(matrix, torch.Tensor):
+        matrix = matrix.detach().to("cpu", torch.float32).numpy()
+    import numpy as np
+    m = np.ascontiguousarray(np.asarray(matrix, dtype=np.float32))
+    n = len(pattern)
+    if m.shape != (n, n):
+        raise ValueError("matrix must be [n_layers, n_layers]")
+    out = ctypes.c_double(0.0)
+    _lib.check(lib.idxc_overlap_proxy_loss(pattern.encode("ascii"), n,
+                                           m.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                                           ctypes.byref(out)))
+    return float(out.value)
 
 
 class StackCall:

@@ -32,8 +32,12 @@ EXPORTED = (
     "idxc_last_error", "idxc_version", "idxc_validate_pattern", "idxc_schedule",
     "idxc_indexer_scores", "idxc_topk", "idxc_topk_workspace_bytes", "idxc_workspace_bytes",
     "idxc_indexer_topk", "idxc_sparse_attn", "idxc_sparse_attn_workspace_bytes",
-    "idxc_layer_stack_forward", "idxc_overlap",
+    "idxc_layer_stack_forward", "idxc_overlap", "idxc_overlap_matrix_workspace_bytes",
+    "idxc_overlap_matrix", "idxc_greedy_pattern", "idxc_overlap_proxy_loss",
 )
+
+# double loss(const char* pattern, void* user)
+LOSS_FN = ctypes.CFUNCTYPE(ctypes.c_double, ctypes.c_char_p, ctypes.c_void_p)
 
 
 class IdxcDims(ctypes.Structure):
@@ -84,6 +88,12 @@ def load() -> ctypes.CDLL:
                                       ctypes.c_float, vp, vp, sz, P(i32), vp, vp],
                                      ctypes.c_int),
         "idxc_overlap": ([vp, vp, P(IdxcDims), vp, vp, vp, vp], ctypes.c_int),
+        "idxc_overlap_matrix_workspace_bytes": ([i32], sz),
+        "idxc_overlap_matrix": ([vp, i32, P(IdxcDims), vp, sz, vp, vp], ctypes.c_int),
+        "idxc_greedy_pattern": ([i32, i32, LOSS_FN, vp, ctypes.c_char_p, P(ctypes.c_int64)],
+                                ctypes.c_int),
+        "idxc_overlap_proxy_loss": ([ctypes.c_char_p, i32, P(ctypes.c_float),
+                                     P(ctypes.c_double)], ctypes.c_int),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)

@@ -56,6 +56,7 @@ constexpr int kMaxLk = 1 << 24;
 // Common size checks. need: bit 0 = indexer fields, bit 1 = attention fields,
 // bit 2 = k.
 constexpr int kMaxOverlapLk = 262144;  // two LDS bitmaps of Lk bits (64 KB)
+constexpr int kMaxMatrixLayers = 64;   // n*n 64-bit LDS accumulators (32 KB)
 
 int check_dims(const idxc_dims* d, int need) {
   if (d == nullptr) return fail(IDXC_ERR_INVALID_ARG, "dims is NULL");
@@ -433,6 +434,92 @@ int idxc_overlap(const int32_t* a, const int32_t* b, const idxc_dims* dims, int3
   return hip_status(launch_overlap(a, b, dims->B * dims->Lq, dims->k, dims->Lk, inter, overlap,
                                    jaccard, static_cast<hipStream_t>(hip_stream)),
                     "overlap launch");
+}
+
+size_t idxc_overlap_matrix_workspace_bytes(int32_t n_layers) {
+  if (n_layers < 1 || n_layers > kMaxMatrixLayers) return 0;
+  return align_up((size_t)n_layers * n_layers * 8);
+}
+
+int idxc_overlap_matrix(const int32_t* sel, int32_t n_layers, const idxc_dims* dims,
+                        void* workspace, size_t workspace_bytes, float* matrix,
+                        void* hip_stream) {
+  int r = check_dims(dims, 4);
+  if (r != IDXC_OK) return r;
+  if (n_layers < 1) return fail(IDXC_ERR_INVALID_ARG, "n_layers must be >= 1");
+  if (n_layers > kMaxMatrixLayers)
+    return fail(IDXC_ERR_UNSUPPORTED, "n_layers = %d above %d", n_layers, kMaxMatrixLayers);
+  if (dims->Lk > kMaxOverlapLk)
+    return fail(IDXC_ERR_UNSUPPORTED, "Lk = %d above %d for idxc_overlap_matrix", dims->Lk,
+                kMaxOverlapLk);
+  if (sel == nullptr || matrix == nullptr || workspace == nullptr)
+    return fail(IDXC_ERR_INVALID_ARG, "sel, matrix and workspace must not be NULL");
+  if ((reinterpret_cast<uintptr_t>(sel) & 3u) || (reinterpret_cast<uintptr_t>(matrix) & 3u))
+    return fail(IDXC_ERR_INVALID_ARG, "sel and matrix must be 4-byte aligned");
+  if (reinterpret_cast<uintptr_t>(workspace) & 15u)
+    return fail(IDXC_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  const size_t need = idxc_overlap_matrix_workspace_bytes(n_layers);
+  if (workspace_bytes < need)
+    return fail(IDXC_ERR_INVALID_ARG, "workspace of %zu bytes is below the %zu needed",
+                workspace_bytes, need);
+  return hip_status(launch_overlap_matrix(sel, n_layers, dims->B * dims->Lq, dims->k, dims->Lk,
+                                          static_cast<unsigned long long*>(workspace), matrix,
+                                          static_cast<hipStream_t>(hip_stream)),
+                    "overlap matrix launch");
+}
+
+int idxc_overlap_proxy_loss(const char* pattern, int32_t n_layers, const float* matrix,
+                            double* loss) {
+  const int r = check_pattern(pattern, n_layers, nullptr);
+  if (r != IDXC_OK) return r;
+  if (matrix == nullptr || loss == nullptr)
+    return fail(IDXC_ERR_INVALID_ARG, "matrix and loss must not be NULL");
+  double sum = 0.0;
+  int last_f = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    if (pattern[l] == 'F') {
+      last_f = l;
+      continue;
+    }
+    sum += 1.0 - (double)matrix[(size_t)l * n_layers + last_f];
+  }
+  *loss = sum / (double)n_layers;
+  return ok();
+}
+
+int idxc_greedy_pattern(int32_t n_layers, int32_t removals, idxc_loss_fn loss, void* user,
+                        char* pattern, int64_t* evals) {
+  if (n_layers < 1) return fail(IDXC_ERR_INVALID_ARG, "n_layers must be >= 1");
+  if (removals < 0 || removals > n_layers - 1)
+    return fail(IDXC_ERR_INVALID_ARG, "removals = %d outside [0, %d]", removals, n_layers - 1);
+  if (loss == nullptr || pattern == nullptr)
+    return fail(IDXC_ERR_INVALID_ARG, "loss and pattern must not be NULL");
+  // the working pattern lives in the caller's buffer (n_layers + 1 chars)
+  memset(pattern, 'F', (size_t)n_layers);
+  pattern[n_layers] = '\0';
+  int64_t count = 0;
+  for (int step = 0; step < removals; ++step) {
+    int best = -1;
+    double best_v = 0.0;
+    for (int l = 1; l < n_layers; ++l) {
+      if (pattern[l] != 'F') continue;
+      pattern[l] = 'S';
+      const double v = loss(pattern, user);
+      pattern[l] = 'F';
+      ++count;
+      if (!(v == v)) {
+        if (evals) *evals = count;
+        return fail(IDXC_ERR_INVALID_ARG, "loss returned NaN for layer %d at step %d", l, step);
+      }
+      if (best < 0 || v < best_v) {  // ties keep the lower layer
+        best = l;
+        best_v = v;
+      }
+    }
+    pattern[best] = 'S';
+  }
+  if (evals) *evals = count;
+  return ok();
 }
 
 int idxc_layer_stack_forward(const char* pattern, int32_t n_layers, const idxc_layer* layers,

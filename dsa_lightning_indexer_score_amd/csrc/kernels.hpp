@@ -82,5 +82,10 @@ size_t attn_workspace_bytes(int B, int Lq, int H, int D, int k);
 size_t overlap_lds_bytes(int Lk);
 hipError_t launch_overlap(const int32_t* a, const int32_t* b, int rows, int k, int Lk,
                           int32_t* inter, float* overlap, float* jaccard, hipStream_t st);
+// Overlap matrix of n index tensors sel[n][rows][k] (matrix[a*n+b] = mean over
+// rows of overlap(sel[a], sel[b])); acc is a device workspace of n*n uint64.
+size_t overlap_matrix_lds_bytes(int n, int Lk);
+hipError_t launch_overlap_matrix(const int32_t* sel, int n, int rows, int k, int Lk,
+                                 unsigned long long* acc, float* matrix, hipStream_t st);
 
 }  // namespace idxc

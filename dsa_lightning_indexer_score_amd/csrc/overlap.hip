@@ -86,7 +86,126 @@ void overlap_kernel(const int32_t* __restrict__ a, const int32_t* __restrict__ b
   }
 }
 
+// ---------------------------------------------------------------------------
+// Overlap matrix of n index tensors sel[n][rows][k]: M[a][b] = mean over rows
+// of overlap(sel[a], sel[b]) (same per-row definition as above, so M[a][a] =
+// 1). One wave per workgroup walks rows blockIdx.x, blockIdx.x + gridDim.x,
+// ...; per row it builds layer a's bitmap, then for every b > a a bitmap of
+// b's new positions, counting |B| and |A ∩ B| in one pass. Each per-row
+// ratio is added as a 32.32 fixed-point integer (floor(inter * 2^32 / |A|),
+// error below 2^-32), first into the workgroup's LDS accumulators, then with
+// one 64-bit atomic add per pair into acc[n*n]: integer sums do not depend
+// on the order of the additions, so the result is deterministic.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void ov_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// overlap(X -> Y) as 32.32 fixed point: inter / |X|, 1 if both are empty, 0
+// if only X is
+__device__ __forceinline__ unsigned long long ov_fix(int inter, int nx, int ny) {
+  if (nx > 0) return ((unsigned long long)inter << 32) / (unsigned long long)nx;
+  return ny > 0 ? 0ull : (1ull << 32);
+}
+
+__global__ __launch_bounds__(kWave)
+void overlap_matrix_kernel(const int32_t* __restrict__ sel, int n, int rows, int k, int Lk,
+                           int words, unsigned long long* __restrict__ acc_out) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  unsigned long long* acc = reinterpret_cast<unsigned long long*>(smem);  // [n*n]
+  uint32_t* bits_a = reinterpret_cast<uint32_t*>(smem + (size_t)n * n * 8);
+  uint32_t* bits_b = bits_a + words;
+  const int lane = lane_id();
+  for (int p = lane; p < n * n; p += kWave) acc[p] = 0ull;
+  for (int row = blockIdx.x; row < rows; row += gridDim.x) {
+    for (int a = 0; a < n; ++a) {
+      const int32_t* A = sel + ((size_t)a * rows + row) * k;
+      for (int w = lane; w < words; w += kWave) bits_a[w] = 0u;
+      ov_wave_sync();
+      int na = 0;
+      for (int e = lane; e < k; e += kWave) {
+        const int p = A[e];
+        if (p >= 0 && p < Lk) {
+          const uint32_t m = 1u << (p & 31);
+          na += (atomicOr(&bits_a[p >> 5], m) & m) ? 0 : 1;
+        }
+      }
+      na = wave_sum(na);
+      ov_wave_sync();
+      for (int b = a + 1; b < n; ++b) {
+        const int32_t* Bl = sel + ((size_t)b * rows + row) * k;
+        for (int w = lane; w < words; w += kWave) bits_b[w] = 0u;
+        ov_wave_sync();
+        int nb = 0, ni = 0;
+        for (int e = lane; e < k; e += kWave) {
+          const int p = Bl[e];
+          if (p >= 0 && p < Lk) {
+            const uint32_t m = 1u << (p & 31);
+            if (!(atomicOr(&bits_b[p >> 5], m) & m)) {
+              ++nb;
+              ni += (bits_a[p >> 5] & m) ? 1 : 0;
+            }
+          }
+        }
+        nb = wave_sum(nb);
+        ni = wave_sum(ni);
+        if (lane == 0) {
+          acc[a * n + b] += ov_fix(ni, na, nb);
+          acc[b * n + a] += ov_fix(ni, nb, na);
+        }
+        ov_wave_sync();
+      }
+    }
+  }
+  ov_wave_sync();
+  for (int p = lane; p < n * n; p += kWave)
+    if (acc[p] != 0ull) atomicAdd(&acc_out[p], acc[p]);
+}
+
+__global__ void overlap_matrix_zero(unsigned long long* __restrict__ acc, int count) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) acc[i] = 0ull;
+}
+
+__global__ void overlap_matrix_finish(const unsigned long long* __restrict__ acc, int n, int rows,
+                                      float* __restrict__ matrix) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n * n) return;
+  const int a = i / n, b = i % n;
+  matrix[i] = (a == b) ? 1.0f : (float)((double)acc[i] * 0x1p-32 / (double)rows);
+}
+
 }  // namespace
+
+size_t overlap_matrix_lds_bytes(int n, int Lk) {
+  return (size_t)n * n * 8 + (size_t)2 * ((Lk + 31) / 32) * 4;
+}
+
+hipError_t launch_overlap_matrix(const int32_t* sel, int n, int rows, int k, int Lk,
+                                 unsigned long long* acc, float* matrix, hipStream_t st) {
+  const int words = (Lk + 31) / 32;
+  const size_t shmem = overlap_matrix_lds_bytes(n, Lk);
+  if (shmem > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(overlap_matrix_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (e != hipSuccess) return e;
+  }
+  const int nn = n * n;
+  hipLaunchKernelGGL(overlap_matrix_zero, dim3((unsigned)((nn + 255) / 256)), dim3(256), 0, st,
+                     acc, nn);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // enough single-wave workgroups to fill the chip; each walks several rows
+  const int grid = rows < 4096 ? rows : 4096;
+  hipLaunchKernelGGL(overlap_matrix_kernel, dim3((unsigned)grid), dim3(kWave), shmem, st, sel, n,
+                     rows, k, Lk, words, acc);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(overlap_matrix_finish, dim3((unsigned)((nn + 255) / 256)), dim3(256), 0, st,
+                     acc, n, rows, matrix);
+  return hipGetLastError();
+}
 
 size_t overlap_lds_bytes(int Lk) { return (size_t)2 * ((Lk + 31) / 32) * 4; }
 

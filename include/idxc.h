@@ -207,6 +207,51 @@ int idxc_layer_stack_forward(const char* pattern, int32_t n_layers,
 int idxc_overlap(const int32_t* a, const int32_t* b, const idxc_dims* dims, int32_t* inter,
                  float* overlap, float* jaccard, void* hip_stream);
 
+/* Overlap matrix of n_layers index tensors sel [n_layers, B, Lq, k] int32
+ * (DEVICE; for instance the debug_indices of an all-F idxc_layer_stack_forward,
+ * i.e. every layer's own top-k): matrix[a * n_layers + b] = mean over the B*Lq
+ * rows of overlap(sel[a], sel[b]) = |A ∩ B| / |A|, with the per-row
+ * conventions of idxc_overlap (so the diagonal is 1). This is the adjacent-
+ * and cross-layer agreement of "IndexCache：跨层复用稀疏注意力的索引",
+ * section "相邻层重叠很高，但“重叠率”不是搜索目标" (Overlap equation), for
+ * every pair of layers at once. matrix: DEVICE float [n_layers * n_layers].
+ * workspace: DEVICE, 16-byte aligned, at least
+ * idxc_overlap_matrix_workspace_bytes(n_layers) bytes; its contents on entry
+ * do not matter. Deterministic (per-row ratios are summed as 32.32 fixed-point
+ * integers; error below 2^-32 per row). n_layers above 64 or Lk above 262144
+ * returns IDXC_ERR_UNSUPPORTED. Uses B, Lq, Lk, k. Asynchronous on hip_stream. */
+size_t idxc_overlap_matrix_workspace_bytes(int32_t n_layers); /* 0 if n_layers is outside [1, 64] */
+int idxc_overlap_matrix(const int32_t* sel, int32_t n_layers, const idxc_dims* dims,
+                        void* workspace, size_t workspace_bytes, float* matrix,
+                        void* hip_stream);
+
+/* Loss callback of idxc_greedy_pattern: pattern is a NUL-terminated string of
+ * n_layers roles ('F'/'S', first 'F'); returns the loss of running the model
+ * with that pattern (lower is better). Called on the calling host thread. */
+typedef double (*idxc_loss_fn)(const char* pattern, void* user);
+
+/* Greedy F/S pattern search, host only ("IndexCache：跨层复用稀疏注意力的索引",
+ * section "Training-free：直接用语言模型损失选择 Full 层"; "NLP——IndexCache"
+ * notes, section "核心算法：Greedy Layer Selection"): start from all F with
+ * layer 0 pinned to F; `removals` times, try every remaining F layer l >= 1 as
+ * S, evaluate loss(trial pattern, user), and commit the lowest (ties go to the
+ * lower layer). pattern: HOST buffer of n_layers + 1 chars, receives the
+ * result. *evals (HOST, may be NULL) receives the number of loss calls,
+ * sum_{i < removals} (n_layers - 1 - i). removals outside [0, n_layers - 1]
+ * is IDXC_ERR_INVALID_ARG; a NaN loss stops the search with
+ * IDXC_ERR_INVALID_ARG. No device is touched. */
+int idxc_greedy_pattern(int32_t n_layers, int32_t removals, idxc_loss_fn loss, void* user,
+                        char* pattern, int64_t* evals);
+
+/* An overlap proxy loss for idxc_greedy_pattern when no model is at hand (the
+ * pages drive the search with the language-model loss; this stand-in only
+ * measures how much of each S layer's own selection its reused cache keeps):
+ * loss = (1 / n_layers) * sum over S layers l of (1 - matrix[l][f(l)]), with
+ * f(l) the latest F layer before l and matrix the HOST copy of an
+ * idxc_overlap_matrix result [n_layers * n_layers]. Host only. */
+int idxc_overlap_proxy_loss(const char* pattern, int32_t n_layers, const float* matrix,
+                            double* loss);
+
 #ifdef __cplusplus
 }
 #endif

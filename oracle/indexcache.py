@@ -277,6 +277,30 @@ def mean_overlap(a: np.ndarray, b: np.ndarray) -> Tuple[float, float]:
     return float(np.mean(vals)), float(np.min(vals))
 
 
+def overlap_matrix(sel: np.ndarray) -> np.ndarray:
+    """M[a, b] = mean over rows of overlap(sel[a], sel[b]) for index tensors
+    sel [n_layers, ..., k]: the pages' Overlap(l, j) for every pair of layers
+    ([W] "相邻层重叠很高，但“重叠率”不是搜索目标", Overlap equation), in fp64."""
+    sel = np.asarray(sel)
+    n = sel.shape[0]
+    m = np.empty((n, n), dtype=np.float64)
+    for a in range(n):
+        for b in range(n):
+            m[a, b] = mean_overlap(sel[a], sel[b])[0]
+    return m
+
+
+def overlap_proxy_loss(pattern: str, matrix: np.ndarray) -> float:
+    """Stand-in loss for the greedy search when no language model is at hand
+    (the pages use the LM loss): (1/n) * sum over S layers l of
+    (1 - M[l, f(l)]), f(l) the latest F layer before l ([J] "IndexCache 方法")."""
+    validate_pattern(pattern, len(pattern))
+    src = nearest_full(pattern)
+    n = len(pattern)
+    total = sum(1.0 - float(matrix[l][src[l]]) for l in range(n) if pattern[l] == "S")
+    return total / n
+
+
 # --------------------------------------------------------------------------- #
 # Greedy layer selection with an injectable loss ([W] "Training-free：直接用语言
 # 模型损失选择 Full 层"; [J] "核心算法：Greedy Layer Selection", Algorithm 1)

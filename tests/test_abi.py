@@ -183,3 +183,86 @@ def test_overlap_argument_errors(lib):
     assert f(P(), P(), big, P(), None, None, None) == _lib.IDXC_ERR_UNSUPPORTED
     # nothing requested: no launch
     assert f(P(), P(), d, None, None, None, None) == _lib.IDXC_OK
+
+
+def _golden(name):
+    import json
+    with open(os.path.join(ROOT, "tests", "golden", name)) as f:
+        return json.load(f)
+
+
+def test_greedy_driver_toy_example_and_forward_count():
+    import dsa_lightning_indexer_score_amd as idxc
+    g = _golden("greedy_toy.json")
+    imp = g["importance"]
+    pat, evals = idxc.idxc_greedy_pattern(
+        g["n_layers"], g["removals"], lambda p: sum(v for r, v in zip(p, imp) if r == "S"))
+    assert pat == g["expected_pattern"] and evals == 7
+    for N, K, want in g["forward_count_cases"]:
+        _, evals = idxc.idxc_greedy_pattern(N, K, lambda p: 0.0)
+        assert evals == want
+
+
+def test_greedy_driver_matches_oracle_on_proxy_losses():
+    import numpy as np
+    import dsa_lightning_indexer_score_amd as idxc
+    rng = np.random.default_rng(7)
+    for trial in range(20):
+        n = int(rng.integers(2, 13))
+        K = int(rng.integers(0, n))
+        m = rng.random((n, n)).astype(np.float32)
+        np.fill_diagonal(m, 1.0)
+        if trial % 4 == 0:
+            m[:] = np.round(m * 4) / 4  # many ties: the lower layer must win
+        c_loss = lambda p: idxc.idxc_overlap_proxy_loss(p, m)
+        o_loss = lambda p: oracle.overlap_proxy_loss(p, m.astype(np.float64))
+        assert idxc.idxc_greedy_pattern(n, K, c_loss) == oracle.greedy_pattern(n, K, o_loss)
+        for _ in range(5):
+            p = "F" + "".join(rng.choice(["F", "S"], n - 1))
+            assert idxc.idxc_overlap_proxy_loss(p, m) == pytest.approx(o_loss(p), abs=1e-12)
+
+
+def test_greedy_and_proxy_errors(lib):
+    import numpy as np
+    import dsa_lightning_indexer_score_amd as idxc
+    with pytest.raises(_lib.IdxcError):
+        idxc.idxc_greedy_pattern(5, 5, lambda p: 0.0)
+    with pytest.raises(_lib.IdxcError):
+        idxc.idxc_greedy_pattern(5, -1, lambda p: 0.0)
+    with pytest.raises(_lib.IdxcError):
+        idxc.idxc_greedy_pattern(5, 2, lambda p: float("nan"))
+    with pytest.raises(ZeroDivisionError):
+        idxc.idxc_greedy_pattern(5, 2, lambda p: 1 / 0)
+    buf = ctypes.create_string_buffer(6)
+    fn = _lib.LOSS_FN(lambda p, u: 0.0)
+    assert lib.idxc_greedy_pattern(5, 1, _lib.LOSS_FN(), None, buf, None) == \
+        _lib.IDXC_ERR_INVALID_ARG
+    assert lib.idxc_greedy_pattern(5, 1, fn, None, None, None) == _lib.IDXC_ERR_INVALID_ARG
+    assert lib.idxc_greedy_pattern(5, 1, fn, None, buf, None) == _lib.IDXC_OK
+    m = np.eye(3, dtype=np.float32)
+    with pytest.raises(_lib.IdxcError):
+        idxc.idxc_overlap_proxy_loss("SFF", m)
+    out = ctypes.c_double(0.0)
+    mp = m.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    assert lib.idxc_overlap_proxy_loss(b"FSF", 3, None, ctypes.byref(out)) == \
+        _lib.IDXC_ERR_INVALID_ARG
+    assert lib.idxc_overlap_proxy_loss(b"FSF", 4, mp, ctypes.byref(out)) == _lib.IDXC_ERR_PATTERN
+
+
+def test_overlap_matrix_argument_errors(lib):
+    f = lib.idxc_overlap_matrix
+    d = ctypes.byref(_dims(Lq=8, Lk=64, k=16))
+    assert lib.idxc_overlap_matrix_workspace_bytes(0) == 0
+    assert lib.idxc_overlap_matrix_workspace_bytes(65) == 0
+    assert lib.idxc_overlap_matrix_workspace_bytes(47) >= 47 * 47 * 8
+    ws = lib.idxc_overlap_matrix_workspace_bytes(4)
+    assert f(P(), 0, d, P(), ws, P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), 65, d, P(), 1 << 20, P(), None) == _lib.IDXC_ERR_UNSUPPORTED
+    assert f(None, 4, d, P(), ws, P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), 4, d, P(), ws, None, None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), 4, d, P(FAKE + 8), ws, P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(FAKE + 2), 4, d, P(), ws, P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), 4, d, P(), ws - 8, P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    big = ctypes.byref(_dims(Lq=1, Lk=262145, q_pos0=262144, k=16))
+    assert f(P(), 4, big, P(), ws, P(), None) == _lib.IDXC_ERR_UNSUPPORTED
+    assert f(P(), 4, ctypes.byref(_dims(k=0)), P(), ws, P(), None) == _lib.IDXC_ERR_INVALID_ARG

@@ -430,6 +430,51 @@ def test_overlap_of_adjacent_layer_selections():
     assert np.all(ov.cpu().numpy()[0, :k] == 1.0)
 
 
+def test_overlap_matrix_matches_oracle_on_random_sets():
+    rng = np.random.default_rng(12)
+    n, B, Lq, k, Lk = 5, 2, 33, 16, 200
+    sel = rng.integers(0, 40, size=(n, B, Lq, k)).astype(np.int32)   # duplicates
+    sel[rng.random(sel.shape) < 0.25] = -1
+    sel[0, 0, 0] = -1                       # empty rows
+    sel[1, 0, 0] = -1
+    sel[2, 1, 3] = sel[3, 1, 3][::-1]       # same set, other order
+    sel[4, 1, 4] = np.where(sel[0, 1, 4] >= 0, sel[0, 1, 4] + 100, -1)  # disjoint
+    _say("overlap matrix n=%d rows=%d" % (n, B * Lq))
+    m = idxc.idxc_overlap_matrix(cu(torch.from_numpy(sel)), Lk)
+    m2 = idxc.idxc_overlap_matrix(cu(torch.from_numpy(sel)), Lk)
+    torch.cuda.synchronize()
+    want = oracle.overlap_matrix(sel)
+    got = m.cpu().numpy()
+    assert np.abs(got - want).max() <= 1e-6
+    assert np.array_equal(got, m2.cpu().numpy())      # deterministic
+    assert np.all(np.diag(got) == 1.0)
+
+
+def test_overlap_matrix_and_greedy_search_on_stack_selections():
+    # every layer's own top-k from an all-F stack, the overlap matrix of them,
+    # and the greedy F/S search driven by the overlap proxy loss
+    import dataclasses
+    n = 6
+    cfg = dataclasses.replace(gen.C2, name="greedy", n_layers=n, pattern="F" * n, Lq=640,
+                              Lk=640, k=128)
+    _say("all-F stack n=%d L=%d, overlap matrix + greedy" % (n, cfg.Lq))
+    layers = _layers(cfg)
+    dev_layers = [{nm: cu(t) for nm, t in L.items()} for L in layers]
+    res = idxc.idxc_layer_stack_forward(cfg.pattern, dev_layers, cfg.k, cfg.scale,
+                                        debug_indices=True)
+    sel = res["debug_indices"]
+    m = idxc.idxc_overlap_matrix(sel, cfg.Lk)
+    torch.cuda.synchronize()
+    got = m.cpu().numpy()
+    want = oracle.overlap_matrix(sel.cpu().numpy())
+    assert np.abs(got - want).max() <= 1e-6
+    K = 4
+    pat, evals = idxc.idxc_greedy_pattern(n, K, lambda p: idxc.idxc_overlap_proxy_loss(p, got))
+    ref = oracle.greedy_pattern(n, K, lambda p: oracle.overlap_proxy_loss(p, got.astype(np.float64)))
+    assert (pat, evals) == ref
+    assert evals == K * (n - 1) - K * (K - 1) // 2 and pat.count("S") == K
+
+
 # --------------------------------------------------------------------------- #
 # the stack captured in a HIP graph
 # --------------------------------------------------------------------------- #

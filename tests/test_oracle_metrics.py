@@ -64,3 +64,35 @@ def test_greedy_forward_count_formula(golden_dir):
             _, evals = oracle.greedy_pattern(N, K, lambda p: p.count("S") * 0.0)
             assert evals == want
         assert K * (N - 1) - K * (K - 1) // 2 == want
+
+
+def test_overlap_matrix_hand_example():
+    # three layers, two rows each; counted by hand
+    l0 = np.array([[1, 2, 3, 4], [5, 6, -1, -1]], np.int32)
+    l1 = np.array([[3, 4, 5, 6], [5, 7, -1, -1]], np.int32)
+    l2 = np.array([[9, 8, 7, 6], [-1, -1, -1, -1]], np.int32)
+    m = oracle.overlap_matrix(np.stack([l0, l1, l2]))
+    want = np.array([
+        [1.0, (2 / 4 + 1 / 2) / 2, (0 / 4 + 0 / 2) / 2],
+        [(2 / 4 + 1 / 2) / 2, 1.0, (1 / 4 + 0 / 2) / 2],
+        [(0 / 4 + 0.0) / 2, (1 / 4 + 0.0) / 2, 1.0],  # empty A, non-empty B -> 0
+    ])
+    assert np.allclose(m, want, atol=0, rtol=0)
+
+
+def test_overlap_matrix_identities():
+    rng = np.random.default_rng(1)
+    sel = np.stack([np.stack([rng.choice(200, 8, replace=False) for _ in range(5)])] * 3)
+    assert np.array_equal(oracle.overlap_matrix(sel), np.ones((3, 3)))
+    disjoint = np.stack([np.arange(8, dtype=np.int32).reshape(1, 8) + 8 * i for i in range(4)])
+    assert np.array_equal(oracle.overlap_matrix(disjoint), np.eye(4))
+
+
+def test_overlap_proxy_loss_hand_examples():
+    m = np.eye(4)
+    m[2, 1], m[2, 0], m[1, 0], m[3, 0] = 0.75, 0.5, 0.25, 0.125
+    assert oracle.overlap_proxy_loss("FFFF", m) == 0.0
+    assert oracle.overlap_proxy_loss("FFSF", m) == (1 - 0.75) / 4
+    assert oracle.overlap_proxy_loss("FSSS", m) == ((1 - 0.25) + (1 - 0.5) + (1 - 0.125)) / 4
+    with pytest.raises(ValueError):
+        oracle.overlap_proxy_loss("SFFF", m)
