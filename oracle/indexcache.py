@@ -90,14 +90,25 @@ def _canon_zero(x: np.ndarray) -> np.ndarray:
     return x
 
 
+def row_position(b: int, i: int, q_pos0: int, q_pos: Optional[np.ndarray], Lk: int) -> int:
+    """Absolute position t of query row (b, i): q_pos0 + i, or q_pos[b, i] for
+    per-row (ragged) positions, where a negative entry means "no candidates"
+    (-1) and entries past the last key are read as Lk - 1."""
+    if q_pos is None:
+        return q_pos0 + i
+    t = int(np.asarray(q_pos)[b, i])
+    return -1 if t < 0 else min(t, Lk - 1)
+
+
 def indexer_scores(q_idx: np.ndarray, k_idx: np.ndarray, w: np.ndarray,
-                   q_pos0: int, Lk: Optional[int] = None) -> np.ndarray:
+                   q_pos0: int, Lk: Optional[int] = None,
+                   q_pos: Optional[np.ndarray] = None) -> np.ndarray:
     """score[b,i,s] = fp32( sum_h w[b,i,h] * max(0, q_idx[b,i,h,:] . k_idx[b,s,:]) ).
 
     Shapes: q_idx [B,Lq,H_I,d_I], k_idx [B,Lk,d_I], w [B,Lq,H_I] (exact fp64
-    values of the bf16 inputs). Row i is query position t = q_pos0 + i; only
-    s <= t are candidates, the rest are returned as -inf. Sums in fp64, one
-    rounding to fp32, then -0.0 -> +0.0.
+    values of the bf16 inputs). Row i is query position t = q_pos0 + i (or
+    q_pos[b, i], see row_position); only s <= t are candidates, the rest are
+    returned as -inf. Sums in fp64, one rounding to fp32, then -0.0 -> +0.0.
     """
     q_idx = np.asarray(q_idx, dtype=np.float64)
     k_idx = np.asarray(k_idx, dtype=np.float64)
@@ -105,12 +116,14 @@ def indexer_scores(q_idx: np.ndarray, k_idx: np.ndarray, w: np.ndarray,
     B, Lq, H_I, d_I = q_idx.shape
     if Lk is None:
         Lk = k_idx.shape[1]
-    if q_pos0 + Lq > Lk:
+    if q_pos is None and q_pos0 + Lq > Lk:
         raise ValueError("query rows exceed the key range")
     out = np.full((B, Lq, Lk), -np.inf, dtype=np.float32)
     for b in range(B):
         for i in range(Lq):
-            t = q_pos0 + i
+            t = row_position(b, i, q_pos0, q_pos, Lk)
+            if t < 0:
+                continue
             keys = k_idx[b, : t + 1, :]                  # [t+1, d_I]
             dots = keys @ q_idx[b, i].T                   # [t+1, H_I], fp64
             relu = np.maximum(dots, 0.0)
@@ -139,13 +152,15 @@ def topk_row(scores_row: np.ndarray, n_cand: int, k: int) -> np.ndarray:
     return out
 
 
-def topk(scores: np.ndarray, k: int, q_pos0: int) -> np.ndarray:
-    """indices[b,i,:] = topk_row(scores[b,i], t+1, k) with t = q_pos0 + i."""
-    B, Lq, _ = scores.shape
+def topk(scores: np.ndarray, k: int, q_pos0: int,
+         q_pos: Optional[np.ndarray] = None) -> np.ndarray:
+    """indices[b,i,:] = topk_row(scores[b,i], t+1, k) with t = q_pos0 + i (or
+    q_pos[b, i], see row_position)."""
+    B, Lq, Lk = scores.shape
     out = np.empty((B, Lq, k), dtype=np.int32)
     for b in range(B):
         for i in range(Lq):
-            out[b, i] = topk_row(scores[b, i], q_pos0 + i + 1, k)
+            out[b, i] = topk_row(scores[b, i], row_position(b, i, q_pos0, q_pos, Lk) + 1, k)
     return out
 
 
@@ -208,7 +223,8 @@ def schedule(layer_scores: Sequence[np.ndarray], pattern: str, k: int,
 
 
 def layer_stack(pattern: str, layers: Sequence[Dict[str, np.ndarray]], k: int,
-                scale: float, q_pos0: int, Lk: Optional[int] = None):
+                scale: float, q_pos0: int, Lk: Optional[int] = None,
+                q_pos: Optional[np.ndarray] = None):
     """Full hot path over a stack: per layer {indexer + top-k if F} + attention.
 
     layers[l] holds fp64 arrays q_idx, k_idx, w (read on F layers only) and
@@ -222,8 +238,8 @@ def layer_stack(pattern: str, layers: Sequence[Dict[str, np.ndarray]], k: int,
     for l, role in enumerate(pattern):
         L = layers[l]
         if role == "F":
-            sc = indexer_scores(L["q_idx"], L["k_idx"], L["w"], q_pos0, Lk)
-            cache = topk(sc, k, q_pos0)
+            sc = indexer_scores(L["q_idx"], L["k_idx"], L["w"], q_pos0, Lk, q_pos)
+            cache = topk(sc, k, q_pos0, q_pos)
             calls += 1
             scores_all.append(sc)
         else:

@@ -116,3 +116,36 @@ def test_position_order_keeps_the_set_and_sorts_positions():
         v = b[b >= 0]
         assert set(a[a >= 0]) == set(v) and np.all(np.diff(v) > 0)
         assert np.all(b[len(v):] == -1)
+
+
+def test_ragged_positions_equal_per_sequence_runs():
+    # a decode batch of sequences with their own lengths, keys padded to the
+    # longest: each row equals the uniform path run on its own sequence alone
+    rng = np.random.default_rng(5)
+    lens = [5, 9, 12, 1]
+    B, Lk, H_I, d_I, k = len(lens), max(lens), 3, 4, 6
+    q = rng.integers(-4, 5, size=(B, 1, H_I, d_I)).astype(np.float64)
+    kk = rng.integers(-4, 5, size=(B, Lk, d_I)).astype(np.float64)
+    w = rng.choice([0.25, 0.5, 1.0], size=(B, 1, H_I))
+    q_pos = np.array([[n - 1] for n in lens])
+    sc = oracle.indexer_scores(q, kk, w, 0, q_pos=q_pos)
+    got = oracle.topk(sc, k, 0, q_pos=q_pos)
+    for b, n in enumerate(lens):
+        one = oracle.indexer_scores(q[b:b + 1], kk[b:b + 1, :n], w[b:b + 1], n - 1)
+        assert np.array_equal(sc[b, 0, :n], one[0, 0])
+        assert np.all(np.isneginf(sc[b, 0, n:]))
+        assert np.array_equal(got[b], oracle.topk(one, k, n - 1)[0])
+    # per-row positions q_pos0 + i reproduce the uniform chunk
+    q2 = rng.integers(-4, 5, size=(1, 4, H_I, d_I)).astype(np.float64)
+    w2 = rng.choice([0.25, 0.5, 1.0], size=(1, 4, H_I))
+    kk2 = kk[2:3]
+    uni = oracle.indexer_scores(q2, kk2, w2, 7)
+    rag = oracle.indexer_scores(q2, kk2, w2, 0, q_pos=np.arange(7, 11).reshape(1, 4))
+    assert np.array_equal(uni, rag)
+    # a negative position selects nothing; one past the keys reads as the last key
+    neg = oracle.topk(oracle.indexer_scores(q2, kk2, w2, 0, q_pos=np.full((1, 4), -1)), k, 0,
+                      q_pos=np.full((1, 4), -1))
+    assert np.all(neg == oracle.PAD)
+    far = oracle.indexer_scores(q2, kk2, w2, 0, q_pos=np.full((1, 4), 10 ** 6))
+    last = oracle.indexer_scores(q2, kk2, w2, 0, q_pos=np.full((1, 4), Lk - 1))
+    assert np.array_equal(far, last)
