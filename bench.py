@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--only", default="",
-                    help="prefill-12f | prefill-allf | decode | pmc (profiling)")
+                    help="prefill-12f | prefill-allf | decode | sweep | pmc (profiling)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CMD_F", "CMD_W"),
                     help="write profiles/hbm_traffic.md from the two counter passes (no GPU)")
     return ap.parse_args()
@@ -211,6 +211,79 @@ def long_context(L, chunk, H_I=64, d_I=128, k=2048, seed=0):
     return {"L": L, "chunk": chunk, "chunks": n, "ms": ms, "tokens_per_s": L / (ms * 1e-3),
             "indexer_flops": flops, "TFLOPs": flops / (ms * 1e-3) / 1e12,
             "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
+def decode_layer(lens, k=2048, H_I=64, d_I=128, H=64, D=128, seed=0, ragged=True):
+    """One F decode layer (fused indexer + top-k, then sparse attention) for a
+    batch of sequences with cache lengths `lens` (one new query each), keys
+    padded to the longest. ragged=False times the same batch as a uniform one
+    (every sequence at the longest length). Returns per-layer ms."""
+    import torch
+    import idxc_inputs as gen
+    import dsa_lightning_indexer_score_amd as idxc
+    B, Lk = len(lens), max(lens)
+    q, kk, w = gen.indexer_inputs(B, 1, Lk, H_I, d_I, kind="normal", seed=seed,
+                                  idx_std=d_I ** -0.5, device="cuda")
+    Q, K, V = gen.attn_inputs(B, 1, Lk, H, D, seed=seed + 1, device="cuda")
+    pos = torch.tensor([[n - 1] for n in lens], dtype=torch.int32, device="cuda")
+    ws = torch.empty(idxc.idxc_workspace_bytes(B, 1, Lk, Lk - 1, H_I, d_I, k, H, D),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, 1, k), dtype=torch.int32, device="cuda")
+    o = torch.empty_like(Q)
+    scale = D ** -0.5
+
+    def sel():
+        if ragged:
+            idxc.idxc_indexer_topk_ragged(q, kk, w, k, pos, workspace=ws, out=out,
+                                          order="position")
+        else:
+            idxc.idxc_indexer_topk(q, kk, w, k, q_pos0=Lk - 1, workspace=ws, out=out,
+                                   order="position")
+    idx_ms = events_ms(sel, 10)
+    att_ms = events_ms(lambda: idxc.idxc_sparse_attn(Q, K, V, out, scale, workspace=ws, out=o),
+                       10)
+    del q, kk, w, Q, K, V, ws
+    torch.cuda.empty_cache()
+    return idx_ms, att_ms
+
+
+def context_sweep():
+    """The pages' context grid (about 10K, 60K, 120K and 200K tokens): prefill
+    indexer + top-k of one layer in query chunks, and one decode layer for 64
+    sequences at that cache length, composed to the 47-layer 12-F decode step;
+    then a ragged decode batch (64 lengths spread over 1K..196K) against the
+    same batch padded to its longest sequence."""
+    import torch
+    out = {}
+    for L, chunk in ((10240, 2048), (61440, 4096), (122880, 4096), (196608, 4096)):
+        lc = long_context(L, chunk)
+        torch.cuda.empty_cache()
+        idx_ms, att_ms = decode_layer([L] * 64)
+        step12 = 12 * idx_ms + 47 * att_ms
+        out[str(L)] = {"prefill_indexer_topk_ms": lc["ms"],
+                       "prefill_indexer_topk_tokens_per_s": lc["tokens_per_s"],
+                       "prefill_indexer_TFLOPs": lc["TFLOPs"],
+                       "decode_layer_indexer_topk_ms": idx_ms,
+                       "decode_layer_attention_ms": att_ms,
+                       "decode_12F_step_ms_composed": step12,
+                       "decode_12F_tokens_per_s_composed": 64 / (step12 * 1e-3)}
+        log("context %d: prefill indexer+top-k %.1f ms (%.0f TFLOP/s); decode layer %.3f + %.3f ms"
+            % (L, lc["ms"], lc["TFLOPs"], idx_ms, att_ms))
+    import random
+    rnd = random.Random(0)
+    lens = [int(1024 + (196608 - 1024) * i / 63) for i in range(64)]
+    rnd.shuffle(lens)
+    r_idx, r_att = decode_layer(lens, ragged=True)
+    p_idx, p_att = decode_layer(lens, ragged=False)
+    out["ragged_decode"] = {
+        "lengths": "64 sequences, cache lengths evenly spread over 1024..196608 (mean %d)"
+                   % (sum(lens) // len(lens)),
+        "indexer_topk_ms": r_idx, "attention_ms": r_att,
+        "padded_indexer_topk_ms": p_idx, "padded_attention_ms": p_att,
+        "indexer_speedup_vs_padded": p_idx / r_idx}
+    log("ragged decode: indexer+top-k %.3f ms vs %.3f ms padded to the longest"
+        % (r_idx, p_idx))
+    return out
 
 
 def standalone_topk(B, Lq, Lk, q_pos0, k, seed=0):
@@ -424,12 +497,15 @@ def main():
     if args.only == "pmc":
         pmc_launches()
         return
+    if args.only == "sweep":
+        print(json.dumps({"context_sweep": context_sweep()}), flush=True)
+        return
 
     res = {}
     extra = {}
     # ----------------------------------------------------------------- prefill
     idx_ms = att_ms = pass_ms = None
-    if args.only != "decode":
+    if args.only not in ("decode",):
         cfg12, cfgF = gen.C3_12F, gen.C3_ALLF
         t0 = time.perf_counter()
         layers, sets = build_stack(cfg12, N_SETS)
@@ -510,6 +586,8 @@ def main():
         log("long context L=%d in %d chunks: %.1f ms, %.0f TFLOP/s indexer"
             % (lc["L"], lc["chunks"], lc["ms"], lc["TFLOPs"]))
         extra["long_context_indexer_topk"] = lc
+        torch.cuda.empty_cache()
+        extra["context_sweep"] = context_sweep()
         torch.cuda.empty_cache()
         tk = {"decode_rows": standalone_topk(64, 1, 65536, 65535, 2048),
               "prefill_rows": standalone_topk(1, 8192, 8192, 0, 2048)}

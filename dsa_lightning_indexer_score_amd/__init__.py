@@ -17,7 +17,8 @@ from ._lib import IdxcDims, IdxcError, IdxcLayer
 __all__ = ["idxc_version", "idxc_validate_pattern", "idxc_schedule", "idxc_indexer_scores",
            "idxc_topk", "idxc_topk_workspace_bytes", "idxc_workspace_bytes", "idxc_indexer_topk", "idxc_sparse_attn", "idxc_sparse_attn_workspace_bytes", "idxc_overlap",
            "idxc_layer_stack_forward", "idxc_overlap_matrix", "idxc_greedy_pattern",
-           "idxc_overlap_proxy_loss", "make_dims", "IdxcError", "StackCall"]
+           "idxc_overlap_proxy_loss", "idxc_indexer_topk_ragged",
+           "idxc_layer_stack_forward_ragged", "make_dims", "IdxcError", "StackCall"]
 
 
 def _stream(stream=None) -> ctypes.c_void_p:
@@ -126,8 +127,7 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=device)
 
 
-def idxc_indexer_topk(q_idx, k_idx, w, k: int, q_pos0: int = 0, workspace=None, out=None,
-                      stream=None, order: str = "score"):
+def _indexer_topk(q_idx, k_idx, w, k, q_pos0, q_pos, workspace, out, stream, order):
     lib = _lib.load()
     d = _idx_dims(q_idx, k_idx, q_pos0, k)
     if workspace is None:
@@ -135,13 +135,28 @@ def idxc_indexer_topk(q_idx, k_idx, w, k: int, q_pos0: int = 0, workspace=None, 
                                q_idx.device)
     if out is None:
         out = torch.empty((d.B, d.Lq, k), dtype=torch.int32, device=q_idx.device)
-    _lib.check(lib.idxc_indexer_topk(_ptr(q_idx, "q_idx", torch.bfloat16),
-                                     _ptr(k_idx, "k_idx", torch.bfloat16),
-                                     _ptr(w, "w", torch.bfloat16), ctypes.byref(d),
-                                     _order(order), _ptr(workspace, "workspace"),
-                                     workspace.numel() * workspace.element_size(),
-                                     _ptr(out, "indices", torch.int32), _stream(stream)))
+    args = [_ptr(q_idx, "q_idx", torch.bfloat16), _ptr(k_idx, "k_idx", torch.bfloat16),
+            _ptr(w, "w", torch.bfloat16), ctypes.byref(d)]
+    tail = [_order(order), _ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _ptr(out, "indices", torch.int32),
+            _stream(stream)]
+    if q_pos is None:
+        _lib.check(lib.idxc_indexer_topk(*args, *tail))
+    else:
+        _lib.check(lib.idxc_indexer_topk_ragged(*args, _ptr(q_pos, "q_pos", torch.int32), *tail))
     return out
+
+
+def idxc_indexer_topk(q_idx, k_idx, w, k: int, q_pos0: int = 0, workspace=None, out=None,
+                      stream=None, order: str = "score"):
+    return _indexer_topk(q_idx, k_idx, w, k, q_pos0, None, workspace, out, stream, order)
+
+
+def idxc_indexer_topk_ragged(q_idx, k_idx, w, k: int, q_pos, workspace=None, out=None,
+                             stream=None, order: str = "score"):
+    """Row r = b*Lq + i at absolute position q_pos[b, i] (int32 [B, Lq] on the
+    device; negative = no candidates); keys padded to the longest sequence."""
+    return _indexer_topk(q_idx, k_idx, w, k, 0, q_pos, workspace, out, stream, order)
 
 
 def idxc_sparse_attn_workspace_bytes(B, Lq, Lk, H, D, k) -> int:
@@ -177,6 +192,20 @@ def idxc_layer_stack_forward(pattern: str, layers: Sequence[Dict[str, torch.Tens
     """Run the stack. layers[l] holds q_idx, k_idx, w (F layers), q, k, v and
     optionally out. Returns dict(out=[...], indexer_calls=int,
     index_cache=tensor, debug_indices=tensor or None)."""
+    return _stack(pattern, layers, k, scale, q_pos0, None, index_cache, workspace,
+                  debug_indices, stream)
+
+
+def idxc_layer_stack_forward_ragged(pattern: str, layers: Sequence[Dict[str, torch.Tensor]],
+                                    k: int, scale: float, q_pos, index_cache=None,
+                                    workspace=None, debug_indices: bool = False, stream=None):
+    """The stack with per-row query positions q_pos (int32 [B, Lq] on the device)."""
+    return _stack(pattern, layers, k, scale, 0, q_pos, index_cache, workspace, debug_indices,
+                  stream)
+
+
+def _stack(pattern, layers, k, scale, q_pos0, q_pos, index_cache, workspace, debug_indices,
+           stream):
     lib = _lib.load()
     n = len(layers)
     ref = next(L for L in layers if L.get("q") is not None)
@@ -206,12 +235,15 @@ def idxc_layer_stack_forward(pattern: str, layers: Sequence[Dict[str, torch.Tens
                            _ptr(L["v"], "v", torch.bfloat16).value,
                            _ptr(o, "out", torch.bfloat16).value)
     calls = ctypes.c_int32(-1)
-    _lib.check(lib.idxc_layer_stack_forward(pattern.encode(), n, arr, ctypes.byref(d),
-                                            float(scale), _ptr(index_cache, "index_cache"),
-                                            _ptr(workspace, "workspace"),
-                                            workspace.numel() * workspace.element_size(),
-                                            ctypes.byref(calls), _ptr(dbg, "debug_indices"),
-                                            _stream(stream)))
+    head = [pattern.encode(), n, arr, ctypes.byref(d)]
+    tail = [float(scale), _ptr(index_cache, "index_cache"), _ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), ctypes.byref(calls),
+            _ptr(dbg, "debug_indices"), _stream(stream)]
+    if q_pos is None:
+        _lib.check(lib.idxc_layer_stack_forward(*head, *tail))
+    else:
+        _lib.check(lib.idxc_layer_stack_forward_ragged(*head, _ptr(q_pos, "q_pos", torch.int32),
+                                                       *tail))
     return dict(out=outs, indexer_calls=calls.value, index_cache=index_cache,
                 debug_indices=dbg)
 

@@ -34,6 +34,7 @@ EXPORTED = (
     "idxc_indexer_topk", "idxc_sparse_attn", "idxc_sparse_attn_workspace_bytes",
     "idxc_layer_stack_forward", "idxc_overlap", "idxc_overlap_matrix_workspace_bytes",
     "idxc_overlap_matrix", "idxc_greedy_pattern", "idxc_overlap_proxy_loss",
+    "idxc_indexer_topk_ragged", "idxc_layer_stack_forward_ragged",
 )
 
 # double loss(const char* pattern, void* user)
@@ -88,6 +89,11 @@ def load() -> ctypes.CDLL:
                                       ctypes.c_float, vp, vp, sz, P(i32), vp, vp],
                                      ctypes.c_int),
         "idxc_overlap": ([vp, vp, P(IdxcDims), vp, vp, vp, vp], ctypes.c_int),
+        "idxc_indexer_topk_ragged": ([vp, vp, vp, P(IdxcDims), vp, ctypes.c_int32, vp, sz, vp,
+                                      vp], ctypes.c_int),
+        "idxc_layer_stack_forward_ragged": ([ctypes.c_char_p, i32, P(IdxcLayer), P(IdxcDims), vp,
+                                             ctypes.c_float, vp, vp, sz, P(i32), vp, vp],
+                                            ctypes.c_int),
         "idxc_overlap_matrix_workspace_bytes": ([i32], sz),
         "idxc_overlap_matrix": ([vp, i32, P(IdxcDims), vp, sz, vp, vp], ctypes.c_int),
         "idxc_greedy_pattern": ([i32, i32, LOSS_FN, vp, ctypes.c_char_p, P(ctypes.c_int64)],

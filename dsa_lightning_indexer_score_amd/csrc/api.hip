@@ -129,17 +129,19 @@ struct Plan {
   size_t min_bytes;
 };
 
-// The few-row path writes per-chunk top-k segments that one workgroup per
-// row must be able to stage.
+// The few-row path writes per-chunk top-k segments; one workgroup per row
+// selects from them, after a per-group stage when there are too many to
+// stage at once.
 bool split_topk_fits(const idxc_dims* d) {
-  const long long nch = indexer_split_chunks(d->Lk);
-  return nch <= kMaxSegments && nch * d->k <= kMaxStagePairs;
+  const int nch = indexer_split_chunks(d->Lk);
+  return nch <= kMaxSegments && topk_segment_groups(nch, d->k) >= 1;
 }
 
 size_t split_part_bytes(const idxc_dims* d) {
   const size_t rows = (size_t)d->B * d->Lq;
   const size_t nch = (size_t)indexer_split_chunks(d->Lk);
-  return align_up(rows * nch * d->k * 8) + align_up(rows * nch * 4);
+  return align_up(rows * nch * d->k * 8) + align_up(rows * nch * 4) +
+         align_up(topk_group_bytes((int)rows, (int)nch, d->k));
 }
 
 Plan plan_for(const idxc_dims* d, bool with_attn = false) {
@@ -193,8 +195,9 @@ bool topk_rows_supported(const idxc_dims* d) {
 // Indexer + top-k for one layer into `indices`, using the workspace.
 hipError_t run_indexer_topk(const void* q_idx, const void* k_idx, const void* w,
                             const idxc_dims* d, void* ws, size_t ws_bytes, int32_t* indices,
-                            bool pos_order, hipStream_t st) {
+                            bool pos_order, const int32_t* q_pos, hipStream_t st) {
   IndexerArgs ia{};
+  ia.q_pos = q_pos;
   ia.q_idx = static_cast<const uint16_t*>(q_idx);
   ia.k_idx = static_cast<const uint16_t*>(k_idx);
   ia.w = static_cast<const uint16_t*>(w);
@@ -223,6 +226,12 @@ hipError_t run_indexer_topk(const void* q_idx, const void* k_idx, const void* w,
     if (e != hipSuccess) return e;
     ta.cand = ia.cand;
     ta.cand_count = ia.cand_count;
+    const int groups = topk_segment_groups(nch, d->k);
+    if (groups > 1) {  // scratch of the per-group stage, after the segments
+      uint8_t* gb = base + align_up((size_t)rows * nch * d->k * 8) + align_up((size_t)rows * nch * 4);
+      ta.part = reinterpret_cast<u32x2_t*>(gb);
+      ta.part_count = reinterpret_cast<int*>(gb + (size_t)rows * groups * d->k * 8);
+    }
     ta.nseg = nch;
     ta.seg_cap = d->k;
     ta.stage_cap = nch * d->k;
@@ -379,7 +388,31 @@ int idxc_indexer_topk(const void* q_idx, const void* k_idx, const void* w,
     return fail(IDXC_ERR_INVALID_ARG, "workspace of %zu bytes is below the minimum %zu",
                 workspace_bytes, p.min_bytes);
   return hip_status(run_indexer_topk(q_idx, k_idx, w, dims, workspace, workspace_bytes, indices,
-                                     order == IDXC_ORDER_POSITION,
+                                     order == IDXC_ORDER_POSITION, nullptr,
+                                     static_cast<hipStream_t>(hip_stream)),
+                    "indexer_topk launch");
+}
+
+int idxc_indexer_topk_ragged(const void* q_idx, const void* k_idx, const void* w,
+                             const idxc_dims* dims, const int32_t* q_pos, int32_t order,
+                             void* workspace, size_t workspace_bytes, int32_t* indices,
+                             void* hip_stream) {
+  REQUIRE_PTR(q_pos, "q_pos");
+  int r = check_dims(dims, 1 | 4);
+  if (r != IDXC_OK) return r;
+  if (order != IDXC_ORDER_SCORE && order != IDXC_ORDER_POSITION)
+    return fail(IDXC_ERR_INVALID_ARG, "order = %d is not an IDXC_ORDER_* value", order);
+  REQUIRE_PTR(q_idx, "q_idx");
+  REQUIRE_PTR(k_idx, "k_idx");
+  REQUIRE_PTR(w, "w");
+  REQUIRE_PTR(workspace, "workspace");
+  REQUIRE_PTR(indices, "indices");
+  const Plan p = plan_for(dims);
+  if (workspace_bytes < p.min_bytes)
+    return fail(IDXC_ERR_INVALID_ARG, "workspace of %zu bytes is below the minimum %zu",
+                workspace_bytes, p.min_bytes);
+  return hip_status(run_indexer_topk(q_idx, k_idx, w, dims, workspace, workspace_bytes, indices,
+                                     order == IDXC_ORDER_POSITION, q_pos,
                                      static_cast<hipStream_t>(hip_stream)),
                     "indexer_topk launch");
 }
@@ -522,10 +555,10 @@ int idxc_greedy_pattern(int32_t n_layers, int32_t removals, idxc_loss_fn loss, v
   return ok();
 }
 
-int idxc_layer_stack_forward(const char* pattern, int32_t n_layers, const idxc_layer* layers,
-                             const idxc_dims* dims, float scale, int32_t* index_cache,
-                             void* workspace, size_t workspace_bytes, int32_t* indexer_calls,
-                             int32_t* debug_indices, void* hip_stream) {
+static int stack_forward(const char* pattern, int32_t n_layers, const idxc_layer* layers,
+                         const idxc_dims* dims, const int32_t* q_pos, float scale,
+                         int32_t* index_cache, void* workspace, size_t workspace_bytes,
+                         int32_t* indexer_calls, int32_t* debug_indices, void* hip_stream) {
   int r = check_pattern(pattern, n_layers, nullptr);
   if (r != IDXC_OK) return r;
   r = check_dims(dims, 1 | 2 | 4);
@@ -571,7 +604,7 @@ int idxc_layer_stack_forward(const char* pattern, int32_t n_layers, const idxc_l
       // the cache keeps each row's top-k set in position order: attention
       // does not depend on the order, and its gathers then sweep the keys
       hipError_t e = run_indexer_topk(L.q_idx, L.k_idx, L.w, dims, workspace, workspace_bytes,
-                                      index_cache, true, st);
+                                      index_cache, true, q_pos, st);
       if (e != hipSuccess) {
         *indexer_calls = calls;
         return hip_status(e, "stack indexer launch");
@@ -595,6 +628,25 @@ int idxc_layer_stack_forward(const char* pattern, int32_t n_layers, const idxc_l
   }
   *indexer_calls = calls;
   return ok();
+}
+
+int idxc_layer_stack_forward(const char* pattern, int32_t n_layers, const idxc_layer* layers,
+                             const idxc_dims* dims, float scale, int32_t* index_cache,
+                             void* workspace, size_t workspace_bytes, int32_t* indexer_calls,
+                             int32_t* debug_indices, void* hip_stream) {
+  return stack_forward(pattern, n_layers, layers, dims, nullptr, scale, index_cache, workspace,
+                       workspace_bytes, indexer_calls, debug_indices, hip_stream);
+}
+
+int idxc_layer_stack_forward_ragged(const char* pattern, int32_t n_layers,
+                                    const idxc_layer* layers, const idxc_dims* dims,
+                                    const int32_t* q_pos, float scale, int32_t* index_cache,
+                                    void* workspace, size_t workspace_bytes,
+                                    int32_t* indexer_calls, int32_t* debug_indices,
+                                    void* hip_stream) {
+  REQUIRE_PTR(q_pos, "q_pos");
+  return stack_forward(pattern, n_layers, layers, dims, q_pos, scale, index_cache, workspace,
+                       workspace_bytes, indexer_calls, debug_indices, hip_stream);
 }
 
 }  // extern "C"

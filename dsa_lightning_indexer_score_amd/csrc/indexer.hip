@@ -195,7 +195,7 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
                          const uint16_t* __restrict__ w, int B, int Lq, int Lk,
                          int q_pos0, int H_I, float* __restrict__ scores,
                          u32x2* __restrict__ cand, int* __restrict__ cand_count,
-                         int cap, int k) {
+                         int cap, int k, const int32_t* __restrict__ q_pos) {
   constexpr int NCH = DI / 8;            // 16-byte chunks per key row
   constexpr int KS = DI / 16;            // MFMA k-steps over d_I
   constexpr int TILE_CHUNKS = kKeyTile * NCH;
@@ -206,6 +206,7 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
   __shared__ __attribute__((aligned(16))) uint8_t tile_lds[2][kKeyTile * ROW_BYTES];
   __shared__ __attribute__((aligned(16))) uint32_t samp_lds[MODE == 1 ? kRowWaves * kSampleKeys : 4];
   __shared__ int rescan_lds;
+  __shared__ int trange_lds[2];
 
   const int nqb = (Lq + kRowWaves - 1) / kRowWaves;
   // longest rows first: block 0 takes the last query block of every batch
@@ -215,12 +216,31 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
   const int lane = lane_id();
   const int i_row = qb * kRowWaves + wave;
   const bool active = i_row < Lq;
-  const int t = q_pos0 + i_row;
-  const int t_first = q_pos0 + qb * kRowWaves;
-  const int last_row = min(qb * kRowWaves + kRowWaves - 1, Lq - 1);
-  const int t_last = q_pos0 + last_row;
-  const int ntiles = t_last / kKeyTile + 1;
   const size_t row = (size_t)b * Lq + (active ? i_row : 0);
+  // Query positions: q_pos0 + i, or per row from q_pos (ragged batches;
+  // negative = no candidates, past the keys = the last key). t_first / t_last
+  // are the least / greatest position of the workgroup's rows that have
+  // candidates.
+  int t = q_pos0 + i_row;
+  int t_first = q_pos0 + qb * kRowWaves;
+  int t_last = q_pos0 + min(qb * kRowWaves + kRowWaves - 1, Lq - 1);
+  if (q_pos != nullptr) {
+    t = active ? q_pos[row] : -1;
+    t = t < 0 ? -1 : min(t, Lk - 1);
+    if (threadIdx.x == 0) {
+      trange_lds[0] = 0x7FFFFFFF;
+      trange_lds[1] = -1;
+    }
+    __syncthreads();
+    if (lane == 0 && t >= 0) {
+      atomicMin(&trange_lds[0], t);
+      atomicMax(&trange_lds[1], t);
+    }
+    __syncthreads();
+    t_last = trange_lds[1];
+    t_first = t_last < 0 ? -1 : trange_lds[0];
+  }
+  const int ntiles = t_last < 0 ? 0 : t_last / kKeyTile + 1;
 
   // --- query operands (A: heads x d) and head weights, held in registers
   bf16x8 a_op[HB][KS];
@@ -344,7 +364,7 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
   // pass 0: sample tiles (if any) then the causal key sweep; pass 1 (rare):
   // the sweep again, without threshold, for rows whose sampled threshold
   // turned out too high
-  bool compute_row = active;
+  bool compute_row = active && t >= 0;
   for (int pass = 0; pass < (MODE == 1 ? 2 : 1); ++pass) {
     int nsamp = 0;
     if (MODE == 1 && pass == 0 && t_first + 1 > cap) {
@@ -560,7 +580,8 @@ void indexer_split_topk_kernel(const uint16_t* __restrict__ q_idx,
                                const uint16_t* __restrict__ k_idx,
                                const uint16_t* __restrict__ w, int B, int Lq, int Lk,
                                int q_pos0, int H_I, int k, int nchunks,
-                               u32x2* __restrict__ part, int* __restrict__ part_count) {
+                               u32x2* __restrict__ part, int* __restrict__ part_count,
+                               const int32_t* __restrict__ q_pos) {
   constexpr int KS = DI / 16;
   __shared__ __attribute__((aligned(16))) uint32_t skey[kDecChunk];
   __shared__ SelectSmem sel;
@@ -568,7 +589,9 @@ void indexer_split_topk_kernel(const uint16_t* __restrict__ q_idx,
   const size_t row = blockIdx.x / nchunks;  // b * Lq + i
   const int b = (int)(row / Lq);
   const int i_row = (int)(row % Lq);
-  const int t = q_pos0 + i_row;
+  // per-row positions (ragged batches): negative = no candidates, past the
+  // keys = the last key
+  const int t = q_pos ? (q_pos[row] < 0 ? -1 : min(q_pos[row], Lk - 1)) : q_pos0 + i_row;
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
   const int c0 = chunk * kDecChunk;
@@ -656,7 +679,8 @@ hipError_t launch_split_topk(const IndexerArgs& a, hipStream_t st) {
   const int nchunks = (a.Lk + kDecChunk - 1) / kDecChunk;
   dim3 grid((unsigned)(nchunks * a.B * a.Lq)), block(kSplitWaves * kWave);
   hipLaunchKernelGGL((indexer_split_topk_kernel<DI, HB>), grid, block, 0, st, a.q_idx, a.k_idx,
-                     a.w, a.B, a.Lq, a.Lk, a.q_pos0, a.H_I, a.k, nchunks, a.cand, a.cand_count);
+                     a.w, a.B, a.Lq, a.Lk, a.q_pos0, a.H_I, a.k, nchunks, a.cand, a.cand_count,
+                     a.q_pos);
   return hipGetLastError();
 }
 
@@ -667,11 +691,11 @@ hipError_t launch_rows(const IndexerArgs& a, int mode, hipStream_t st) {
   if (mode == 0) {
     hipLaunchKernelGGL((indexer_rows_kernel<DI, HB, 0>), grid, block, 0, st, a.q_idx, a.k_idx,
                        a.w, a.B, a.Lq, a.Lk, a.q_pos0, a.H_I, a.scores, nullptr, nullptr, 0,
-                       a.k);
+                       a.k, nullptr);
   } else {
     hipLaunchKernelGGL((indexer_rows_kernel<DI, HB, 1>), grid, block, 0, st, a.q_idx, a.k_idx,
                        a.w, a.B, a.Lq, a.Lk, a.q_pos0, a.H_I, nullptr, a.cand, a.cand_count,
-                       a.cap, a.k);
+                       a.cap, a.k, a.q_pos);
   }
   return hipGetLastError();
 }

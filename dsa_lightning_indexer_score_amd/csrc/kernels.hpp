@@ -16,6 +16,9 @@ struct IndexerArgs {
   uint32_t __attribute__((ext_vector_type(2)))* cand;  // candidate mode: (order key, s)
   int* cand_count;
   int cap;
+  // per-row query positions [B*Lq] (device; NULL = q_pos0 + i); candidate
+  // and few-row top-k modes only
+  const int32_t* q_pos;
 };
 
 // Materialised scores [B, Lq, Lk].
@@ -59,6 +62,11 @@ int topk_row_chunks(int Lk);
 // Scratch bytes launch_topk needs for materialised rows of length Lk.
 size_t topk_part_bytes(int rows, int Lk, int k);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+// Candidate rows of nseg segments of k: groups of segments selected first when
+// one workgroup cannot stage them all (1 = single stage, 0 = unsupported),
+// and the scratch (TopkArgs::part / part_count) that first stage writes.
+int topk_segment_groups(int nseg, int k);
+size_t topk_group_bytes(int rows, int nseg, int k);
 
 struct AttnArgs {
   const uint16_t* q;

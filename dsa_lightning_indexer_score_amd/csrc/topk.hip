@@ -158,21 +158,27 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int sort_off) {
       }
     }
   } else {
+    // segments [s0, s1) of the row: all of them (nchunks = 1), or group
+    // `chunk` of ceil(nseg / nchunks) consecutive segments (a stage of a
+    // two-level selection); consecutive segments keep position order
+    const int per_group = (a.nseg + nchunks - 1) / nchunks;
+    const int s0 = min(a.nseg, chunk * per_group);
+    const int ns = min(a.nseg, s0 + per_group) - s0;
     if (tid == 0) {
       int off = 0;
-      for (int s = 0; s < a.nseg; ++s) {
+      for (int s = 0; s < ns; ++s) {
         sm.seg_off[s] = off;
-        off += a.cand_count[row * a.nseg + s];
+        off += a.cand_count[row * a.nseg + s0 + s];
       }
-      sm.seg_off[a.nseg] = off;
+      sm.seg_off[ns] = off;
     }
     __syncthreads();
-    n = sm.seg_off[a.nseg];
+    n = sm.seg_off[ns];
     spos = skey + a.stage_cap;
-    for (int s = 0; s < a.nseg; ++s) {
+    for (int s = 0; s < ns; ++s) {
       const int off = sm.seg_off[s];
       const int cnt = sm.seg_off[s + 1] - off;
-      const u32x2* src = a.cand + ((size_t)row * a.nseg + s) * a.seg_cap;
+      const u32x2* src = a.cand + ((size_t)row * a.nseg + s0 + s) * a.seg_cap;
       for (int base = 0; base < cnt; base += NT * kBatch) {
         u32x2 v[kBatch];
 #pragma unroll
@@ -289,16 +295,51 @@ size_t topk_part_bytes(int rows, int Lk, int k) {
   return (size_t)rows * nch * k * 8 + (size_t)rows * nch * 4 + 256;
 }
 
+int topk_segment_groups(int nseg, int k) {
+  if ((long long)nseg * k <= kMaxStagePairs) return 1;
+  const int per_group = kMaxStagePairs / k;  // segments one workgroup stages
+  const int groups = (nseg + per_group - 1) / per_group;
+  return (long long)groups * k <= kMaxStagePairs ? groups : 0;
+}
+
+size_t topk_group_bytes(int rows, int nseg, int k) {
+  const int g = topk_segment_groups(nseg, k);
+  if (g <= 1) return 0;
+  return (size_t)rows * g * k * 8 + (size_t)rows * g * 4 + 256;
+}
+
 hipError_t launch_topk(const TopkArgs& a0, hipStream_t st) {
   TopkArgs a = a0;
   if (a.cand) {
     // candidate lists (one or more position-ordered segments per row); keys,
     // then positions when there are several segments, each area a multiple
     // of 16 bytes
-    a.stage_cap = (a.stage_cap + 3) / 4 * 4;
-    if (a.nseg == 1)
+    if (a.nseg == 1) {
+      a.stage_cap = (a.stage_cap + 3) / 4 * 4;
       return launch_one<kSrcCand1, kOutFinal>(a, 0, 1, (size_t)a.stage_cap * 4, st);
-    return launch_one<kSrcCand, kOutFinal, kThreadsWide>(a, 0, 1, (size_t)a.stage_cap * 8, st);
+    }
+    const int groups = topk_segment_groups(a.nseg, a.k);
+    if (groups <= 1) {
+      a.stage_cap = (a.stage_cap + 3) / 4 * 4;
+      return launch_one<kSrcCand, kOutFinal, kThreadsWide>(a, 0, 1, (size_t)a.stage_cap * 8,
+                                                           st);
+    }
+    // too many segments for one workgroup: the exact top-k of each group of
+    // consecutive segments (into a.part), then of the groups' winners (every
+    // key of the row's top-k is in its group's top-k)
+    TopkArgs g = a;
+    const int per_group = (a.nseg + groups - 1) / groups;
+    g.stage_cap = (per_group * a.k + 3) / 4 * 4;
+    hipError_t e = launch_one<kSrcCand, kOutPart, kThreadsWide>(g, 0, groups,
+                                                                (size_t)g.stage_cap * 8, st);
+    if (e != hipSuccess) return e;
+    TopkArgs f = a;
+    f.cand = a.part;
+    f.cand_count = a.part_count;
+    f.nseg = groups;
+    f.seg_cap = a.k;
+    f.stage_cap = (groups * a.k + 3) / 4 * 4;
+    return launch_one<kSrcCand, kOutFinal, kThreadsWide>(f, 0, 1, (size_t)f.stage_cap * 8, st);
   }
   const int nch = topk_row_chunks(a.Lk);
   if (nch <= 1) {

@@ -194,6 +194,27 @@ int idxc_layer_stack_forward(const char* pattern, int32_t n_layers,
                              size_t workspace_bytes, int32_t* indexer_calls,
                              int32_t* debug_indices, void* hip_stream);
 
+/* Ragged batches (per-sequence lengths and positions, as a serving batch
+ * has them): like idxc_indexer_topk / idxc_layer_stack_forward, but query row
+ * r = b*Lq + i sits at the absolute position q_pos[r] (DEVICE int32 [B*Lq])
+ * instead of q_pos0 + i, and scores keys 0..q_pos[r] of its batch. Keys stay
+ * in [B, Lk, d] buffers padded to the longest sequence (Lk); a row with
+ * q_pos[r] < 0 selects nothing (all -1; its attention output is 0), and a
+ * position >= Lk is read as Lk - 1. dims->q_pos0 is not used for positions
+ * but must still pass the usual checks (0 is fine). A decode batch of
+ * sequences with lengths n_b is B rows with Lq = 1, q_pos[b] = n_b - 1 and
+ * Lk = max n_b. Workspace as for the uniform calls with the same dims. */
+int idxc_indexer_topk_ragged(const void* q_idx, const void* k_idx, const void* w,
+                             const idxc_dims* dims, const int32_t* q_pos, int32_t order,
+                             void* workspace, size_t workspace_bytes, int32_t* indices,
+                             void* hip_stream);
+int idxc_layer_stack_forward_ragged(const char* pattern, int32_t n_layers,
+                                    const idxc_layer* layers, const idxc_dims* dims,
+                                    const int32_t* q_pos, float scale, int32_t* index_cache,
+                                    void* workspace, size_t workspace_bytes,
+                                    int32_t* indexer_calls, int32_t* debug_indices,
+                                    void* hip_stream);
+
 /* Cross-layer agreement of two index tensors a, b [B,Lq,k] int32 (DEVICE;
  * entries are positions in [0, Lk) or -1, in any order; other values are
  * ignored). Per row, over the valid entries taken as sets: inter = |A ∩ B|,

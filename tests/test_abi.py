@@ -266,3 +266,23 @@ def test_overlap_matrix_argument_errors(lib):
     big = ctypes.byref(_dims(Lq=1, Lk=262145, q_pos0=262144, k=16))
     assert f(P(), 4, big, P(), ws, P(), None) == _lib.IDXC_ERR_UNSUPPORTED
     assert f(P(), 4, ctypes.byref(_dims(k=0)), P(), ws, P(), None) == _lib.IDXC_ERR_INVALID_ARG
+
+
+def test_ragged_argument_errors(lib):
+    f = lib.idxc_indexer_topk_ragged
+    d = ctypes.byref(_dims(Lq=8, Lk=64, k=16))
+    # q_pos NULL or misaligned; then the usual checks of the uniform call
+    assert f(P(), P(), P(), d, None, 0, P(), 1 << 30, P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), P(), P(), d, P(FAKE + 4), 0, P(), 1 << 30, P(), None) == \
+        _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), P(), P(), d, P(), 7, P(), 1 << 30, P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), P(), P(), d, P(), 0, P(), 16, P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), P(), P(), ctypes.byref(_dims(d_I=48)), P(), 0, P(), 1 << 30, P(), None) == \
+        _lib.IDXC_ERR_UNSUPPORTED
+    g = lib.idxc_layer_stack_forward_ragged
+    calls = ctypes.c_int32(0)
+    layer = (IdxcLayer * 1)(IdxcLayer(*([FAKE] * 7)))
+    assert g(b"F", 1, layer, d, None, 1.0, P(), P(), 1 << 30, ctypes.byref(calls), None,
+             None) == _lib.IDXC_ERR_INVALID_ARG
+    assert g(b"S", 1, layer, d, P(), 1.0, P(), P(), 1 << 30, ctypes.byref(calls), None,
+             None) == _lib.IDXC_ERR_PATTERN

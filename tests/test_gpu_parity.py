@@ -375,6 +375,116 @@ def test_stack_random_small_overlap():
 
 
 # --------------------------------------------------------------------------- #
+# ragged batches: per-row query positions
+# --------------------------------------------------------------------------- #
+def _ragged_ref(q, kk, w, q_pos, k):
+    sc = oracle.indexer_scores(f64(q), f64(kk), f64(w), 0, q_pos=q_pos)
+    return oracle.topk(sc, k, 0, q_pos=q_pos)
+
+
+@pytest.mark.parametrize("order", ["score", "position"])
+def test_ragged_decode_batch_exact(order):
+    # sequences of their own lengths (shorter than k, one chunk, several
+    # 8192-key chunks) in key buffers padded to the longest: few-row path
+    lens = [1, 300, 2048, 5000, 9000, 20000]
+    B, Lk, H_I, d_I, k = len(lens), max(lens), 64, 128, 2048
+    q, kk, w = gen.indexer_inputs(B, 1, Lk, H_I, d_I, kind="int", seed=41, w_kind="quarter")
+    q_pos = np.array([[n - 1] for n in lens], dtype=np.int32)
+    _say("ragged decode lens=%s order=%s" % (lens, order))
+    got = idxc.idxc_indexer_topk_ragged(cu(q), cu(kk), cu(w), k, cu(torch.from_numpy(q_pos)),
+                                        order=order)
+    torch.cuda.synchronize()
+    want = _ragged_ref(q, kk, w, q_pos, k)
+    if order == "position":
+        want = oracle.position_order(want)
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
+def test_long_decode_rows_grouped_selection_exact():
+    # rows longer than 8 chunks of 8192 keys: the chunk segments no longer fit
+    # one workgroup and are selected per group of segments first
+    lens = [140000, 70000, 5, 90001]
+    B, Lk, H_I, d_I, k = len(lens), max(lens), 64, 128, 2048
+    q, kk, w = gen.indexer_inputs(B, 1, Lk, H_I, d_I, kind="int", seed=47, w_kind="quarter")
+    q_pos = np.array([[n - 1] for n in lens], dtype=np.int32)
+    _say("grouped decode selection lens=%s" % lens)
+    pos_t = cu(torch.from_numpy(q_pos))
+    got_s = idxc.idxc_indexer_topk_ragged(cu(q), cu(kk), cu(w), k, pos_t)
+    got_p = idxc.idxc_indexer_topk_ragged(cu(q), cu(kk), cu(w), k, pos_t, order="position")
+    # the uniform call on the longest row (q_pos0 = Lk - 1) takes the same path
+    uni = idxc.idxc_indexer_topk(cu(q[:1]), cu(kk[:1]), cu(w[:1]), k, q_pos0=Lk - 1)
+    torch.cuda.synchronize()
+    want = _ragged_ref(q, kk, w, q_pos, k)
+    assert np.array_equal(got_s.cpu().numpy(), want)
+    assert np.array_equal(got_p.cpu().numpy(), oracle.position_order(want))
+    assert np.array_equal(uni.cpu().numpy(), want[:1])
+
+
+@pytest.mark.parametrize("Lk,k,ws", [(3000, 256, None), (6000, 64, None), (6000, 64, "min")])
+def test_ragged_rows_exact(Lk, k, ws):
+    # many rows at scattered positions (negative, past the keys, short and
+    # long rows in one workgroup): row-stationary path, with sampled
+    # thresholds and, with the minimum workspace, compactions
+    rng = np.random.default_rng(Lk + k)
+    B, Lq, H_I, d_I = 2, 200, 64, 128
+    q, kk, w = gen.indexer_inputs(B, Lq, Lk, H_I, d_I, kind="int", seed=43, w_kind="quarter")
+    q_pos = rng.integers(0, Lk, size=(B, Lq)).astype(np.int32)
+    q_pos[0, :5] = -1
+    q_pos[1, :3] = Lk + 17
+    q_pos[1, 3:11] = np.arange(8)          # rows shorter than k
+    workspace = None
+    if ws == "min":
+        d = idxc.make_dims(B, Lq, Lk, 0, H_I, d_I, k=k)
+        need = (B * Lq * 4 + 255) // 256 * 256 + B * Lq * ((k + 64 + 63) // 64 * 64) * 8
+        workspace = torch.empty((need,), dtype=torch.uint8, device="cuda")
+    _say("ragged rows Lk=%d k=%d ws=%s" % (Lk, k, ws))
+    got = idxc.idxc_indexer_topk_ragged(cu(q), cu(kk), cu(w), k, cu(torch.from_numpy(q_pos)),
+                                        workspace=workspace)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), _ragged_ref(q, kk, w, q_pos, k))
+    assert np.all(got.cpu().numpy()[0, :5] == -1)
+
+
+def test_ragged_uniform_positions_equal_uniform_call():
+    B, Lq, Lk, H_I, d_I, k = 1, 512, 4096, 64, 128, 256
+    q, kk, w = gen.indexer_inputs(B, Lq, Lk, H_I, d_I, kind="normal", seed=44,
+                                  idx_std=128 ** -0.5)
+    q_pos0 = Lk - Lq
+    pos = torch.arange(q_pos0, Lk, dtype=torch.int32).reshape(1, Lq)
+    a = idxc.idxc_indexer_topk(cu(q), cu(kk), cu(w), k, q_pos0=q_pos0)
+    b = idxc.idxc_indexer_topk_ragged(cu(q), cu(kk), cu(w), k, cu(pos))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_ragged_decode_stack_matches_oracle():
+    # a 3-layer FSF decode step over sequences of different lengths
+    lens = [700, 64, 3000, 1]
+    B, Lk, H_I, d_I, H, D, k = len(lens), max(lens), 8, 64, 16, 64, 128
+    layers = []
+    for l in range(3):
+        qi, ki, wi = gen.indexer_inputs(B, 1, Lk, H_I, d_I, kind="int", seed=50 + l,
+                                        w_kind="quarter")
+        Q, K, V = gen.attn_inputs(B, 1, Lk, H, D, seed=60 + l)
+        layers.append(dict(q_idx=qi, k_idx=ki, w=wi, q=Q, k=K, v=V))
+    q_pos = np.array([[n - 1] for n in lens], dtype=np.int32)
+    scale = D ** -0.5
+    _say("ragged decode stack lens=%s" % lens)
+    res = idxc.idxc_layer_stack_forward_ragged(
+        "FSF", [{n: cu(t) for n, t in L.items()} for L in layers], k, scale,
+        cu(torch.from_numpy(q_pos)), debug_indices=True)
+    torch.cuda.synchronize()
+    ref = oracle.layer_stack("FSF", [{n: f64(t) for n, t in L.items()} for L in layers], k,
+                             scale, 0, q_pos=q_pos)
+    assert res["indexer_calls"] == ref["calls"] == 2
+    dbg = res["debug_indices"].cpu().numpy()
+    for l in range(3):
+        assert np.array_equal(dbg[l], oracle.position_order(ref["indices"][l]))
+        err = np.abs(res["out"][l].float().cpu().numpy() - ref["out"][l]).max()
+        assert err <= ATOL, (l, err)
+
+
+# --------------------------------------------------------------------------- #
 # cross-layer agreement of index sets
 # --------------------------------------------------------------------------- #
 def _set_stats(a, b):
