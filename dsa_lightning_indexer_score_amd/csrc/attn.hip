@@ -60,12 +60,6 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp));
 }
 
-template <int NRW>
-struct Gather {
-  u32x4 k[NRW];
-  u32x4 v[NRW];
-};
-
 template <int D, int HB>
 __global__ __launch_bounds__(kAttnWaves * kWave, (D == 128 && HB == 1) ? 1 : 2)
 void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kmat,
@@ -123,33 +117,48 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   // them below 2^32)
   const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(kb);
   const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(vb);
-  auto gather = [&](Gather<NRW>& g, int row_of_lane) {
-    uint32_t off[NRW];
+  struct Off {
+    uint32_t o[NRW];
+  };
+  struct Rows {
+    u32x4 r[NRW];
+  };
+  auto offsets = [&](int row_of_lane) {
+    Off f;
 #pragma unroll
-    for (int r = 0; r < NRW; ++r) off[r] = (uint32_t)__shfl(row_of_lane, gkey0 + r, kWave);
+    for (int r = 0; r < NRW; ++r)
+      f.o[r] = (uint32_t)__shfl(row_of_lane, gkey0 + r, kWave) * (uint32_t)(2 * D) +
+               (uint32_t)gch * 16u;
+    return f;
+  };
+  auto gather = [&](const uint8_t* src, const Off& f, Rows& g) {
 #pragma unroll
-    for (int r = 0; r < NRW; ++r) {
-      const uint32_t o = off[r] * (uint32_t)(2 * D) + (uint32_t)gch * 16u;
-      g.k[r] = *reinterpret_cast<const u32x4*>(kb8 + o);
-      g.v[r] = *reinterpret_cast<const u32x4*>(vb8 + o);
-    }
+    for (int r = 0; r < NRW; ++r) g.r[r] = *reinterpret_cast<const u32x4*>(src + f.o[r]);
   };
   uint8_t* base = dyn + ul * 2 * BL::BYTES;
-  auto stage = [&](const Gather<NRW>& g, int buf) {
-    uint8_t* kl = base + buf * BL::BYTES;
-    uint8_t* vl = kl + BL::KB;
+  auto kbuf = [&](int b) { return base + (b & 1) * BL::BYTES; };
+  auto vbuf = [&](int b) { return base + (b & 1) * BL::BYTES + BL::KB; };
+  auto stage_k = [&](const Rows& g, int b) {
 #pragma unroll
-    for (int r = 0; r < NRW; ++r) {
-      *reinterpret_cast<u32x4*>(kl + (gkey0 + r) * BL::SK + gch * 16) = g.k[r];
-      *reinterpret_cast<u32x4*>(vl + (gkey0 + r) * BL::SV + gch * 16) = g.v[r];
-    }
+    for (int r = 0; r < NRW; ++r)
+      *reinterpret_cast<u32x4*>(kbuf(b) + (gkey0 + r) * BL::SK + gch * 16) = g.r[r];
+  };
+  auto stage_v = [&](const Rows& g, int b) {
+#pragma unroll
+    for (int r = 0; r < NRW; ++r)
+      *reinterpret_cast<u32x4*>(vbuf(b) + (gkey0 + r) * BL::SV + gch * 16) = g.r[r];
   };
   // index of key (lane % 32) of block j; invalid entries gather row 0 and are
   // masked out of the softmax
+  // the row's index list through a buffer resource (a 32-bit offset, no
+  // 64-bit address registers): every load is issued unconditionally, at
+  // entry 0 when it lies outside the unit's slice
+  const __amdgpu_buffer_rsrc_t irsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(irow), (short)0, k * 4, 0x00020000);
   auto raw_index = [&](int j) {
     const int e = kbeg + j * 32 + (lane & 31);
     const bool in = active && j < nblk && e < kend;
-    const int v = irow[in ? e : 0];  // unconditional load (entry 0 always exists)
+    const int v = __builtin_amdgcn_raw_buffer_load_b32(irsrc, (in ? e : 0) * 4, 0, 0);
     return in ? v : -1;
   };
   auto resolve = [&](int idx, uint32_t* vmask) {
@@ -157,33 +166,9 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     *vmask = (uint32_t)(ballot(valid) & 0xFFFFFFFFull);
     return valid ? idx : 0;
   };
-
-  Gather<NRW> ga, gb;  // ga: block j+2 (in flight), gb: block j+1
-  uint32_t vm_a = 0, vm_b = 0, vm_c = 0;
-  int ix2 = raw_index(2), ix3 = raw_index(3);
-  gather(ga, resolve(raw_index(0), &vm_c));
-  gather(gb, resolve(raw_index(1), &vm_b));
-  stage(ga, 0);
-  __syncthreads();
-
-  // V^T operand rows for this lane: key 16kk + 8t + 4(l/32) + (l%16)/4 at
-  // column 64db + 32((l/16)%2) + 8(l%4) bytes (t selects operand half)
-  const int vt_lane = (4 * (lane >> 5) + ((lane & 15) >> 2)) * BL::SV + 32 * ((lane >> 4) & 1) +
-                      8 * (lane & 3);
-
-  // One 32-key block. g_far receives block j+2, g_next (block j+1) is staged
-  // at the end; the loop alternates the two register sets.
-  auto block = [&](int j, Gather<NRW>& g_far, Gather<NRW>& g_next) {
-    // issued unconditionally (blocks past the end gather row 0, masked out):
-    // a conditional load here would make the compiler drain every
-    // outstanding load before the staging below, removing the prefetch
-    gather(g_far, resolve(ix2, &vm_a));
-    ix2 = ix3;
-    ix3 = raw_index(j + 4);
-    const uint8_t* kl = base + (j & 1) * BL::BYTES;
-    const uint8_t* vl = kl + BL::KB;
-
-    // ---- S^T = K . Q^T for this wave's 32 heads
+  // S^T = K . Q^T for this wave's 32 heads, K rows of LDS buffer b
+  auto qk = [&](int b) {
+    const uint8_t* kl = kbuf(b);
     f32x16 s = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -191,16 +176,65 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
                                                          (ks * 2 + (lane >> 5)) * 16);
       s = mfma32(ka, qb[ks], s);
     }
-    // ---- online softmax in the exp2 domain with a lazily moved maximum. The
-    // scale (> 0) commutes with the maximum, so the raw scores' maximum is
-    // scaled once and each exponent is one fma, s * sl2 - m.
+    return s;
+  };
+
+  // V^T operand rows for this lane: key 16kk + 8t + 4(l/32) + (l%16)/4 at
+  // column 64db + 32((l/16)%2) + 8(l%4) bytes (t selects operand half)
+  const int vt_lane = (4 * (lane >> 5) + ((lane & 15) >> 2)) * BL::SV + 32 * ((lane >> 4) & 1) +
+                      8 * (lane & 3);
+
+  // Pipeline. K runs one block ahead of V: at the start of iteration j the K
+  // rows of block j+1 and the V rows of block j are in LDS, and S(j) is
+  // already computed. Iteration j issues the gathers of K(j+3) and V(j+2),
+  // computes S(j+1) (MFMAs independent of block j's softmax), finishes block
+  // j (softmax, O^T += V^T . P^T), then stages K(j+2) over K(j) and V(j+1)
+  // over V(j-1), both last read before the previous barrier. In flight in
+  // registers: K(j+2), K(j+3), V(j+1), V(j+2).
+  uint32_t vm0 = 0, vm1 = 0, vm2 = 0, vm3 = 0;  // masks of blocks j .. j+3
+  Rows ka_, kb_, va_, vb_;  // alternate register sets: (kb_, vb_) near, (ka_, va_) far
+  Off off_prev;             // row offsets of the block whose K was issued last
+  {
+    const Off o0 = offsets(resolve(raw_index(0), &vm0));
+    const Off o1 = offsets(resolve(raw_index(1), &vm1));
+    off_prev = offsets(resolve(raw_index(2), &vm2));
+    gather(kb8, o0, ka_);
+    gather(vb8, o0, va_);
+    gather(kb8, o1, kb_);
+    gather(vb8, o1, vb_);
+    stage_k(ka_, 0);
+    stage_v(va_, 0);
+    stage_k(kb_, 1);
+    gather(kb8, off_prev, kb_);  // K(2) in flight; vb_ holds V(1)
+  }
+  int ix3 = raw_index(3), ix4 = raw_index(4);
+  __syncthreads();
+  f32x16 s_cur = qk(0);
+
+  auto iteration = [&](int j, Rows& k_far, Rows& v_far, Rows& k_near, Rows& v_near) {
+    // issued unconditionally (blocks past the end gather row 0, masked out):
+    // a conditional load here would make the compiler drain every
+    // outstanding load before the staging below
+    const Off on = offsets(resolve(ix3, &vm3));
+    ix3 = ix4;
+    ix4 = raw_index(j + 5);
+    gather(kb8, on, k_far);        // K(j+3)
+    gather(vb8, off_prev, v_far);  // V(j+2)
+    off_prev = on;
+    const f32x16 s_nxt = qk(j + 1);  // past the last block: masked rows
+
+    // ---- online softmax of block j in the exp2 domain with a lazily moved
+    // maximum. The scale (> 0) commutes with the maximum, so the raw scores'
+    // maximum is scaled once and each exponent is one fma, s * sl2 - m.
     float x[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = s[i];
-    if (__builtin_expect(vm_c != 0xFFFFFFFFu, 0)) {  // wave-uniform: padded entries
+    for (int i = 0; i < 16; ++i) x[i] = s_cur[i];
+    if (__builtin_expect(vm0 != 0xFFFFFFFFu, 0)) {  // wave-uniform: padded entries
+      // key of x[i] = acc_row(i, lane) = 4(l/32) + 8(i/4) + i%4
+      const uint32_t vml = vm0 >> (4 * (lane >> 5));
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (!((vm_c >> acc_row(i, lane)) & 1u)) x[i] = -INFINITY;
+        if (!((vml >> (8 * (i >> 2) + (i & 3))) & 1u)) x[i] = -INFINITY;
     }
     float mloc = -INFINITY;
 #pragma unroll
@@ -215,13 +249,12 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
       m_used = mnew;
     }
-    // x * sl2 - m_used <= 8 keeps P <= 256; -inf maps to 0
+    // x * sl2 - m_used <= 8 keeps P <= 256; -inf maps to 0. The row sum
+    // accumulates the bf16-rounded weights that the P.V product uses
+    // (two-way dot products with 1), in two chains.
     const float mu = (m_used == -INFINITY) ? 0.0f : m_used;
-    // The row sum accumulates the bf16-rounded weights that the P.V product
-    // uses (two-way dot products with 1), in two chains.
     u32x4 pw[2];
     float psum0 = 0.0f, psum1 = 0.0f;
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
@@ -235,6 +268,7 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     lsum += psum0 + psum1;
     // ---- O^T += V^T . P^T; P^T's k index 8(l/32) + jj is key
     // 16kk + 8(jj/4) + 4(l/32) + jj%4, which the transposed reads match
+    const uint8_t* vl = vbuf(j);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kk]);
@@ -247,16 +281,19 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
         o[db] = mfma32(va, pb, o[db]);
       }
     }
-    // ---- stage block j+1 into the other buffer (nobody has read it since
-    // the barrier that ended block j-1)
-    stage(g_next, (j + 1) & 1);  // past the last block: a buffer nobody reads
-    vm_c = vm_b;
-    vm_b = vm_a;
+    // ---- stage K(j+2) over K(j) and V(j+1) over V(j-1) (past the last
+    // block: buffers nobody reads)
+    stage_k(k_near, j);
+    stage_v(v_near, j + 1);
+    vm0 = vm1;
+    vm1 = vm2;
+    vm2 = vm3;
+    s_cur = s_nxt;
     __syncthreads();
   };
   for (int j = 0; j < nblk; j += 2) {
-    block(j, ga, gb);
-    if (j + 1 < nblk) block(j + 1, gb, ga);
+    iteration(j, ka_, va_, kb_, vb_);
+    if (j + 1 < nblk) iteration(j + 1, kb_, vb_, ka_, va_);
   }
 
   if (!active || h >= H) return;
