@@ -10,9 +10,9 @@ closed forms, brute force or library special cases; none is "parity unpinned".
 from .indexcache import (PAD, validate_pattern, nearest_full, indexer_scores,
                          topk_row, topk, sparse_attention, schedule, layer_stack,
                          overlap, jaccard, mean_overlap, greedy_pattern, position_order,
-                         overlap_matrix, overlap_proxy_loss)
+                         overlap_matrix, overlap_proxy_loss, distill_loss, row_position)
 
 __all__ = ["PAD", "validate_pattern", "nearest_full", "indexer_scores", "topk_row",
            "topk", "sparse_attention", "schedule", "layer_stack", "overlap",
            "jaccard", "mean_overlap", "greedy_pattern", "position_order",
-           "overlap_matrix", "overlap_proxy_loss"]
+           "overlap_matrix", "overlap_proxy_loss", "distill_loss", "row_position"]

@@ -318,6 +318,45 @@ def overlap_proxy_loss(pattern: str, matrix: np.ndarray) -> float:
 
 
 # --------------------------------------------------------------------------- #
+# Multi-layer distillation loss ([J] "方法二：Training-Aware IndexCache":
+# L_multi = sum_j 1/(m+1) sum_t KL(p_t^(l+j) || q_t^(l)), q = Softmax(I_t);
+# Proposition 1: its gradient equals that of KL against the mean teacher)
+# --------------------------------------------------------------------------- #
+def distill_loss(logits: np.ndarray, teachers: np.ndarray, q_pos0: int,
+                 q_pos: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-row multi-teacher KL and its gradient with respect to the logits.
+
+    logits [B,Lq,Lk] are the indexer scores I_t of row (b,i) over keys
+    0..t (t from row_position; entries past t are ignored); teachers
+    [n,B,Lq,Lk] are n distributions over the same keys (entries past t
+    ignored). Returns (loss [B,Lq] = (1/n) sum_j sum_s p_j log(p_j / q),
+    grad [B,Lq,Lk] = dloss/dlogits = q - mean_j p_j on 0..t, 0 beyond), fp64,
+    with 0 log 0 = 0 and q = softmax over 0..t.
+    """
+    I = np.asarray(logits, dtype=np.float64)
+    P = np.asarray(teachers, dtype=np.float64)
+    n = P.shape[0]
+    B, Lq, Lk = I.shape
+    loss = np.zeros((B, Lq))
+    grad = np.zeros((B, Lq, Lk))
+    for b in range(B):
+        for i in range(Lq):
+            t = row_position(b, i, q_pos0, q_pos, Lk)
+            if t < 0:
+                continue
+            x = I[b, i, : t + 1]
+            logq = x - (x.max() + np.log(np.exp(x - x.max()).sum()))
+            total = 0.0
+            for j in range(n):
+                p = P[j, b, i, : t + 1]
+                nz = p > 0
+                total += float(np.sum(p[nz] * (np.log(p[nz]) - logq[nz])))
+            loss[b, i] = total / n
+            grad[b, i, : t + 1] = np.exp(logq) - P[:, b, i, : t + 1].mean(axis=0)
+    return loss, grad
+
+
+# --------------------------------------------------------------------------- #
 # Greedy layer selection with an injectable loss ([W] "Training-free：直接用语言
 # 模型损失选择 Full 层"; [J] "核心算法：Greedy Layer Selection", Algorithm 1)
 # --------------------------------------------------------------------------- #
