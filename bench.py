@@ -286,6 +286,41 @@ def context_sweep():
     return out
 
 
+def distill_rate(Lq=2048, Lk=32768, n_teachers=4, seed=0):
+    """idxc_distill_loss on one query chunk (the last Lq rows of an Lk-token
+    context) against n_teachers teachers (an F layer and the S layers it
+    serves under the 12-F pattern); algorithmic bytes = per causal (row, key)
+    pair one logit read, n_teachers teacher reads and one gradient write."""
+    import torch
+    import dsa_lightning_indexer_score_amd as idxc
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    q_pos0 = Lk - Lq
+    logits = torch.randn((1, Lq, Lk), generator=g, device="cuda")
+    teachers = torch.rand((n_teachers, 1, Lq, Lk), generator=g, device="cuda")
+    teachers /= teachers.sum(-1, keepdim=True)  # synthetic distributions (full rows)
+    loss = torch.empty((1, Lq), device="cuda")
+    grad = torch.empty_like(logits)
+    d = idxc.make_dims(1, Lq, Lk, q_pos0)
+    lib = idxc._lib.load()
+    import ctypes
+
+    def call():
+        idxc._lib.check(lib.idxc_distill_loss(ctypes.c_void_p(logits.data_ptr()),
+                                              ctypes.c_void_p(teachers.data_ptr()), n_teachers,
+                                              ctypes.byref(d), ctypes.c_void_p(loss.data_ptr()),
+                                              ctypes.c_void_p(grad.data_ptr()),
+                                              idxc._stream(None)))
+    ms = events_ms(call, 5)
+    pairs = causal_pairs(q_pos0, Lq)
+    nbytes = pairs * 4 * (2 + n_teachers)
+    del logits, teachers, grad
+    torch.cuda.empty_cache()
+    return {"Lq": Lq, "Lk": Lk, "n_teachers": n_teachers, "ms": ms,
+            "algorithmic_bytes": nbytes, "GBs": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
 def standalone_topk(B, Lq, Lk, q_pos0, k, seed=0):
     """idxc_topk on materialised fp32 scores; algorithmic bytes = valid scores
     read (4 B each) + indices written (4 B each)."""
@@ -498,7 +533,8 @@ def main():
         pmc_launches()
         return
     if args.only == "sweep":
-        print(json.dumps({"context_sweep": context_sweep()}), flush=True)
+        print(json.dumps({"context_sweep": context_sweep(), "distill_loss": distill_rate()}),
+              flush=True)
         return
 
     res = {}
@@ -589,6 +625,10 @@ def main():
         torch.cuda.empty_cache()
         extra["context_sweep"] = context_sweep()
         torch.cuda.empty_cache()
+        dl = distill_rate()
+        log("distillation loss (4 teachers, 2048 x 32768 chunk): %.3f ms, %.0f GB/s"
+            % (dl["ms"], dl["GBs"]))
+        extra["distill_loss"] = dl
         tk = {"decode_rows": standalone_topk(64, 1, 65536, 65535, 2048),
               "prefill_rows": standalone_topk(1, 8192, 8192, 0, 2048)}
         log("standalone top-k: %.0f GB/s (64 x 65536), %.0f GB/s (8192 x 8192 causal)"

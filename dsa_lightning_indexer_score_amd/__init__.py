@@ -18,7 +18,8 @@ __all__ = ["idxc_version", "idxc_validate_pattern", "idxc_schedule", "idxc_index
            "idxc_topk", "idxc_topk_workspace_bytes", "idxc_workspace_bytes", "idxc_indexer_topk", "idxc_sparse_attn", "idxc_sparse_attn_workspace_bytes", "idxc_overlap",
            "idxc_layer_stack_forward", "idxc_overlap_matrix", "idxc_greedy_pattern",
            "idxc_overlap_proxy_loss", "idxc_indexer_topk_ragged",
-           "idxc_layer_stack_forward_ragged", "make_dims", "IdxcError", "StackCall"]
+           "idxc_layer_stack_forward_ragged", "idxc_distill_loss", "make_dims", "IdxcError",
+           "StackCall"]
 
 
 def _stream(stream=None) -> ctypes.c_void_p:
@@ -326,6 +327,24 @@ def idxc_overlap_proxy_loss(pattern: str, matrix) -> float:
                                            m.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
                                            ctypes.byref(out)))
     return float(out.value)
+
+
+def idxc_distill_loss(logits, teachers, q_pos0: int = 0, grad: bool = True, stream=None):
+    """Multi-teacher distillation loss per query row and its gradient with
+    respect to the logits. logits fp32 [B, Lq, Lk]; teachers fp32 [n, B, Lq,
+    Lk]. Returns (row_loss [B, Lq], grad [B, Lq, Lk] or None)."""
+    lib = _lib.load()
+    if logits.dim() != 3 or teachers.dim() != 4 or teachers.shape[1:] != logits.shape:
+        raise ValueError("logits [B, Lq, Lk] and teachers [n, B, Lq, Lk] expected")
+    B, Lq, Lk = logits.shape
+    d = make_dims(B, Lq, Lk, q_pos0)
+    loss = torch.empty((B, Lq), dtype=torch.float32, device=logits.device)
+    g = torch.empty_like(logits) if grad else None
+    _lib.check(lib.idxc_distill_loss(_ptr(logits, "logits", torch.float32),
+                                     _ptr(teachers, "teachers", torch.float32),
+                                     teachers.shape[0], ctypes.byref(d), _ptr(loss, "row_loss"),
+                                     _ptr(g, "grad"), _stream(stream)))
+    return loss, g
 
 
 class StackCall:

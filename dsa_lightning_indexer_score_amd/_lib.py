@@ -34,7 +34,7 @@ EXPORTED = (
     "idxc_indexer_topk", "idxc_sparse_attn", "idxc_sparse_attn_workspace_bytes",
     "idxc_layer_stack_forward", "idxc_overlap", "idxc_overlap_matrix_workspace_bytes",
     "idxc_overlap_matrix", "idxc_greedy_pattern", "idxc_overlap_proxy_loss",
-    "idxc_indexer_topk_ragged", "idxc_layer_stack_forward_ragged",
+    "idxc_indexer_topk_ragged", "idxc_layer_stack_forward_ragged", "idxc_distill_loss",
 )
 
 # double loss(const char* pattern, void* user)
@@ -95,6 +95,7 @@ def load() -> ctypes.CDLL:
                                              ctypes.c_float, vp, vp, sz, P(i32), vp, vp],
                                             ctypes.c_int),
         "idxc_overlap_matrix_workspace_bytes": ([i32], sz),
+        "idxc_distill_loss": ([vp, vp, i32, P(IdxcDims), vp, vp, vp], ctypes.c_int),
         "idxc_overlap_matrix": ([vp, i32, P(IdxcDims), vp, sz, vp, vp], ctypes.c_int),
         "idxc_greedy_pattern": ([i32, i32, LOSS_FN, vp, ctypes.c_char_p, P(ctypes.c_int64)],
                                 ctypes.c_int),

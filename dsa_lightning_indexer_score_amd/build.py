@@ -12,7 +12,7 @@ import sys
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libidxc.so")
-SOURCES = ["api.hip", "indexer.hip", "topk.hip", "attn.hip", "overlap.hip"]
+SOURCES = ["api.hip", "indexer.hip", "topk.hip", "attn.hip", "overlap.hip", "distill.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 instructions are disabled for every HIP file (see the header of

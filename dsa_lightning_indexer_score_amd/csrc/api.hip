@@ -57,6 +57,7 @@ constexpr int kMaxLk = 1 << 24;
 // bit 2 = k.
 constexpr int kMaxOverlapLk = 262144;  // two LDS bitmaps of Lk bits (64 KB)
 constexpr int kMaxMatrixLayers = 64;   // n*n 64-bit LDS accumulators (32 KB)
+constexpr int kMaxTeachers = 64;       // layers one indexer serves
 
 int check_dims(const idxc_dims* d, int need) {
   if (d == nullptr) return fail(IDXC_ERR_INVALID_ARG, "dims is NULL");
@@ -499,6 +500,26 @@ int idxc_overlap_matrix(const int32_t* sel, int32_t n_layers, const idxc_dims* d
                                           static_cast<unsigned long long*>(workspace), matrix,
                                           static_cast<hipStream_t>(hip_stream)),
                     "overlap matrix launch");
+}
+
+int idxc_distill_loss(const float* logits, const float* teachers, int32_t n_teachers,
+                      const idxc_dims* dims, float* row_loss, float* grad, void* hip_stream) {
+  int r = check_dims(dims, 0);
+  if (r != IDXC_OK) return r;
+  if (n_teachers < 1) return fail(IDXC_ERR_INVALID_ARG, "n_teachers must be >= 1");
+  if (n_teachers > kMaxTeachers)
+    return fail(IDXC_ERR_UNSUPPORTED, "n_teachers = %d above %d", n_teachers, kMaxTeachers);
+  REQUIRE_PTR(logits, "logits");
+  REQUIRE_PTR(teachers, "teachers");
+  if (row_loss != nullptr && !aligned16(row_loss))
+    return fail(IDXC_ERR_INVALID_ARG, "row_loss is not 16-byte aligned");
+  if (grad != nullptr && !aligned16(grad))
+    return fail(IDXC_ERR_INVALID_ARG, "grad is not 16-byte aligned");
+  if (row_loss == nullptr && grad == nullptr) return ok();
+  return hip_status(launch_distill(logits, teachers, n_teachers, dims->B, dims->Lq, dims->Lk,
+                                   dims->q_pos0, row_loss, grad,
+                                   static_cast<hipStream_t>(hip_stream)),
+                    "distill launch");
 }
 
 int idxc_overlap_proxy_loss(const char* pattern, int32_t n_layers, const float* matrix,

@@ -90,6 +90,14 @@ size_t attn_workspace_bytes(int B, int Lq, int H, int D, int k);
 size_t overlap_lds_bytes(int Lk);
 hipError_t launch_overlap(const int32_t* a, const int32_t* b, int rows, int k, int Lk,
                           int32_t* inter, float* overlap, float* jaccard, hipStream_t st);
+// Multi-teacher distillation loss: per row (b, i), keys 0..q_pos0+i of
+// logits [B,Lq,Lk] and of n_teachers distributions [n][B,Lq,Lk]; row_loss
+// [B*Lq] and grad [B,Lq,Lk] (q - mean teacher, 0 past the row's keys) may be
+// null.
+hipError_t launch_distill(const float* logits, const float* teachers, int n_teachers, int B,
+                          int Lq, int Lk, int q_pos0, float* row_loss, float* grad,
+                          hipStream_t st);
+
 // Overlap matrix of n index tensors sel[n][rows][k] (matrix[a*n+b] = mean over
 // rows of overlap(sel[a], sel[b])); acc is a device workspace of n*n uint64.
 size_t overlap_matrix_lds_bytes(int n, int Lk);

@@ -215,6 +215,24 @@ int idxc_layer_stack_forward_ragged(const char* pattern, int32_t n_layers,
                                     int32_t* indexer_calls, int32_t* debug_indices,
                                     void* hip_stream);
 
+/* Multi-layer distillation loss of an index-sharing layer group ("NLP——
+ * IndexCache" notes, section "方法二：Training-Aware IndexCache": the F layer's
+ * indexer fits the attention distributions of every layer it serves;
+ * Proposition 1 there: the gradient equals that of one KL against the mean
+ * teacher). For query row r = (b, i) at t = q_pos0 + i, over keys 0..t:
+ *   q = Softmax(logits[b,i,0..t]),
+ *   row_loss[r] = (1/n) sum_j sum_s p_j[s] log(p_j[s] / q[s])   (0 log 0 = 0),
+ *   grad[b,i,s] = q[s] - (1/n) sum_j p_j[s] for s <= t, 0 for s > t,
+ * with p_j = teachers[j, b, i, :] (n = n_teachers distributions, each summing
+ * to 1 over 0..t; entries past t are not read) and grad = d row_loss /
+ * d logits. logits [B,Lq,Lk] fp32 (e.g. idxc_indexer_scores' output),
+ * teachers [n_teachers,B,Lq,Lk] fp32, row_loss [B*Lq] fp32 and grad
+ * [B,Lq,Lk] fp32, all DEVICE; row_loss or grad may be NULL. Uses B, Lq, Lk,
+ * q_pos0. 1 <= n_teachers <= 64. fp32 arithmetic, deterministic.
+ * Asynchronous on hip_stream. */
+int idxc_distill_loss(const float* logits, const float* teachers, int32_t n_teachers,
+                      const idxc_dims* dims, float* row_loss, float* grad, void* hip_stream);
+
 /* Cross-layer agreement of two index tensors a, b [B,Lq,k] int32 (DEVICE;
  * entries are positions in [0, Lk) or -1, in any order; other values are
  * ignored). Per row, over the valid entries taken as sets: inter = |A ∩ B|,

@@ -286,3 +286,17 @@ def test_ragged_argument_errors(lib):
              None) == _lib.IDXC_ERR_INVALID_ARG
     assert g(b"S", 1, layer, d, P(), 1.0, P(), P(), 1 << 30, ctypes.byref(calls), None,
              None) == _lib.IDXC_ERR_PATTERN
+
+
+def test_distill_argument_errors(lib):
+    f = lib.idxc_distill_loss
+    d = ctypes.byref(_dims(Lq=8, Lk=64))
+    assert f(P(), P(), 0, d, P(), P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), P(), 65, d, P(), P(), None) == _lib.IDXC_ERR_UNSUPPORTED
+    assert f(None, P(), 2, d, P(), P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), None, 2, d, P(), P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), P(), 2, d, P(FAKE + 4), P(), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), P(), 2, d, P(), P(FAKE + 8), None) == _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), P(), 2, ctypes.byref(_dims(Lq=8, Lk=4)), P(), P(), None) == \
+        _lib.IDXC_ERR_INVALID_ARG
+    assert f(P(), P(), 2, d, None, None, None) == _lib.IDXC_OK   # nothing requested: no launch

@@ -485,6 +485,50 @@ def test_ragged_decode_stack_matches_oracle():
 
 
 # --------------------------------------------------------------------------- #
+# multi-layer distillation loss (training-aware IndexCache)
+# --------------------------------------------------------------------------- #
+def _teachers(n, B, Lq, Lk, q_pos0, seed):
+    g = torch.Generator().manual_seed(seed)
+    tl = torch.randn((n, B, Lq, Lk), generator=g, dtype=torch.float64) * 1.5
+    cols = torch.arange(Lk).view(1, 1, 1, Lk)
+    t = (q_pos0 + torch.arange(Lq)).view(1, 1, Lq, 1)
+    tl = tl.masked_fill(cols > t, -math.inf)
+    P = torch.softmax(tl, dim=-1)
+    P[0, 0, -1, 0] = 0.0                # a zero teacher entry (the last row has the most keys)
+    P[0, 0, -1] /= P[0, 0, -1].sum()
+    return P.float()
+
+
+@pytest.mark.parametrize("n,B,Lq,Lk,q_pos0", [(4, 2, 50, 300, 250), (1, 1, 64, 64, 0),
+                                             (2, 1, 3, 5000, 4997), (3, 2, 7, 257, 250)])
+def test_distill_loss_matches_oracle(n, B, Lq, Lk, q_pos0):
+    g = torch.Generator().manual_seed(n * 100 + Lq)
+    logits = (torch.randn((B, Lq, Lk), generator=g) * 3.0).float()
+    # entries past each row's keys hold -inf, as idxc_indexer_scores writes them
+    cols = torch.arange(Lk).view(1, 1, Lk)
+    logits = logits.masked_fill(cols > (q_pos0 + torch.arange(Lq)).view(1, Lq, 1), -math.inf)
+    P = _teachers(n, B, Lq, Lk, q_pos0, seed=n + Lk)
+    _say("distill n=%d B=%d Lq=%d Lk=%d" % (n, B, Lq, Lk))
+    loss, grad = idxc.idxc_distill_loss(cu(logits), cu(P), q_pos0)
+    torch.cuda.synchronize()
+    wl, wg = oracle.distill_loss(logits.double().numpy(), P.double().numpy(), q_pos0)
+    assert np.allclose(loss.cpu().numpy(), wl, rtol=1e-4, atol=1e-4)
+    assert np.abs(grad.cpu().numpy() - wg).max() <= 2e-6
+
+
+def test_distill_loss_zero_when_teachers_equal_student():
+    B, Lq, Lk = 1, 40, 40
+    g = torch.Generator().manual_seed(9)
+    logits = torch.randn((B, Lq, Lk), generator=g).float()
+    cols = torch.arange(Lk).view(1, 1, Lk)
+    masked = logits.masked_fill(cols > torch.arange(Lq).view(1, Lq, 1), -math.inf)
+    P = torch.softmax(masked.double(), -1).float().unsqueeze(0).repeat(3, 1, 1, 1)
+    loss, grad = idxc.idxc_distill_loss(cu(logits), cu(P), 0)   # finite junk past t is not read
+    torch.cuda.synchronize()
+    assert loss.abs().max().item() < 1e-5 and grad.abs().max().item() < 1e-6
+
+
+# --------------------------------------------------------------------------- #
 # cross-layer agreement of index sets
 # --------------------------------------------------------------------------- #
 def _set_stats(a, b):
