@@ -113,11 +113,11 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // must still take one more 64-key tile.
 int min_cap(int k) { return (k + 64 + 63) / 64 * 64; }
 
-// Default candidate capacity: room for the ~2k keys a sampled threshold lets
-// through, with a margin of several standard deviations; also the number of
-// candidates the selection kernel stages per row.
+// Default candidate capacity: room for the ~1.5k keys a sampled threshold
+// lets through, with a margin of several standard deviations; also the number
+// of candidates the selection kernel stages per row.
 int default_cap(int k) {
-  int cap = 3 * k;
+  int cap = 5 * k / 2;
   if (cap < k + 64) cap = k + 64;
   if (cap < 1024) cap = 1024;
   if (cap > kMaxStagePairs) cap = kMaxStagePairs;

@@ -183,7 +183,7 @@ __device__ void wave_compact(u32x2* __restrict__ buf, int& n, int k, uint32_t& t
 // ---------------------------------------------------------------------------
 constexpr int kSampleTiles = 16;  // at most
 constexpr int kSampleKeys = kSampleTiles * kKeyTile;
-constexpr float kSampleSlack = 2.0f;
+constexpr float kSampleSlack = 1.5f;
 // expected sampled keys at or above the threshold; the threshold's rank in the
 // row then has a relative spread of about 1/sqrt(kSampleHits)
 constexpr float kSampleHits = 100.0f;
