@@ -113,11 +113,13 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // must still take one more 64-key tile.
 int min_cap(int k) { return (k + 64 + 63) / 64 * 64; }
 
-// Default candidate capacity: room for the ~1.5k keys a sampled threshold
-// lets through, with a margin of several standard deviations; also the number
-// of candidates the selection kernel stages per row.
-int default_cap(int k) {
-  int cap = 5 * k / 2;
+// Default candidate capacity: room for the 1.5k-1.75k keys a sampled
+// threshold lets through (2.25k on rows long enough to use the larger slack,
+// which only key ranges beyond 60000 have), with a margin of several standard
+// deviations; also the number of candidates the selection kernel stages per
+// row.
+int default_cap(int k, int Lk) {
+  int cap = Lk > 60000 ? 7 * k / 2 : 5 * k / 2;
   if (cap < k + 64) cap = k + 64;
   if (cap < 1024) cap = 1024;
   if (cap > kMaxStagePairs) cap = kMaxStagePairs;
@@ -153,7 +155,7 @@ Plan plan_for(const idxc_dims* d, bool with_attn = false) {
     p.bytes = split_part_bytes(d);
     p.min_bytes = p.bytes;
   } else {
-    p.bytes = align_up(rows * 4) + rows * (size_t)default_cap(d->k) * 8;
+    p.bytes = align_up(rows * 4) + rows * (size_t)default_cap(d->k, d->Lk) * 8;
     p.min_bytes = align_up(rows * 4) + rows * (size_t)min_cap(d->k) * 8;
   }
   if (with_attn) {
@@ -172,7 +174,7 @@ int cap_for(const idxc_dims* d, size_t ws_bytes) {
   if (ws_bytes < head) return 0;
   size_t cap = (ws_bytes - head) / (rows * 8);
   cap = cap / 64 * 64;
-  const size_t dc = (size_t)default_cap(d->k);
+  const size_t dc = (size_t)default_cap(d->k, d->Lk);
   if (cap > dc) cap = dc;
   return (int)cap;
 }

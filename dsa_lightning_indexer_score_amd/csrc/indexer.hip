@@ -167,11 +167,11 @@ __device__ void wave_compact(u32x2* __restrict__ buf, int& n, int k, uint32_t& t
 //
 // MODE 1 threshold. Rows longer than the candidate capacity first score a
 // stratified sample of their keys: up to 16 tiles of 128 consecutive keys
-// spread evenly over [0, t_first] (t_first = the workgroup's first row), run
+// spread evenly over [0, t_first] (t_first = the workgroup's least position), run
 // through the same pipeline before the key sweep; the tile count grows with
 // the row length so that about kSampleHits sampled keys land above the
 // threshold. A row's threshold is the m-th largest sampled order key, m
-// chosen so that about kSampleSlack * k keys of the row are expected at or
+// chosen so that about slack * k keys of the row are expected at or
 // above it. The threshold is only a filter:
 //  * if the buffer still overflows, it is compacted to the exact k best seen
 //    so far (wave_compact) and the threshold rises to the k-th of them;
@@ -183,7 +183,18 @@ __device__ void wave_compact(u32x2* __restrict__ buf, int& n, int k, uint32_t& t
 // ---------------------------------------------------------------------------
 constexpr int kSampleTiles = 16;  // at most
 constexpr int kSampleKeys = kSampleTiles * kKeyTile;
-constexpr float kSampleSlack = 1.5f;
+// The survivor count of a threshold set at about kSampleHits sampled hits has
+// a relative spread of about 1/sqrt(kSampleHits) = 10%: a row falls short of k
+// (and its workgroup sweeps again) beyond (1 - 1/slack) / 0.1 standard
+// deviations. A sweep again delays a launch by up to one workgroup's time, so
+// launches of many workgroups take slack 1.5 (3.3 sigma, cheaper selection)
+// and smaller ones 1.75 (4.3 sigma); the host passes it in.
+constexpr float kSampleSlackMany = 1.5f;
+constexpr float kSampleSlackFew = 1.75f;
+constexpr int kSlackManyRows = 16384;  // query rows per launch for the smaller slack
+// Rows so long that the sample reaches kSampleTiles first get fewer sampled
+// hits (about 48 at 196K keys with this slack: 3.9 sigma).
+constexpr float kSampleSlackCapped = 2.25f;
 // expected sampled keys at or above the threshold; the threshold's rank in the
 // row then has a relative spread of about 1/sqrt(kSampleHits)
 constexpr float kSampleHits = 100.0f;
@@ -195,7 +206,8 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
                          const uint16_t* __restrict__ w, int B, int Lq, int Lk,
                          int q_pos0, int H_I, float* __restrict__ scores,
                          u32x2* __restrict__ cand, int* __restrict__ cand_count,
-                         int cap, int k, const int32_t* __restrict__ q_pos) {
+                         int cap, int k, const int32_t* __restrict__ q_pos,
+                         float slack_rows) {
   constexpr int NCH = DI / 8;            // 16-byte chunks per key row
   constexpr int KS = DI / 16;            // MFMA k-steps over d_I
   constexpr int TILE_CHUNKS = kKeyTile * NCH;
@@ -367,8 +379,10 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
   bool compute_row = active && t >= 0;
   for (int pass = 0; pass < (MODE == 1 ? 2 : 1); ++pass) {
     int nsamp = 0;
+    float slack = slack_rows;
     if (MODE == 1 && pass == 0 && t_first + 1 > cap) {
-      const float tiles = kSampleHits * (float)(t_first + 1) / (kSampleSlack * (float)k * kKeyTile);
+      const float tiles = kSampleHits * (float)(t_first + 1) / (slack_rows * (float)k * kKeyTile);
+      if (tiles > (float)kSampleTiles) slack = kSampleSlackCapped;
       nsamp = max(2, min(kSampleTiles, (int)ceilf(tiles)));
     }
     const int nv = nsamp + ntiles;
@@ -387,7 +401,7 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
       if (MODE == 1 && v == nsamp && nsamp > 0 && compute_row) {
         // threshold = m-th largest sampled order key (binary search on bits)
         const int nkeys = nsamp * kKeyTile;
-        const float want = kSampleSlack * (float)k * (float)nkeys / (float)(t + 1);
+        const float want = slack * (float)k * (float)nkeys / (float)(t + 1);
         const int m = max(1, min(nkeys, (int)ceilf(want)));
         uint32_t T = 0u;
         for (int bit = 31; bit >= 0; --bit) {
@@ -691,11 +705,12 @@ hipError_t launch_rows(const IndexerArgs& a, int mode, hipStream_t st) {
   if (mode == 0) {
     hipLaunchKernelGGL((indexer_rows_kernel<DI, HB, 0>), grid, block, 0, st, a.q_idx, a.k_idx,
                        a.w, a.B, a.Lq, a.Lk, a.q_pos0, a.H_I, a.scores, nullptr, nullptr, 0,
-                       a.k, nullptr);
+                       a.k, nullptr, kSampleSlackMany);
   } else {
     hipLaunchKernelGGL((indexer_rows_kernel<DI, HB, 1>), grid, block, 0, st, a.q_idx, a.k_idx,
                        a.w, a.B, a.Lq, a.Lk, a.q_pos0, a.H_I, nullptr, a.cand, a.cand_count,
-                       a.cap, a.k, a.q_pos);
+                       a.cap, a.k, a.q_pos,
+                       a.B * a.Lq >= kSlackManyRows ? kSampleSlackMany : kSampleSlackFew);
   }
   return hipGetLastError();
 }
