@@ -79,7 +79,14 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   const int ul = wave / HB;  // unit slot in this workgroup
   const int hb = wave % HB;
   const int rows = B * Lq;
-  const int unit = blockIdx.x * UPW + ul;
+  // Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD
+  // b % 8); renumber them so that each XCD takes a contiguous range of rows
+  // and its L2 sees the index lists of neighbouring rows (a bijection:
+  // XCD x holds counts nwg/8 (+1 for x < nwg % 8)).
+  const int nwg = (int)gridDim.x;
+  const int xcd = (int)(blockIdx.x % 8);
+  const int wg = xcd * (nwg / 8) + min(xcd, nwg % 8) + (int)(blockIdx.x / 8);
+  const int unit = wg * UPW + ul;
   const int rowq = unit / nsplit;
   const int split = unit % nsplit;
   const bool active = rowq < rows;
