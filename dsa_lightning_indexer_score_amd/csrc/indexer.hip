@@ -579,17 +579,19 @@ void indexer_split_kernel(const uint16_t* __restrict__ q_idx,
 
 // ---------------------------------------------------------------------------
 // Split-key kernel with chunk-local top-k (few query rows, e.g. decode): a
-// workgroup owns one query row and an 8192-key chunk (2048 keys per wave,
-// three 32-key blocks in flight per wave), keeps the chunk's order keys in
-// LDS and writes the chunk's exact top-k, in position order, as one
+// workgroup of 8 waves owns one query row and a 16384-key chunk (2048 keys
+// per wave, three 32-key blocks in flight per wave), keeps the chunk's order
+// keys in LDS and writes the chunk's exact top-k, in position order, as one
 // candidate segment; a selection launch over the row's segments finishes the
-// row. Every key of the row's top-k is in its chunk's top-k.
+// row. Every key of the row's top-k is in its chunk's top-k. (16384-key
+// chunks halve the segments the final selection stages, against 8192.)
 // ---------------------------------------------------------------------------
-constexpr int kDecChunk = 8192;
-constexpr int kDecKeysPerWave = kDecChunk / kSplitWaves;
+constexpr int kDecChunk = 16384;
+constexpr int kDecWaves = 8;
+constexpr int kDecKeysPerWave = kDecChunk / kDecWaves;
 
 template <int DI, int HB>
-__global__ __launch_bounds__(kSplitWaves * kWave, 2)
+__global__ __launch_bounds__(kDecWaves * kWave, 2)
 void indexer_split_topk_kernel(const uint16_t* __restrict__ q_idx,
                                const uint16_t* __restrict__ k_idx,
                                const uint16_t* __restrict__ w, int B, int Lq, int Lk,
@@ -598,7 +600,7 @@ void indexer_split_topk_kernel(const uint16_t* __restrict__ q_idx,
                                const int32_t* __restrict__ q_pos) {
   constexpr int KS = DI / 16;
   __shared__ __attribute__((aligned(16))) uint32_t skey[kDecChunk];
-  __shared__ SelectSmem sel;
+  __shared__ SelectSmemT<kDecWaves * kWave> sel;
   const int chunk = blockIdx.x % nchunks;
   const size_t row = blockIdx.x / nchunks;  // b * Lq + i
   const int b = (int)(row / Lq);
@@ -681,17 +683,16 @@ void indexer_split_topk_kernel(const uint16_t* __restrict__ q_idx,
   __syncthreads();
 
   u32x2* seg = part + row * (size_t)nchunks * k + (size_t)chunk * k;
-  const int kk = block_topk_collect(skey, n, k, sel, [&](int e) { return c0 + e; },
-                                           [&](int slot, uint32_t key, uint32_t pos) {
-                                             seg[slot] = u32x2{key, pos};
-                                           });
+  const int kk = block_topk_collect<kDecWaves * kWave>(
+      skey, n, k, sel, [&](int e) { return c0 + e; },
+      [&](int slot, uint32_t key, uint32_t pos) { seg[slot] = u32x2{key, pos}; });
   if (threadIdx.x == 0) part_count[row * nchunks + chunk] = kk;
 }
 
 template <int DI, int HB>
 hipError_t launch_split_topk(const IndexerArgs& a, hipStream_t st) {
   const int nchunks = (a.Lk + kDecChunk - 1) / kDecChunk;
-  dim3 grid((unsigned)(nchunks * a.B * a.Lq)), block(kSplitWaves * kWave);
+  dim3 grid((unsigned)(nchunks * a.B * a.Lq)), block(kDecWaves * kWave);
   hipLaunchKernelGGL((indexer_split_topk_kernel<DI, HB>), grid, block, 0, st, a.q_idx, a.k_idx,
                      a.w, a.B, a.Lq, a.Lk, a.q_pos0, a.H_I, a.k, nchunks, a.cand, a.cand_count,
                      a.q_pos);
