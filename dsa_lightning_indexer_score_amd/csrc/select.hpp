@@ -7,8 +7,9 @@
 // asc), emitted in position order through emit(slot, key, position),
 // slot = 0..min(k,n)-1.
 //
-// Method: the keys lie in [lo, lo + R); each pass histograms them into
-// kSelBins equal-width bins of that range, finds the bin holding the rem-th
+// Method: the keys lie in [lo, hi]; each pass histograms them into at most
+// kSelBins bins of one power-of-two width (the smallest that covers the range,
+// so a bin index is a shift of key - lo), finds the bin holding the rem-th
 // largest key and narrows the range to it. It ends when the range is one key
 // (ties: keep the `rem` lowest positions of it) or when every key of the bin
 // is needed. An ordered pass (block prefix sums) then emits the winners.
@@ -19,7 +20,8 @@
 namespace idxc {
 
 constexpr int kSelThreads = 256;  // default workgroup size
-constexpr int kSelBins = 2048;
+constexpr int kSelBinsLog2 = 11;
+constexpr int kSelBins = 1 << kSelBinsLog2;
 constexpr int kSelPerThread = 8;  // ordered pass: consecutive entries per thread
 
 // Scratch of a selection by an NT-thread workgroup.
@@ -63,10 +65,12 @@ __device__ int block_topk_collect(const uint32_t* skey, int n, int k, SelectSmem
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   // ---- select the k-th best key (only needed when n > k). The keys lie in
-  // [lo, lo + R); each pass histograms them into kSelBins equal-width bins of
-  // that range, finds the bin holding the rem-th largest key and narrows the
-  // range to it. It ends when the range is one key (ties: keep the `rem`
-  // lowest positions of it) or when every key of the bin is needed.
+  // [lo, hi]; each pass histograms them into bins of width 2^shift, the
+  // smallest power of two with (hi - lo) >> shift < kSelBins, finds the bin
+  // holding the rem-th largest key and narrows the range to it (by a factor
+  // of at least kSelBins / 2, so at most three passes). It ends when the
+  // range is one key (ties: keep the `rem` lowest positions of it) or when
+  // every key of the bin is needed.
   uint32_t lo = 0u, hi = 0u;  // final key range; keys above hi are all kept
   int rem = 0;
   bool take_range = true;  // keep every key of [lo, hi]
@@ -101,13 +105,13 @@ __device__ int block_topk_collect(const uint32_t* skey, int n, int k, SelectSmem
     take_range = false;
     constexpr int BPT = kSelBins / kSelThreads;  // bins per thread
     while (hi > lo) {
-      const uint64_t R = (uint64_t)hi - lo + 1ull;
+      const uint32_t span = hi - lo;
+      const int shift = max(0, (32 - __clz((int)span)) - kSelBinsLog2);
       for (int b = tid; b < kSelBins; b += kSelThreads) sm.hist[b] = 0u;
       __syncthreads();
       for (int e = tid; e < n; e += kSelThreads) {
         const uint32_t key = skey[e];
-        if (key >= lo && key <= hi)
-          atomicAdd(&sm.hist[(uint32_t)(((uint64_t)(key - lo) * kSelBins) / R)], 1u);
+        if (key >= lo && key <= hi) atomicAdd(&sm.hist[(key - lo) >> shift], 1u);
       }
       __syncthreads();
       // thread tid owns bins top - BPT*tid - (0..BPT-1), highest first
@@ -134,15 +138,14 @@ __device__ int block_topk_collect(const uint32_t* skey, int n, int k, SelectSmem
         }
       }
       __syncthreads();
-      const uint64_t bstar = (uint64_t)sm.bcast[0];
+      const uint32_t bstar = (uint32_t)sm.bcast[0];
       rem -= sm.bcast[1];
       const int cnt_b = sm.bcast[2];
       __syncthreads();
-      // keys of bin b*: key - lo in [ceil(b* R / kSelBins), ceil((b*+1) R / kSelBins) - 1]
-      const uint32_t nlo = lo + (uint32_t)((bstar * R + kSelBins - 1) / kSelBins);
-      const uint32_t nhi = lo + (uint32_t)(((bstar + 1) * R + kSelBins - 1) / kSelBins) - 1u;
+      // keys of bin b*: key - lo in [b* 2^shift, (b*+1) 2^shift - 1], within [lo, hi]
+      const uint32_t nlo = lo + (bstar << shift);
+      hi = nlo + min(hi - nlo, (1u << shift) - 1u);
       lo = nlo;
-      hi = nhi;
       if (cnt_b == rem) {
         take_range = true;
         break;
