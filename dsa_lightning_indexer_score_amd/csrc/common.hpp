@@ -94,27 +94,78 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 
 __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 
-// Wave-wide inclusive prefix sum of an int (64 lanes).
-__device__ __forceinline__ int wave_incl_scan(int v) {
+// v of lane (l ^ M), M a power of two below 64, without LDS traffic: DPP
+// quad permutes (1, 2), a row shift either way (4), a row rotate (8), or a
+// permlane swap (16, 32), which returns both values of each lane pair.
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "lane mask");
   const int lane = lane_id();
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    int o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
+  if constexpr (M == 1) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+  } else if constexpr (M == 2) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  } else if constexpr (M == 4) {
+    const uint32_t up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x104, 0xF, 0xF, false);  // row_shl:4
+    const uint32_t dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    return (lane & 4) ? dn : up;
+  } else if constexpr (M == 8) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane & 32) ? r[0] : r[1];
   }
+}
+
+// Wave-wide inclusive prefix sum of an int (64 lanes): Hillis-Steele steps
+// within each 16-lane row (DPP row shifts, lanes shifted in from outside the
+// row read 0), then each row's last value is added to the rows above it (DPP
+// row broadcasts of lanes 15 and 31).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2 and 3
   return v;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  v = fmaxf(v, __uint_as_float(lane_xor<32>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(lane_xor<16>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(lane_xor<8>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(lane_xor<4>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(lane_xor<2>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(lane_xor<1>(__float_as_uint(v))));
   return v;
 }
 
 __device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  v += (int)lane_xor<32>((uint32_t)v);
+  v += (int)lane_xor<16>((uint32_t)v);
+  v += (int)lane_xor<8>((uint32_t)v);
+  v += (int)lane_xor<4>((uint32_t)v);
+  v += (int)lane_xor<2>((uint32_t)v);
+  v += (int)lane_xor<1>((uint32_t)v);
   return v;
+}
+
+// Wave-wide minimum and maximum of a uint32 (every lane gets both).
+__device__ __forceinline__ void wave_minmax(uint32_t& mn, uint32_t& mx) {
+#define IDXC_MINMAX_STEP(M)              \
+  mn = min(mn, lane_xor<M>(mn));         \
+  mx = max(mx, lane_xor<M>(mx));
+  IDXC_MINMAX_STEP(32)
+  IDXC_MINMAX_STEP(16)
+  IDXC_MINMAX_STEP(8)
+  IDXC_MINMAX_STEP(4)
+  IDXC_MINMAX_STEP(2)
+  IDXC_MINMAX_STEP(1)
+#undef IDXC_MINMAX_STEP
 }
 
 }  // namespace idxc

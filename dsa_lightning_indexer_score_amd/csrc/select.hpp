@@ -82,11 +82,7 @@ __device__ int block_topk_collect(const uint32_t* skey, int n, int k, SelectSmem
       kmin = min(kmin, key);
       kmax = max(kmax, key);
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, kWave));
-      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, kWave));
-    }
+    wave_minmax(kmin, kmax);
     if (lane_id() == 0) {
       sm.kred[wave] = kmin;
       sm.kred[kSelWaves + wave] = kmax;

@@ -53,9 +53,25 @@ constexpr size_t kSortBytes = (size_t)kMaxK * 8;
 enum SrcKind { kSrcRow = 0, kSrcCand = 1, kSrcCand1 = 2 };
 enum OutKind { kOutFinal = 0, kOutPart = 1 };
 
+// 64-bit word of lane (l ^ m) for m = 1 .. 32 (constant once unrolled).
+__device__ __forceinline__ uint64_t lane_xor64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  uint32_t plo, phi;
+  switch (m) {
+    case 1: plo = lane_xor<1>(lo); phi = lane_xor<1>(hi); break;
+    case 2: plo = lane_xor<2>(lo); phi = lane_xor<2>(hi); break;
+    case 4: plo = lane_xor<4>(lo); phi = lane_xor<4>(hi); break;
+    case 8: plo = lane_xor<8>(lo); phi = lane_xor<8>(hi); break;
+    case 16: plo = lane_xor<16>(lo); phi = lane_xor<16>(hi); break;
+    default: plo = lane_xor<32>(lo); phi = lane_xor<32>(hi); break;
+  }
+  return ((uint64_t)phi << 32) | plo;
+}
+
 // Descending bitonic sort of 2048 64-bit words held 8 per thread (thread t
 // holds slots 8t..8t+7). Strides 1-4 stay in the thread, 8-256 cross lanes of
-// the wave, 512 and 1024 go through LDS. Fully unrolled.
+// the wave (DPP and permlane exchanges), 512 and 1024 go through LDS. Fully
+// unrolled.
 __device__ __forceinline__ void sort2048_regs(uint64_t (&v)[8], uint64_t* lds, int tid) {
 #pragma unroll
   for (int size = 2; size <= 2048; size <<= 1) {
@@ -72,17 +88,17 @@ __device__ __forceinline__ void sort2048_regs(uint64_t (&v)[8], uint64_t* lds, i
           for (int j = 0; j < 8; ++j) p[j] = lds[(tid * 8 + j) ^ stride];
         } else {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const uint32_t lo = __shfl_xor((uint32_t)v[j], stride >> 3, kWave);
-            const uint32_t hi = __shfl_xor((uint32_t)(v[j] >> 32), stride >> 3, kWave);
-            p[j] = ((uint64_t)hi << 32) | lo;
-          }
+          for (int j = 0; j < 8; ++j) p[j] = lane_xor64(v[j], stride >> 3);
         }
+        // the lane keeps the larger word when it is the lower slot of a
+        // descending pair or the upper slot of an ascending one (the same
+        // for all 8 words of the thread)
+        const int i = tid * 8;
+        const bool take_max = ((i & stride) == 0) == ((i & size) == 0);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int i = tid * 8 + j;
-          const bool take_max = ((i & stride) == 0) == ((i & size) == 0);
-          v[j] = take_max ? (v[j] > p[j] ? v[j] : p[j]) : (v[j] < p[j] ? v[j] : p[j]);
+          const bool gt = v[j] > p[j];
+          v[j] = (gt == take_max) ? v[j] : p[j];
         }
       } else {
 #pragma unroll
