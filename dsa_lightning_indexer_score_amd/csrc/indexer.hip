@@ -587,6 +587,7 @@ void indexer_split_kernel(const uint16_t* __restrict__ q_idx,
 // chunks halve the segments the final selection stages, against 8192.)
 // ---------------------------------------------------------------------------
 constexpr int kDecChunk = 16384;
+static_assert(kDecChunk <= kSelMaxKeys, "selection histogram counts fit 16 bits");
 constexpr int kDecWaves = 8;
 constexpr int kDecKeysPerWave = kDecChunk / kDecWaves;
 

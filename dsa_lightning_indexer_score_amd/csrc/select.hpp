@@ -1,8 +1,8 @@
 // Block-wide exact top-k selection over keys staged in LDS (shared by the
 // selection kernels and the decode indexer). Internal to libidxc.
 //
-// Input: n order-preserving 32-bit keys skey[0..n) in increasing position
-// order; pos_of(e) gives the position of entry e and is called only for the
+// Input: n <= kSelMaxKeys order-preserving 32-bit keys skey[0..n) in
+// increasing position order; pos_of(e) gives the position of entry e and is called only for the
 // winners. Output: the min(k, n) best entries under (key desc, position
 // asc), emitted in position order through emit(slot, key, position),
 // slot = 0..min(k,n)-1.
@@ -24,14 +24,19 @@ constexpr int kSelBinsLog2 = 11;
 constexpr int kSelBins = 1 << kSelBinsLog2;
 constexpr int kSelPerThread = 8;  // ordered pass: consecutive entries per thread
 
-// Scratch of a selection by an NT-thread workgroup.
+// Scratch of a selection by an NT-thread workgroup. The histogram packs two
+// 16-bit counts per word (bin b in half b % 2 of word b / 2): a selection
+// covers fewer than 65536 keys, so no count carries into its neighbour. It
+// comes last, so a caller can overlay a larger buffer on it once the
+// selection is done.
 template <int NT = kSelThreads>
 struct SelectSmemT {
-  uint32_t hist[kSelBins];
   int scan[NT / kWave];
   int bcast[4];
   uint32_t kred[2 * (NT / kWave)];
+  alignas(16) uint32_t hist[kSelBins / 2];
 };
+constexpr int kSelMaxKeys = 65535;
 using SelectSmem = SelectSmemT<>;
 
 // Block-wide exclusive prefix sum (NT threads); *total = block sum.
@@ -61,7 +66,7 @@ __device__ int block_topk_collect(const uint32_t* skey, int n, int k, SelectSmem
   constexpr int kSelThreads = NT;
   constexpr int kSelWaves = NT / kWave;
   constexpr int kSelChunk = NT * kSelPerThread;
-  static_assert(kSelBins % NT == 0, "bins split evenly over the threads");
+  static_assert(kSelBins % (2 * NT) == 0, "whole histogram words per thread");
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   // ---- select the k-th best key (only needed when n > k). The keys lie in
@@ -103,21 +108,27 @@ __device__ int block_topk_collect(const uint32_t* skey, int n, int k, SelectSmem
     while (hi > lo) {
       const uint32_t span = hi - lo;
       const int shift = max(0, (32 - __clz((int)span)) - kSelBinsLog2);
-      for (int b = tid; b < kSelBins; b += kSelThreads) sm.hist[b] = 0u;
+      for (int b = tid; b < kSelBins / 2; b += kSelThreads) sm.hist[b] = 0u;
       __syncthreads();
       for (int e = tid; e < n; e += kSelThreads) {
         const uint32_t key = skey[e];
-        if (key >= lo && key <= hi) atomicAdd(&sm.hist[(key - lo) >> shift], 1u);
+        if (key >= lo && key <= hi) {
+          const uint32_t bin = (key - lo) >> shift;
+          atomicAdd(&sm.hist[bin >> 1], 1u << ((bin & 1u) << 4));
+        }
       }
       __syncthreads();
-      // thread tid owns bins top - BPT*tid - (0..BPT-1), highest first
+      // thread tid owns bins top - q, q = 0..BPT-1 (highest first; top is
+      // odd, so bins top - q and top - q - 1 share a word for even q)
       const int top = kSelBins - 1 - BPT * tid;
       int cnts[BPT];
       int local = 0;
 #pragma unroll
-      for (int q = 0; q < BPT; ++q) {
-        cnts[q] = (int)sm.hist[top - q];
-        local += cnts[q];
+      for (int q = 0; q < BPT; q += 2) {
+        const uint32_t w = sm.hist[(top - q) >> 1];
+        cnts[q] = (int)(w >> 16);
+        cnts[q + 1] = (int)(w & 0xFFFFu);
+        local += cnts[q] + cnts[q + 1];
       }
       int total;
       const int excl = sel_excl_scan<NT>(local, sm.scan, &total);

@@ -33,20 +33,28 @@ constexpr int kThreads = kSelThreads;
 // workgroups: there are few of them, so latency per row is what counts
 constexpr int kThreadsWide = 1024;
 constexpr int kBatch = 8;  // staged loads in flight per thread
+static_assert(kTopkChunk <= kSelMaxKeys && kMaxStagePairs <= kSelMaxKeys,
+              "selection histogram counts fit 16 bits");
 
-// LDS: selection scratch and segment offsets, then the staged keys, then
-// (multi-segment candidate lists only) the staged positions, then (score
-// order only) the sort buffer. Position-order output needs no sort buffer,
-// and single-segment lists read their winners' positions back from memory,
-// so the common candidate case stages keys alone.
+// LDS: segment offsets and selection scratch, then the staged keys, then
+// (multi-segment candidate lists only) the staged positions. Score-order
+// output sorts its winners in a buffer laid over the selection histogram
+// (which the winners' collection no longer reads), extended past the end of
+// the scratch, so the staged keys start after it. Position-order output needs
+// no sort buffer, and single-segment lists read their winners' positions
+// back from memory, so the common candidate case stages keys alone.
 template <int NT>
 struct Smem {
-  SelectSmemT<NT> sel;
   int seg_off[kMaxSegments + 1];
+  SelectSmemT<NT> sel;  // histogram last
 };
 template <int NT>
 constexpr size_t smem_bytes() {
   return (sizeof(Smem<NT>) + 15) / 16 * 16;
+}
+template <int NT>
+constexpr size_t sort_off() {
+  return offsetof(Smem<NT>, sel) + offsetof(SelectSmemT<NT>, hist);
 }
 constexpr size_t kSortBytes = (size_t)kMaxK * 8;
 
@@ -120,15 +128,15 @@ __device__ __forceinline__ void sort2048_regs(uint64_t (&v)[8], uint64_t* lds, i
 // One workgroup = one (row, chunk). SRC kSrcRow: positions [c0, c1) of a score
 // row. SRC kSrcCand: the concatenation of nseg segments of a row (positions
 // staged too). SRC kSrcCand1: one segment (positions read back for winners).
-// The sort buffer sits at byte sort_off of the dynamic LDS.
+// The staged input starts at byte stage_off of the dynamic LDS.
 template <int SRC, int OUT, int NT>
 __global__ __launch_bounds__(NT)
-void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int sort_off) {
+void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int stage_off) {
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   Smem<NT>& sm = *reinterpret_cast<Smem<NT>*>(dyn);
-  uint32_t* skey = reinterpret_cast<uint32_t*>(dyn + smem_bytes<NT>());
+  uint32_t* skey = reinterpret_cast<uint32_t*>(dyn + stage_off);
   uint32_t* spos = nullptr;  // SRC kSrcCand: positions after the keys
-  uint64_t* sortbuf = reinterpret_cast<uint64_t*>(dyn + sort_off);
+  uint64_t* sortbuf = reinterpret_cast<uint64_t*>(dyn + sort_off<NT>());
 
   const int tid = threadIdx.x;
   const int k = a.k;
@@ -282,14 +290,16 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int sort_off) {
   }
 }
 
-// stage_bytes: the staged input; the sort buffer follows it unless the output
-// is in position order (or is a stage-1 part)
+// stage_bytes: the staged input, after the scratch or, for score-order
+// output, after the sort buffer laid over the histogram
 template <int SRC, int OUT, int NT = kThreads>
 hipError_t launch_one(const TopkArgs& a, int chunk_len, int nchunks, size_t stage_bytes,
                       hipStream_t st) {
-  const size_t sort_off = smem_bytes<NT>() + (stage_bytes + 15) / 16 * 16;
+  static_assert(sort_off<NT>() % 16 == 0, "aligned sort buffer");
   const bool need_sort = OUT == kOutFinal && !a.pos_order;
-  const size_t shmem = sort_off + (need_sort ? kSortBytes : 0);
+  size_t stage_off = smem_bytes<NT>();
+  if (need_sort && sort_off<NT>() + kSortBytes > stage_off) stage_off = sort_off<NT>() + kSortBytes;
+  const size_t shmem = stage_off + (stage_bytes + 15) / 16 * 16;
   auto fn = topk_kernel<SRC, OUT, NT>;
   if (shmem > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
@@ -297,7 +307,7 @@ hipError_t launch_one(const TopkArgs& a, int chunk_len, int nchunks, size_t stag
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(fn, dim3((unsigned)(a.rows * nchunks)), dim3(NT), shmem, st, a,
-                     chunk_len, nchunks, (int)sort_off);
+                     chunk_len, nchunks, (int)stage_off);
   return hipGetLastError();
 }
 
