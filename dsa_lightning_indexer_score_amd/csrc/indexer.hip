@@ -638,13 +638,16 @@ void indexer_split_topk_kernel(const uint16_t* __restrict__ q_idx,
   const int e_end = min(e_begin + kDecKeysPerWave, n);
   const int nb = e_end > e_begin ? (e_end - e_begin + 31) / 32 : 0;
 
+  // Loads are issued unconditionally, at the last key for rows past the
+  // keys (blocks past the wave's range included): their scores are never
+  // stored, and loads under a branch would make the compiler wait for every
+  // outstanding load at the top of the loop instead of for the oldest block.
   auto load_b = [&](int j, bf16x8* dst) {
-    const int s = c0 + e_begin + j * 32 + (lane & 31);
-    const bool ok = s < Lk;
+    const int s = min(c0 + e_begin + j * 32 + (lane & 31), Lk - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int c = ks * 2 + (lane >> 5);
-      dst[ks] = ok ? *reinterpret_cast<const bf16x8*>(kbase + (size_t)s * DI + c * 8) : bf16x8{};
+      dst[ks] = *reinterpret_cast<const bf16x8*>(kbase + (size_t)s * DI + c * 8);
     }
   };
   auto score_block = [&](int j, const bf16x8* bop) {
@@ -665,20 +668,18 @@ void indexer_split_topk_kernel(const uint16_t* __restrict__ q_idx,
     if (lane < 32 && e < e_end) skey[e] = order_key(val);
   };
 
-  bf16x8 b0[KS], b1[KS], b2[KS];
-  if (nb > 0) load_b(0, b0);
-  if (nb > 1) load_b(1, b1);
-  if (nb > 2) load_b(2, b2);
-  for (int j = 0; j < nb; j += 3) {
-    score_block(j, b0);
-    if (j + 3 < nb) load_b(j + 3, b0);
-    if (j + 1 < nb) {
+  if (nb > 0) {  // wave-uniform; inside, every block's loads and MFMAs run
+    bf16x8 b0[KS], b1[KS], b2[KS];
+    load_b(0, b0);
+    load_b(1, b1);
+    load_b(2, b2);
+    for (int j = 0; j < nb; j += 3) {
+      score_block(j, b0);
+      load_b(j + 3, b0);
       score_block(j + 1, b1);
-      if (j + 4 < nb) load_b(j + 4, b1);
-    }
-    if (j + 2 < nb) {
+      load_b(j + 4, b1);
       score_block(j + 2, b2);
-      if (j + 5 < nb) load_b(j + 5, b2);
+      load_b(j + 5, b2);
     }
   }
   __syncthreads();

@@ -193,8 +193,18 @@ __device__ int block_topk_collect(const uint32_t* skey, int n, int k, SelectSmem
         }
       }
     }
-    int eq_total;
-    const int eq_excl = eq_seen + sel_excl_scan<NT>(__popc(eq_bits), sm.scan, &eq_total);
+    // positions of the entries that may be kept, fetched before the prefix
+    // sums so that a pos_of that reads memory overlaps them
+    uint32_t pv[kSelPerThread];
+    const unsigned cand_bits = gt_bits | eq_bits;
+#pragma unroll
+    for (int j = 0; j < kSelPerThread; ++j)
+      pv[j] = ((cand_bits >> j) & 1u) ? (uint32_t)pos_of(e0 + j) : 0u;
+    // entries equal to the threshold key exist only after a selection that
+    // ended on a single key (a block-uniform condition)
+    int eq_total = 0, eq_excl = eq_seen;
+    if (!select_all && !take_range)
+      eq_excl += sel_excl_scan<NT>(__popc(eq_bits), sm.scan, &eq_total);
     unsigned keep_bits = gt_bits;
     int r = eq_excl;
 #pragma unroll
@@ -209,7 +219,7 @@ __device__ int block_topk_collect(const uint32_t* skey, int n, int k, SelectSmem
 #pragma unroll
     for (int j = 0; j < kSelPerThread; ++j) {
       if (keep_bits & (1u << j)) {
-        emit(pos, keys[j], (uint32_t)pos_of(e0 + j));
+        emit(pos, keys[j], pv[j]);
         ++pos;
       }
     }
