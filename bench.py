@@ -321,9 +321,10 @@ def distill_rate(Lq=2048, Lk=32768, n_teachers=4, seed=0):
             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
-def standalone_topk(B, Lq, Lk, q_pos0, k, seed=0):
-    """idxc_topk on materialised fp32 scores; algorithmic bytes = valid scores
-    read (4 B each) + indices written (4 B each)."""
+def standalone_topk(B, Lq, Lk, q_pos0, k, seed=0, order="score"):
+    """idxc_topk on materialised fp32 scores, in score order (sorted output)
+    or position order (the index cache's order, no sort); algorithmic bytes =
+    valid scores read (4 B each) + indices written (4 B each)."""
     import torch
     import dsa_lightning_indexer_score_amd as idxc
     g = torch.Generator(device="cuda")
@@ -332,10 +333,12 @@ def standalone_topk(B, Lq, Lk, q_pos0, k, seed=0):
     ws_n = idxc.idxc_topk_workspace_bytes(B, Lq, Lk, q_pos0, k)
     ws = torch.empty((max(ws_n, 256),), dtype=torch.uint8, device="cuda")
     out = torch.empty((B, Lq, k), dtype=torch.int32, device="cuda")
-    ms = events_ms(lambda: idxc.idxc_topk(s, k, q_pos0=q_pos0, workspace=ws, out=out), 5)
+    ms = events_ms(lambda: idxc.idxc_topk(s, k, q_pos0=q_pos0, workspace=ws, out=out,
+                                          order=order), 5)
     nbytes = B * causal_pairs(q_pos0, Lq) * 4 + B * Lq * k * 4
     del s
-    return {"shape": [B, Lq, Lk], "k": k, "ms": ms, "GBs": nbytes / (ms * 1e-3) / 1e9,
+    return {"shape": [B, Lq, Lk], "k": k, "order": order, "ms": ms,
+            "GBs": nbytes / (ms * 1e-3) / 1e9,
             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
@@ -630,9 +633,15 @@ def main():
             % (dl["ms"], dl["GBs"]))
         extra["distill_loss"] = dl
         tk = {"decode_rows": standalone_topk(64, 1, 65536, 65535, 2048),
-              "prefill_rows": standalone_topk(1, 8192, 8192, 0, 2048)}
-        log("standalone top-k: %.0f GB/s (64 x 65536), %.0f GB/s (8192 x 8192 causal)"
-            % (tk["decode_rows"]["GBs"], tk["prefill_rows"]["GBs"]))
+              "prefill_rows": standalone_topk(1, 8192, 8192, 0, 2048),
+              "decode_rows_position_order": standalone_topk(64, 1, 65536, 65535, 2048,
+                                                            order="position"),
+              "prefill_rows_position_order": standalone_topk(1, 8192, 8192, 0, 2048,
+                                                             order="position")}
+        log("standalone top-k: %.0f GB/s (64 x 65536), %.0f GB/s (8192 x 8192 causal); "
+            "position order %.0f / %.0f GB/s"
+            % (tk["decode_rows"]["GBs"], tk["prefill_rows"]["GBs"],
+               tk["decode_rows_position_order"]["GBs"], tk["prefill_rows_position_order"]["GBs"]))
         extra["standalone_topk"] = tk
         torch.cuda.empty_cache()
 

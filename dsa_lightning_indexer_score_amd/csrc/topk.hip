@@ -152,7 +152,31 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int stage_off) {
     pos0 = chunk * chunk_len;
     n = max(0, min(len, pos0 + chunk_len) - pos0);
     const float* src = a.scores + (size_t)row * a.Lk + pos0;
-    for (int base = 0; base < n; base += NT * kBatch) {
+    int done = 0;
+    if ((reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+      // 16-byte loads (4 keys each), kBatch of them in flight per thread
+      const int n4 = n >> 2;
+      const f32x4* src4 = reinterpret_cast<const f32x4*>(src);
+      for (int base = 0; base < n4; base += NT * kBatch) {
+        f32x4 v[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int e = base + j * NT + tid;
+          v[j] = e < n4 ? src4[e] : f32x4{};
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int e = base + j * NT + tid;
+          if (e < n4)
+            *reinterpret_cast<u32x4*>(skey + 4 * e) =
+                u32x4{order_key(v[j][0]), order_key(v[j][1]), order_key(v[j][2]),
+                      order_key(v[j][3])};
+        }
+      }
+      done = n4 * 4;
+    }
+    // the rest: a tail of up to 3 keys, or a row that is not 16-byte aligned
+    for (int base = done; base < n; base += NT * kBatch) {
       float v[kBatch];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
@@ -168,7 +192,27 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int stage_off) {
   } else if (SRC == kSrcCand1) {
     n = a.cand_count[row];
     const u32x2* src = a.cand + (size_t)row * a.seg_cap;
-    for (int base = 0; base < n; base += NT * kBatch) {
+    int done = 0;
+    if ((reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+      // 16-byte loads (2 pairs each), kBatch of them in flight per thread
+      const int n2 = n >> 1;
+      const u32x4* src2 = reinterpret_cast<const u32x4*>(src);
+      for (int base = 0; base < n2; base += NT * kBatch) {
+        u32x4 v[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int e = base + j * NT + tid;
+          v[j] = e < n2 ? src2[e] : u32x4{};
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int e = base + j * NT + tid;
+          if (e < n2) *reinterpret_cast<u32x2*>(skey + 2 * e) = u32x2{v[j][0], v[j][2]};
+        }
+      }
+      done = n2 * 2;
+    }
+    for (int base = done; base < n; base += NT * kBatch) {
       uint32_t v[kBatch];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
