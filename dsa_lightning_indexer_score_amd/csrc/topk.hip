@@ -76,11 +76,14 @@ __device__ __forceinline__ uint64_t lane_xor64(uint64_t v, int m) {
   return ((uint64_t)phi << 32) | plo;
 }
 
-// Descending bitonic sort of 2048 64-bit words held 8 per thread (thread t
-// holds slots 8t..8t+7). Strides 1-4 stay in the thread, 8-256 cross lanes of
-// the wave (DPP and permlane exchanges), 512 and 1024 go through LDS. Fully
+// Descending bitonic sort of 2048 64-bit words held 8 per thread by the
+// first 256 threads of the workgroup (thread t holds slots 8t..8t+7; `act`
+// marks them, whole waves: the others only take part in the barriers).
+// Strides 1-4 stay in the thread, 8-256 cross lanes of the wave (DPP and
+// permlane exchanges), 512 and 1024 go through LDS (2048 words). Fully
 // unrolled.
-__device__ __forceinline__ void sort2048_regs(uint64_t (&v)[8], uint64_t* lds, int tid) {
+__device__ __forceinline__ void sort2048_regs(uint64_t (&v)[8], uint64_t* lds, int tid,
+                                              bool act) {
 #pragma unroll
   for (int size = 2; size <= 2048; size <<= 1) {
 #pragma unroll
@@ -89,15 +92,20 @@ __device__ __forceinline__ void sort2048_regs(uint64_t (&v)[8], uint64_t* lds, i
         uint64_t p[8];
         if (stride >= 8 * kWave) {
           __syncthreads();
+          if (act) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) lds[tid * 8 + j] = v[j];
+            for (int j = 0; j < 8; ++j) lds[tid * 8 + j] = v[j];
+          }
           __syncthreads();
+          if (act) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) p[j] = lds[(tid * 8 + j) ^ stride];
-        } else {
+            for (int j = 0; j < 8; ++j) p[j] = lds[(tid * 8 + j) ^ stride];
+          }
+        } else if (act) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) p[j] = lane_xor64(v[j], stride >> 3);
         }
+        if (!act) continue;
         // the lane keeps the larger word when it is the lower slot of a
         // descending pair or the upper slot of an ascending one (the same
         // for all 8 words of the thread)
@@ -108,7 +116,7 @@ __device__ __forceinline__ void sort2048_regs(uint64_t (&v)[8], uint64_t* lds, i
           const bool gt = v[j] > p[j];
           v[j] = (gt == take_max) ? v[j] : p[j];
         }
-      } else {
+      } else if (act) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           if ((j & stride) == 0) {
@@ -295,19 +303,25 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int stage_off) {
   // ---- bitonic sort, descending, of the kk winners padded to a power of two
   int P = 1;
   while (P < kk) P <<= 1;
-  if (NT == kThreads && P == NT * 8) {
+  static_assert(kMaxK == 8 * kThreads && NT % kThreads == 0, "register sort layout");
+  if (P >= 512) {
+    // the register sort of all 2048 slots, the ones past kk zero (every
+    // winner's word is nonzero, so they sort last)
+    const bool act = NT == kThreads || tid < kThreads;
     __syncthreads();
     uint64_t v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int idx = tid * 8 + j;
-      v[j] = idx < kk ? sortbuf[idx] : 0ull;
+      v[j] = (act && idx < kk) ? sortbuf[idx] : 0ull;
     }
-    sort2048_regs(v, sortbuf, tid);
+    sort2048_regs(v, sortbuf, tid, act);
+    if (act) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int idx = tid * 8 + j;
-      if (idx < k) orow[idx] = (idx < kk) ? (int32_t)(~(uint32_t)(v[j] & 0xFFFFFFFFull)) : -1;
+      for (int j = 0; j < 8; ++j) {
+        const int idx = tid * 8 + j;
+        if (idx < k) orow[idx] = (idx < kk) ? (int32_t)(~(uint32_t)(v[j] & 0xFFFFFFFFull)) : -1;
+      }
     }
     return;
   }
