@@ -650,6 +650,7 @@ void indexer_split_topk_kernel(const uint16_t* __restrict__ q_idx,
       dst[ks] = *reinterpret_cast<const bf16x8*>(kbase + (size_t)s * DI + c * 8);
     }
   };
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;  // range of the keys this lane stores
   auto score_block = [&](int j, const bf16x8* bop) {
     float part0 = 0.0f, part1 = 0.0f;
 #pragma unroll
@@ -665,7 +666,12 @@ void indexer_split_topk_kernel(const uint16_t* __restrict__ q_idx,
     }
     const float val = pair_sum(part0 + part1) + 0.0f;
     const int e = e_begin + j * 32 + lane;
-    if (lane < 32 && e < e_end) skey[e] = order_key(val);
+    if (lane < 32 && e < e_end) {
+      const uint32_t key = order_key(val);
+      skey[e] = key;
+      kmin = min(kmin, key);
+      kmax = max(kmax, key);
+    }
   };
 
   if (nb > 0) {  // wave-uniform; inside, every block's loads and MFMAs run
@@ -682,12 +688,14 @@ void indexer_split_topk_kernel(const uint16_t* __restrict__ q_idx,
       load_b(j + 5, b2);
     }
   }
+  sel_store_key_range<kDecWaves * kWave>(kmin, kmax, sel);
   __syncthreads();
 
   u32x2* seg = part + row * (size_t)nchunks * k + (size_t)chunk * k;
   const int kk = block_topk_collect<kDecWaves * kWave>(
       skey, n, k, sel, [&](int e) { return c0 + e; },
-      [&](int slot, uint32_t key, uint32_t pos) { seg[slot] = u32x2{key, pos}; });
+      [&](int slot, uint32_t key, uint32_t pos) { seg[slot] = u32x2{key, pos}; },
+      /*range_ready=*/true);
   if (threadIdx.x == 0) part_count[row * nchunks + chunk] = kk;
 }
 

@@ -60,9 +60,24 @@ __device__ __forceinline__ int sel_excl_scan(int v, int* scan, int* total) {
   return off + incl - v;
 }
 
+// The key range of a selection gathered while the keys are staged: each
+// thread passes the least and greatest key it stored (UINT32_MAX and 0 if
+// none), each wave's reduction lands in the scratch, and a barrier must come
+// before block_topk_collect(..., range_ready = true) reads it.
+template <int NT>
+__device__ __forceinline__ void sel_store_key_range(uint32_t kmin, uint32_t kmax,
+                                                    SelectSmemT<NT>& sm) {
+  wave_minmax(kmin, kmax);
+  if (lane_id() == 0) {
+    const int wave = threadIdx.x / kWave;
+    sm.kred[wave] = kmin;
+    sm.kred[NT / kWave + wave] = kmax;
+  }
+}
+
 template <int NT = kSelThreads, typename PosOf, typename Emit>
 __device__ int block_topk_collect(const uint32_t* skey, int n, int k, SelectSmemT<NT>& sm,
-                                  PosOf pos_of, Emit emit) {
+                                  PosOf pos_of, Emit emit, bool range_ready = false) {
   constexpr int kSelThreads = NT;
   constexpr int kSelWaves = NT / kWave;
   constexpr int kSelChunk = NT * kSelPerThread;
@@ -82,17 +97,15 @@ __device__ int block_topk_collect(const uint32_t* skey, int n, int k, SelectSmem
   const bool select_all = n <= k;
   if (!select_all) {
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-    for (int e = tid; e < n; e += kSelThreads) {
-      const uint32_t key = skey[e];
-      kmin = min(kmin, key);
-      kmax = max(kmax, key);
+    if (!range_ready) {  // block-uniform
+      for (int e = tid; e < n; e += kSelThreads) {
+        const uint32_t key = skey[e];
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
+      }
+      sel_store_key_range<NT>(kmin, kmax, sm);
+      __syncthreads();
     }
-    wave_minmax(kmin, kmax);
-    if (lane_id() == 0) {
-      sm.kred[wave] = kmin;
-      sm.kred[kSelWaves + wave] = kmax;
-    }
-    __syncthreads();
     kmin = sm.kred[0];
     kmax = sm.kred[kSelWaves];
 #pragma unroll

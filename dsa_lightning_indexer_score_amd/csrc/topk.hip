@@ -151,8 +151,10 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int stage_off) {
   const int row = blockIdx.x / nchunks;
   const int chunk = blockIdx.x % nchunks;
 
-  // ---- stage the input in LDS (keys, and positions for candidate lists)
+  // ---- stage the input in LDS (keys, and positions for candidate lists),
+  // noting the range of the keys this thread stores
   int n;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   int pos0 = 0;  // kSrcRow: position of entry 0
   if (SRC == kSrcRow) {
     const int i = row % a.Lq;
@@ -175,10 +177,13 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int stage_off) {
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
           const int e = base + j * NT + tid;
-          if (e < n4)
-            *reinterpret_cast<u32x4*>(skey + 4 * e) =
-                u32x4{order_key(v[j][0]), order_key(v[j][1]), order_key(v[j][2]),
-                      order_key(v[j][3])};
+          if (e < n4) {
+            const u32x4 kv = u32x4{order_key(v[j][0]), order_key(v[j][1]),
+                                   order_key(v[j][2]), order_key(v[j][3])};
+            *reinterpret_cast<u32x4*>(skey + 4 * e) = kv;
+            kmin = min(min(kmin, min(kv[0], kv[1])), min(kv[2], kv[3]));
+            kmax = max(max(kmax, max(kv[0], kv[1])), max(kv[2], kv[3]));
+          }
         }
       }
       done = n4 * 4;
@@ -194,7 +199,12 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int stage_off) {
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         const int e = base + j * NT + tid;
-        if (e < n) skey[e] = order_key(v[j]);
+        if (e < n) {
+          const uint32_t key = order_key(v[j]);
+          skey[e] = key;
+          kmin = min(kmin, key);
+          kmax = max(kmax, key);
+        }
       }
     }
   } else if (SRC == kSrcCand1) {
@@ -215,7 +225,11 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int stage_off) {
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
           const int e = base + j * NT + tid;
-          if (e < n2) *reinterpret_cast<u32x2*>(skey + 2 * e) = u32x2{v[j][0], v[j][2]};
+          if (e < n2) {
+            *reinterpret_cast<u32x2*>(skey + 2 * e) = u32x2{v[j][0], v[j][2]};
+            kmin = min(kmin, min(v[j][0], v[j][2]));
+            kmax = max(kmax, max(v[j][0], v[j][2]));
+          }
         }
       }
       done = n2 * 2;
@@ -230,7 +244,11 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int stage_off) {
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         const int e = base + j * NT + tid;
-        if (e < n) skey[e] = v[j];
+        if (e < n) {
+          skey[e] = v[j];
+          kmin = min(kmin, v[j]);
+          kmax = max(kmax, v[j]);
+        }
       }
     }
   } else {
@@ -267,12 +285,15 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int stage_off) {
           const int e = base + j * NT + tid;
           if (e < cnt) {
             skey[off + e] = v[j].x;
+            kmin = min(kmin, v[j].x);
+            kmax = max(kmax, v[j].x);
             spos[off + e] = v[j].y;
           }
         }
       }
     }
   }
+  sel_store_key_range<NT>(kmin, kmax, sm.sel);
   __syncthreads();
 
   u32x2* part = nullptr;
@@ -290,7 +311,8 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int stage_off) {
         if (OUT == kOutPart) part[slot] = u32x2{key, pos};
         else if (pos_order) orow[slot] = (int32_t)pos;
         else sortbuf[slot] = (((uint64_t)key) << 32) | (uint64_t)(~pos);
-      });
+      },
+      /*range_ready=*/true);
   if (OUT == kOutPart) {
     if (tid == 0) a.part_count[row * nchunks + chunk] = kk;
     return;
