@@ -1,8 +1,8 @@
 // Block-wide exact top-k selection over keys staged in LDS (shared by the
 // selection kernels and the decode indexer). Internal to libidxc.
 //
-// Input: n <= kSelMaxKeys order-preserving 32-bit keys skey[0..n) in
-// increasing position order; pos_of(e) gives the position of entry e and is called only for the
+// Input: n <= kSelMaxKeys order-preserving 32-bit keys skey[0..n) (16-byte
+// aligned) in increasing position order; pos_of(e) gives the position of entry e and is called only for the
 // winners. Output: the min(k, n) best entries under (key desc, position
 // asc), emitted in position order through emit(slot, key, position),
 // slot = 0..min(k,n)-1.
@@ -123,13 +123,22 @@ __device__ int block_topk_collect(const uint32_t* skey, int n, int k, SelectSmem
       const int shift = max(0, (32 - __clz((int)span)) - kSelBinsLog2);
       for (int b = tid; b < kSelBins / 2; b += kSelThreads) sm.hist[b] = 0u;
       __syncthreads();
-      for (int e = tid; e < n; e += kSelThreads) {
-        const uint32_t key = skey[e];
+      auto count = [&](uint32_t key) {
         if (key >= lo && key <= hi) {
           const uint32_t bin = (key - lo) >> shift;
           atomicAdd(&sm.hist[bin >> 1], 1u << ((bin & 1u) << 4));
         }
+      };
+      // keys four at a time (16-byte LDS reads), then the tail
+      const int n4 = n >> 2;
+      for (int e = tid; e < n4; e += kSelThreads) {
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(skey + 4 * e);
+        count(kv[0]);
+        count(kv[1]);
+        count(kv[2]);
+        count(kv[3]);
       }
+      for (int e = 4 * n4 + tid; e < n; e += kSelThreads) count(skey[e]);
       __syncthreads();
       // thread tid owns bins top - q, q = 0..BPT-1 (highest first; top is
       // odd, so bins top - q and top - q - 1 share a word for even q)
