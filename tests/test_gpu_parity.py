@@ -114,6 +114,53 @@ def test_topk_exact(kind, B, Lq, Lk, q_pos0, k):
     assert np.array_equal(got_pos.cpu().numpy(), oracle.position_order(want))
 
 
+def _extreme_rows(kind, B, Lq, Lk, seed=11):
+    """Score rows at the edges of the selection's key handling."""
+    rng = np.random.default_rng(seed)
+    if kind == "equal":  # every key in one histogram bin
+        s = np.full((B, Lq, Lk), 0.75, np.float32)
+    elif kind == "extremes":  # the widest key range: +-max finite, +-inf, zeros, tiny
+        big = np.finfo(np.float32).max
+        vals = np.array([big, -big, np.inf, -np.inf, 0.0, -0.0, 1e-38, -1e-45, 3.0, -3.0],
+                        np.float32)
+        s = rng.choice(vals, size=(B, Lq, Lk)).astype(np.float32)
+    else:  # "ulps": a key range narrower than one pass's bins (1 + i ulp)
+        i = rng.integers(0, 1500, size=(B, Lq, Lk)).astype(np.float32)
+        s = (np.float32(1.0) + i * np.float32(2.0 ** -23)).astype(np.float32)
+    return torch.from_numpy(s)
+
+
+@pytest.mark.parametrize("kind", ["equal", "extremes", "ulps"])
+@pytest.mark.parametrize("B,Lq,Lk,q_pos0,k", [
+    (1, 40, 8192, 8152, 2048),     # one workgroup per row, register sort
+    (1, 3, 16384, 16381, 2048),    # two stages, 1024-thread final selection
+    (2, 2, 12000, 11998, 300),     # two stages, sort of 300 padded to 512
+    (1, 70, 3001, 2931, 1024),     # odd row length: 16-byte staging plus a tail
+])
+def test_topk_extreme_key_ranges_exact(kind, B, Lq, Lk, q_pos0, k):
+    _say("topk extremes %s B=%d Lq=%d Lk=%d q_pos0=%d k=%d" % (kind, B, Lq, Lk, q_pos0, k))
+    s = _extreme_rows(kind, B, Lq, Lk)
+    got = idxc.idxc_topk(cu(s), k, q_pos0=q_pos0)
+    got_pos = idxc.idxc_topk(cu(s), k, q_pos0=q_pos0, order="position")
+    torch.cuda.synchronize()
+    want = oracle.topk(s.numpy(), k, q_pos0)
+    assert np.array_equal(got.cpu().numpy(), want)
+    assert np.array_equal(got_pos.cpu().numpy(), oracle.position_order(want))
+
+
+def test_decode_indexer_all_equal_scores_exact():
+    """Zero indexer keys give every key the score 0: one histogram bin holds
+    all 16384 keys of a decode chunk, and the ties keep the lowest positions."""
+    B, Lk, H_I, d_I, k = 2, 40000, 64, 128, 2048
+    _say("decode indexer equal scores B=%d Lk=%d" % (B, Lk))
+    q, kk, w = gen.indexer_inputs(B, 1, Lk, H_I, d_I, kind="int", seed=21)
+    kk = torch.zeros_like(kk)
+    got = idxc.idxc_indexer_topk(cu(q), cu(kk), cu(w), k, q_pos0=Lk - 1)
+    torch.cuda.synchronize()
+    want = np.broadcast_to(np.arange(k, dtype=np.int32), (B, 1, k))
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
 # --------------------------------------------------------------------------- #
 # fused indexer + top-k
 # --------------------------------------------------------------------------- #
