@@ -80,6 +80,26 @@ def time_steps(fn, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
+_SLEEP_CYCLES_PER_MS = None
+
+
+def gpu_head_start(ms):
+    """Queue a spin kernel of about `ms` milliseconds (torch.cuda._sleep,
+    calibrated once with HIP events) on the current stream."""
+    global _SLEEP_CYCLES_PER_MS
+    import torch
+    if _SLEEP_CYCLES_PER_MS is None:
+        cycles = 1 << 20
+        torch.cuda._sleep(cycles)  # warm-up
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(cycles)
+        b.record()
+        b.synchronize()
+        _SLEEP_CYCLES_PER_MS = cycles / max(a.elapsed_time(b), 1e-3)
+    torch.cuda._sleep(int(min(ms, 2000.0) * _SLEEP_CYCLES_PER_MS))
+
+
 def kernel_pass(cfg, layers, ws, cache, steps):
     """Run the stack layer by layer through the per-layer entry points (the
     same launches, in the same order, as one stack call) with HIP events on
@@ -104,6 +124,10 @@ def kernel_pass(cfg, layers, ws, cache, steps):
             events.append((cfg.pattern[l] == "F", e))
 
     one_step([])
+    # Keep the GPU busy while the host enqueues the timed steps: decode
+    # launches are shorter than their host-side launch work, and events taken
+    # while the GPU waits for the host would time the host.
+    gpu_head_start(steps * 10.0 * len(layers) / 47.0)
     events = []
     for _ in range(steps):
         one_step(events)
@@ -175,10 +199,12 @@ def attn_flops(cfg):
 # --------------------------------------------------------------------------- #
 def events_ms(fn, reps=1):
     """Mean device time of fn() over reps calls on torch's current stream (the
-    stream the library launches on), after one untimed call."""
+    stream the library launches on), after one untimed call, with the GPU
+    kept busy while the host enqueues them."""
     import torch
     st = torch.cuda.current_stream()
     fn()
+    gpu_head_start(1.0 * reps)  # the reps queue up behind it (short launches)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(st)
     for _ in range(reps):
