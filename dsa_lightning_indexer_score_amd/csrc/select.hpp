@@ -2,10 +2,10 @@
 // selection kernels and the decode indexer). Internal to libidxc.
 //
 // Input: n <= kSelMaxKeys order-preserving 32-bit keys skey[0..n) (16-byte
-// aligned) in increasing position order; pos_of(e) gives the position of entry e and is called only for the
-// winners. Output: the min(k, n) best entries under (key desc, position
-// asc), emitted in position order through emit(slot, key, position),
-// slot = 0..min(k,n)-1.
+// aligned) in increasing position order; pos_of(e) gives the position of
+// entry e and is called only for entries that may be kept. Output: the
+// min(k, n) best entries under (key desc, position asc), emitted in position
+// order through emit(slot, key, position), slot = 0..min(k,n)-1.
 //
 // Method: the keys lie in [lo, hi]; each pass histograms them into at most
 // kSelBins bins of one power-of-two width (the smallest that covers the range,
