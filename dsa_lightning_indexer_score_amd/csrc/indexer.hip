@@ -183,6 +183,8 @@ __device__ void wave_compact(u32x2* __restrict__ buf, int& n, int k, uint32_t& t
 // ---------------------------------------------------------------------------
 constexpr int kSampleTiles = 16;  // at most
 constexpr int kSampleKeys = kSampleTiles * kKeyTile;
+// a wave's sample area doubles as the histogram of its compactions
+static_assert(kSampleKeys >= kCompactBins, "compaction histogram fits the sample area");
 // The survivor count of a threshold set at about kSampleHits sampled hits has
 // a relative spread of about 1/sqrt(kSampleHits) = 10%: a row falls short of k
 // (and its workgroup sweeps again) beyond (1 - 1/slack) / 0.1 standard
