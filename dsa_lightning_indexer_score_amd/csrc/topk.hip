@@ -133,13 +133,115 @@ __device__ __forceinline__ void sort2048_regs(uint64_t (&v)[8], uint64_t* lds, i
   }
 }
 
+// Score order by bucket ranks. The kk winners' 64-bit words (key, ~position)
+// sit in sortbuf in position order, and their keys span [wlo, whi]; split
+// that range into kSelBins buckets of one power-of-two width. A winner's rank
+// is the number of winners in higher buckets plus the number of larger words
+// in its own bucket (words are distinct: positions are). `scratch` (8 KB of
+// LDS) takes the packed 16-bit bucket cursors, then the buckets' members as
+// 16-bit slots. Returns false, having written no output, when a bucket holds
+// more than kMaxBucket winners (scores bunched on few values, or spread over
+// many binades): the caller then sorts.
+constexpr int kMaxBucket = 64;
+constexpr int kBucketScratchBytes = kSelBins / 2 * 4 + kMaxK * 2;
+
+template <int NT>
+__device__ bool bucket_rank_output(uint64_t* sortbuf, int kk, int k, uint32_t wlo,
+                                   uint32_t whi, uint32_t* scratch, SelectSmemT<NT>& sm,
+                                   int32_t* orow) {
+  constexpr int BPT = kSelBins / NT;  // buckets per thread
+  const int tid = threadIdx.x;
+  uint32_t* cur = scratch;  // kSelBins / 2 words, bucket b in half b % 2 of word b / 2
+  uint16_t* mem = reinterpret_cast<uint16_t*>(scratch + kSelBins / 2);
+  const int shift = max(0, (32 - __clz((int)(whi - wlo))) - kSelBinsLog2);
+  auto bucket_of = [&](uint64_t w) { return ((uint32_t)(w >> 32) - wlo) >> shift; };
+  for (int b = tid; b < kSelBins / 2; b += NT) cur[b] = 0u;
+  __syncthreads();
+  for (int sl = tid; sl < kk; sl += NT) {
+    const uint32_t b = bucket_of(sortbuf[sl]);
+    atomicAdd(&cur[b >> 1], 1u << ((b & 1u) << 4));
+  }
+  __syncthreads();
+  // bucket starts in descending bucket order: thread tid owns buckets
+  // top - q, q = 0..BPT-1 (top is odd: buckets top - q and top - q - 1 share
+  // a word for even q)
+  const int top = kSelBins - 1 - BPT * tid;
+  int cnts[BPT];
+  int local = 0;
+  uint32_t most = 0u, unused = 0xFFFFFFFFu;
+#pragma unroll
+  for (int q = 0; q < BPT; q += 2) {
+    const uint32_t w = cur[(top - q) >> 1];
+    cnts[q] = (int)(w >> 16);
+    cnts[q + 1] = (int)(w & 0xFFFFu);
+    local += cnts[q] + cnts[q + 1];
+    most = max(most, max(w >> 16, w & 0xFFFFu));
+  }
+  int total;
+  const int excl = sel_excl_scan<NT>(local, sm.scan, &total);
+  wave_minmax(unused, most);
+  if (lane_id() == 0) sm.kred[tid / kWave] = most;
+  __syncthreads();
+  uint32_t bmax = 0u;
+#pragma unroll
+  for (int w = 0; w < NT / kWave; ++w) bmax = max(bmax, sm.kred[w]);
+  if (bmax > (uint32_t)kMaxBucket) return false;  // block-uniform
+  int acc = excl;
+#pragma unroll
+  for (int q = 0; q < BPT; q += 2) {
+    const uint32_t start_hi = (uint32_t)acc;
+    acc += cnts[q];
+    cur[(top - q) >> 1] = (start_hi << 16) | (uint32_t)acc;
+    acc += cnts[q + 1];
+  }
+  __syncthreads();
+  for (int sl = tid; sl < kk; sl += NT) {
+    const uint32_t b = bucket_of(sortbuf[sl]);
+    const uint32_t sh = (b & 1u) << 4;
+    const uint32_t old = atomicAdd(&cur[b >> 1], 1u << sh);
+    mem[(old >> sh) & 0xFFFFu] = (uint16_t)sl;
+  }
+  __syncthreads();
+  // each cursor now holds its bucket's end; bucket b starts where bucket b+1
+  // (the next higher one) ends
+  auto end_of = [&](uint32_t b) { return (cur[b >> 1] >> ((b & 1u) << 4)) & 0xFFFFu; };
+  constexpr int EPT = kMaxK / NT;  // winners per thread at most
+  uint32_t rk[EPT], pv[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int sl = tid + i * NT;
+    rk[i] = 0u;
+    pv[i] = 0u;
+    if (sl < kk) {
+      const uint64_t w = sortbuf[sl];
+      const uint32_t b = bucket_of(w);
+      const uint32_t e = end_of(b);
+      const uint32_t st = b + 1 < (uint32_t)kSelBins ? end_of(b + 1) : 0u;
+      uint32_t rank = st;
+      for (uint32_t j = st; j < e; ++j) rank += sortbuf[mem[j]] > w ? 1u : 0u;
+      rk[i] = rank;
+      pv[i] = ~(uint32_t)(w & 0xFFFFFFFFull);
+    }
+  }
+  // the row in rank order through LDS (over the words, all read by now), so
+  // that it is written with coalesced stores
+  __syncthreads();
+  uint32_t* obuf = reinterpret_cast<uint32_t*>(sortbuf);
+#pragma unroll
+  for (int i = 0; i < EPT; ++i)
+    if (tid + i * NT < kk) obuf[rk[i]] = pv[i];
+  __syncthreads();
+  for (int j = tid; j < k; j += NT) orow[j] = j < kk ? (int32_t)obuf[j] : -1;
+  return true;
+}
+
 // One workgroup = one (row, chunk). SRC kSrcRow: positions [c0, c1) of a score
 // row. SRC kSrcCand: the concatenation of nseg segments of a row (positions
 // staged too). SRC kSrcCand1: one segment (positions read back for winners).
 // The staged input starts at byte stage_off of the dynamic LDS.
 template <int SRC, int OUT, int NT>
 __global__ __launch_bounds__(NT)
-void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int stage_off) {
+void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int stage_off, int stage_bytes) {
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   Smem<NT>& sm = *reinterpret_cast<Smem<NT>*>(dyn);
   uint32_t* skey = reinterpret_cast<uint32_t*>(dyn + stage_off);
@@ -306,11 +408,18 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int stage_off) {
     if (SRC == kSrcCand) return spos[e];
     return cand1[e].y;
   };
+  uint32_t wmin = 0xFFFFFFFFu, wmax = 0u;  // score order: this thread's winners' key range
   const int kk = block_topk_collect<NT>(
       skey, n, k, sm.sel, pos_of, [&](int slot, uint32_t key, uint32_t pos) {
-        if (OUT == kOutPart) part[slot] = u32x2{key, pos};
-        else if (pos_order) orow[slot] = (int32_t)pos;
-        else sortbuf[slot] = (((uint64_t)key) << 32) | (uint64_t)(~pos);
+        if (OUT == kOutPart) {
+          part[slot] = u32x2{key, pos};
+        } else if (pos_order) {
+          orow[slot] = (int32_t)pos;
+        } else {
+          sortbuf[slot] = (((uint64_t)key) << 32) | (uint64_t)(~pos);
+          wmin = min(wmin, key);
+          wmax = max(wmax, key);
+        }
       },
       /*range_ready=*/true);
   if (OUT == kOutPart) {
@@ -322,7 +431,22 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int stage_off) {
     return;
   }
 
-  // ---- bitonic sort, descending, of the kk winners padded to a power of two
+  // ---- score order. Wide workgroups (the final stage of long rows) rank by
+  // buckets when the scores are spread out, with every wave busy (the staged
+  // keys are no longer read, so their LDS is the scratch); otherwise, and in
+  // 256-thread workgroups, where it measured faster, a bitonic sort,
+  // descending, of the kk winners padded to a power of two.
+  if (NT > kThreads && kk >= 512 && stage_bytes >= kBucketScratchBytes) {
+    sel_store_key_range<NT>(wmin, wmax, sm.sel);
+    __syncthreads();
+    uint32_t wlo = sm.sel.kred[0], whi = sm.sel.kred[NT / kWave];
+#pragma unroll
+    for (int w = 1; w < NT / kWave; ++w) {
+      wlo = min(wlo, sm.sel.kred[w]);
+      whi = max(whi, sm.sel.kred[NT / kWave + w]);
+    }
+    if (bucket_rank_output<NT>(sortbuf, kk, k, wlo, whi, skey, sm.sel, orow)) return;
+  }
   int P = 1;
   while (P < kk) P <<= 1;
   static_assert(kMaxK == 8 * kThreads && NT % kThreads == 0, "register sort layout");
@@ -387,7 +511,7 @@ hipError_t launch_one(const TopkArgs& a, int chunk_len, int nchunks, size_t stag
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(fn, dim3((unsigned)(a.rows * nchunks)), dim3(NT), shmem, st, a,
-                     chunk_len, nchunks, (int)stage_off);
+                     chunk_len, nchunks, (int)stage_off, (int)stage_bytes);
   return hipGetLastError();
 }
 

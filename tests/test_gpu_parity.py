@@ -115,7 +115,9 @@ def test_topk_exact(kind, B, Lq, Lk, q_pos0, k):
 
 
 def _extreme_rows(kind, B, Lq, Lk, seed=11):
-    """Score rows at the edges of the selection's key handling."""
+    """Score rows at the edges of the selection's key handling (and of the
+    score-order bucket ranks: one bucket for everything, few values, ties
+    within buckets, scores spread over many binades)."""
     rng = np.random.default_rng(seed)
     if kind == "equal":  # every key in one histogram bin
         s = np.full((B, Lq, Lk), 0.75, np.float32)
@@ -124,18 +126,23 @@ def _extreme_rows(kind, B, Lq, Lk, seed=11):
         vals = np.array([big, -big, np.inf, -np.inf, 0.0, -0.0, 1e-38, -1e-45, 3.0, -3.0],
                         np.float32)
         s = rng.choice(vals, size=(B, Lq, Lk)).astype(np.float32)
+    elif kind == "logspread":  # magnitudes over 40 binades, both signs
+        mag = np.exp2(rng.uniform(-30.0, 10.0, size=(B, Lq, Lk)))
+        sign = np.where(rng.random((B, Lq, Lk)) < 0.3, -1.0, 1.0)
+        s = (sign * mag).astype(np.float32)
     else:  # "ulps": a key range narrower than one pass's bins (1 + i ulp)
         i = rng.integers(0, 1500, size=(B, Lq, Lk)).astype(np.float32)
         s = (np.float32(1.0) + i * np.float32(2.0 ** -23)).astype(np.float32)
     return torch.from_numpy(s)
 
 
-@pytest.mark.parametrize("kind", ["equal", "extremes", "ulps"])
+@pytest.mark.parametrize("kind", ["equal", "extremes", "ulps", "logspread"])
 @pytest.mark.parametrize("B,Lq,Lk,q_pos0,k", [
     (1, 40, 8192, 8152, 2048),     # one workgroup per row, register sort
     (1, 3, 16384, 16381, 2048),    # two stages, 1024-thread final selection
     (2, 2, 12000, 11998, 300),     # two stages, sort of 300 padded to 512
     (1, 70, 3001, 2931, 1024),     # odd row length: 16-byte staging plus a tail
+    (2, 1, 40000, 39999, 2048),    # decode-shaped rows: the final stage ranks by buckets
 ])
 def test_topk_extreme_key_ranges_exact(kind, B, Lq, Lk, q_pos0, k):
     _say("topk extremes %s B=%d Lq=%d Lk=%d q_pos0=%d k=%d" % (kind, B, Lq, Lk, q_pos0, k))
