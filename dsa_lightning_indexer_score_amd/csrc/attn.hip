@@ -60,6 +60,76 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp));
 }
 
+// Online softmax of one 32-key block in the exp2 domain with a lazily moved
+// maximum, then O^T += V^T . P^T with V^T read through transposing LDS reads
+// of the block's V rows at vl. s holds this lane's 16 raw scores (keys
+// acc_row(i, lane) of the block, one head), vmask the block's valid keys. The
+// scale (> 0) commutes with the maximum, so the raw scores' maximum is scaled
+// once and each exponent is one fma, s * sl2 - m.
+template <int D>
+__device__ __forceinline__ void attend_block(const f32x16& s, uint32_t vmask, const uint8_t* vl,
+                                             int vt_lane, float sl2, float& m_used, float& lsum,
+                                             f32x16 (&o)[D / 32]) {
+  using BL = Blk<D>;
+  constexpr int DB = D / 32;
+  const int lane = lane_id();
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = s[i];
+  if (__builtin_expect(vmask != 0xFFFFFFFFu, 0)) {  // wave-uniform: padded entries
+    // key of x[i] = acc_row(i, lane) = 4(l/32) + 8(i/4) + i%4
+    const uint32_t vml = vmask >> (4 * (lane >> 5));
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (!((vml >> (8 * (i >> 2) + (i & 3))) & 1u)) x[i] = -INFINITY;
+  }
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, x[i]);
+  const float mblk = pair_max(mloc) * sl2;
+  const bool move = mblk > m_used + kLazyLog2;
+  if (ballot(move)) {
+    const float mnew = move ? mblk : m_used;
+    const float alpha = move ? __builtin_amdgcn_exp2f(m_used - mnew) : 1.0f;  // 2^-inf = 0
+    lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    m_used = mnew;
+  }
+  // x * sl2 - m_used <= 8 keeps P <= 256; -inf maps to 0. The row sum
+  // accumulates the bf16-rounded weights that the P.V product uses
+  // (two-way dot products with 1), in two chains.
+  const float mu = (m_used == -INFINITY) ? 0.0f : m_used;
+  u32x4 pw[2];
+  float psum0 = 0.0f, psum1 = 0.0f;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(x[i], sl2, -mu));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(x[i + 1], sl2, -mu));
+    const uint32_t pk = pack_bf16x2(p0, p1);
+    pw[i >> 3][(i & 7) >> 1] = pk;
+    const bf16x2 pb2 = __builtin_bit_cast(bf16x2, pk);
+    if (i & 2) psum1 = __builtin_amdgcn_fdot2_f32_bf16(pb2, ones, psum1, false);
+    else psum0 = __builtin_amdgcn_fdot2_f32_bf16(pb2, ones, psum0, false);
+  }
+  lsum += psum0 + psum1;
+  // ---- O^T += V^T . P^T; P^T's k index 8(l/32) + jj is key
+  // 16kk + 8(jj/4) + 4(l/32) + jj%4, which the transposed reads match
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kk]);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const uint8_t* p0 = vl + vt_lane + 16 * kk * BL::SV + 64 * db;
+      const u32x2 lo = lds_read_tr16(p0);
+      const u32x2 hi = lds_read_tr16(p0 + 8 * BL::SV);
+      const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+      o[db] = mfma32(va, pb, o[db]);
+    }
+  }
+}
+
 template <int D, int HB>
 __global__ __launch_bounds__(kAttnWaves * kWave, (D == 128 && HB == 1) ? 1 : 2)
 void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kmat,
@@ -230,64 +300,7 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     off_prev = on;
     const f32x16 s_nxt = qk(j + 1);  // past the last block: masked rows
 
-    // ---- online softmax of block j in the exp2 domain with a lazily moved
-    // maximum. The scale (> 0) commutes with the maximum, so the raw scores'
-    // maximum is scaled once and each exponent is one fma, s * sl2 - m.
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = s_cur[i];
-    if (__builtin_expect(vm0 != 0xFFFFFFFFu, 0)) {  // wave-uniform: padded entries
-      // key of x[i] = acc_row(i, lane) = 4(l/32) + 8(i/4) + i%4
-      const uint32_t vml = vm0 >> (4 * (lane >> 5));
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (!((vml >> (8 * (i >> 2) + (i & 3))) & 1u)) x[i] = -INFINITY;
-    }
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, x[i]);
-    const float mblk = pair_max(mloc) * sl2;
-    const bool move = mblk > m_used + kLazyLog2;
-    if (ballot(move)) {
-      const float mnew = move ? mblk : m_used;
-      const float alpha = move ? __builtin_amdgcn_exp2f(m_used - mnew) : 1.0f;  // 2^-inf = 0
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-      m_used = mnew;
-    }
-    // x * sl2 - m_used <= 8 keeps P <= 256; -inf maps to 0. The row sum
-    // accumulates the bf16-rounded weights that the P.V product uses
-    // (two-way dot products with 1), in two chains.
-    const float mu = (m_used == -INFINITY) ? 0.0f : m_used;
-    u32x4 pw[2];
-    float psum0 = 0.0f, psum1 = 0.0f;
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(x[i], sl2, -mu));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(x[i + 1], sl2, -mu));
-      const uint32_t pk = pack_bf16x2(p0, p1);
-      pw[i >> 3][(i & 7) >> 1] = pk;
-      if (i & 2) psum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, psum1, false);
-      else psum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, psum0, false);
-    }
-    lsum += psum0 + psum1;
-    // ---- O^T += V^T . P^T; P^T's k index 8(l/32) + jj is key
-    // 16kk + 8(jj/4) + 4(l/32) + jj%4, which the transposed reads match
-    const uint8_t* vl = vbuf(j);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[kk]);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const uint8_t* p0 = vl + vt_lane + 16 * kk * BL::SV + 64 * db;
-        const u32x2 lo = lds_read_tr16(p0);
-        const u32x2 hi = lds_read_tr16(p0 + 8 * BL::SV);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-        o[db] = mfma32(va, pb, o[db]);
-      }
-    }
+    attend_block<D>(s_cur, vm0, vbuf(j), vt_lane, sl2, m_used, lsum, o);
     // ---- stage K(j+2) over K(j) and V(j+1) over V(j-1) (past the last
     // block: buffers nobody reads)
     stage_k(k_near, j);
