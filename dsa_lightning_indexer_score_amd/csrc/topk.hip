@@ -9,9 +9,10 @@
 // LDS once (loads batched so many are in flight), selects the exact top-k in
 // position order (select.hpp: range-narrowing radix select plus an ordered
 // pass), and a bitonic sort of 64-bit (key, ~position) words puts the k
-// winners in score order; the index cache of a layer stack keeps them in
-// position order instead (gathers then sweep the keys in order), which needs
-// no sort.
+// winners in score order (in the wide final stage of long rows, ranks from key
+// buckets when the scores are spread out); the index cache of a layer stack
+// keeps them in position order instead (gathers then sweep the keys in
+// order), which needs no sort.
 //
 // Inputs: a materialised score row (positions implicit), or candidate lists of
 // (order key, position) pairs in increasing position order, possibly split in
