@@ -101,6 +101,7 @@ def test_indexer_scores_split_path_integer_exact():
     ("normal", 3, 1, 30000, 29999, 2048),   # decode-shaped rows (two-stage)
     ("ties", 2, 1, 65536, 65535, 2048),     # longest two-stage rows, heavy ties
     ("normal", 1, 3, 40000, 39997, 300),    # many chunks, small k
+    ("normal", 2, 2, 20000, 19998, 100),    # two stages, final sort in LDS (k < 257)
     ("normal", 1, 20, 20, 0, 2048),         # every row shorter than k
 ])
 def test_topk_exact(kind, B, Lq, Lk, q_pos0, k):
