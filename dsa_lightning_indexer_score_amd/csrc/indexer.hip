@@ -695,7 +695,11 @@ void indexer_split_topk_kernel(const uint16_t* __restrict__ q_idx,
 
   u32x2* seg = part + row * (size_t)nchunks * k + (size_t)chunk * k;
   const int kk = block_topk_collect<kDecWaves * kWave>(
-      skey, n, k, sel, [&](int e) { return c0 + e; },
+      skey, n, k, sel,
+      [&](int e0, unsigned, uint32_t (&pv)[kSelPerThread]) {
+#pragma unroll
+        for (int j = 0; j < kSelPerThread; ++j) pv[j] = (uint32_t)(c0 + e0 + j);
+      },
       [&](int slot, uint32_t key, uint32_t pos) { seg[slot] = u32x2{key, pos}; },
       /*range_ready=*/true);
   if (threadIdx.x == 0) part_count[row * nchunks + chunk] = kk;

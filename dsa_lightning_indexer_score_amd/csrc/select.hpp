@@ -2,10 +2,12 @@
 // selection kernels and the decode indexer). Internal to libidxc.
 //
 // Input: n <= kSelMaxKeys order-preserving 32-bit keys skey[0..n) (16-byte
-// aligned) in increasing position order; pos_of(e) gives the position of
-// entry e and is called only for entries that may be kept. Output: the
-// min(k, n) best entries under (key desc, position asc), emitted in position
-// order through emit(slot, key, position), slot = 0..min(k,n)-1.
+// aligned) in increasing position order; pos_group(e0, bits, pv) fills pv[j]
+// with the position of entry e0 + j for every set bit j of `bits` (entries
+// that may be kept; e0 is a multiple of kSelPerThread and e0 + j < n for
+// those). Output: the min(k, n) best entries under (key desc, position asc),
+// emitted in position order through emit(slot, key, position),
+// slot = 0..min(k,n)-1.
 //
 // Method: the keys lie in [lo, hi]; each pass histograms them into at most
 // kSelBins bins of one power-of-two width (the smallest that covers the range,
@@ -75,9 +77,9 @@ __device__ __forceinline__ void sel_store_key_range(uint32_t kmin, uint32_t kmax
   }
 }
 
-template <int NT = kSelThreads, typename PosOf, typename Emit>
+template <int NT = kSelThreads, typename PosGroup, typename Emit>
 __device__ int block_topk_collect(const uint32_t* skey, int n, int k, SelectSmemT<NT>& sm,
-                                  PosOf pos_of, Emit emit, bool range_ready = false) {
+                                  PosGroup pos_group, Emit emit, bool range_ready = false) {
   constexpr int kSelThreads = NT;
   constexpr int kSelWaves = NT / kWave;
   constexpr int kSelChunk = NT * kSelPerThread;
@@ -216,12 +218,9 @@ __device__ int block_topk_collect(const uint32_t* skey, int n, int k, SelectSmem
       }
     }
     // positions of the entries that may be kept, fetched before the prefix
-    // sums so that a pos_of that reads memory overlaps them
+    // sums so that a pos_group that reads memory overlaps them
     uint32_t pv[kSelPerThread];
-    const unsigned cand_bits = gt_bits | eq_bits;
-#pragma unroll
-    for (int j = 0; j < kSelPerThread; ++j)
-      pv[j] = ((cand_bits >> j) & 1u) ? (uint32_t)pos_of(e0 + j) : 0u;
+    pos_group(e0, gt_bits | eq_bits, pv);
     // entries equal to the threshold key exist only after a selection that
     // ended on a single key (a block-uniform condition)
     int eq_total = 0, eq_excl = eq_seen;

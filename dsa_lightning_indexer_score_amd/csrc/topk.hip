@@ -404,14 +404,33 @@ void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int stage_off, int stag
   int32_t* orow = a.out + (size_t)row * k;
   const bool pos_order = OUT == kOutFinal && a.pos_order;
   const u32x2* cand1 = (SRC == kSrcCand1) ? a.cand + (size_t)row * a.seg_cap : nullptr;
-  auto pos_of = [&](int e) -> uint32_t {
-    if (SRC == kSrcRow) return (uint32_t)(pos0 + e);
-    if (SRC == kSrcCand) return spos[e];
-    return cand1[e].y;
+  // positions of a group of kSelPerThread consecutive entries (those of `bits`)
+  const bool cand1_aligned =
+      SRC == kSrcCand1 && (reinterpret_cast<uintptr_t>(cand1) & 15) == 0;
+  auto pos_group = [&](int e0, unsigned bits, uint32_t (&pv)[kSelPerThread]) {
+    if (SRC == kSrcRow) {
+#pragma unroll
+      for (int j = 0; j < kSelPerThread; ++j) pv[j] = (uint32_t)(pos0 + e0 + j);
+    } else if (SRC == kSrcCand) {
+#pragma unroll
+      for (int j = 0; j < kSelPerThread; ++j) pv[j] = ((bits >> j) & 1u) ? spos[e0 + j] : 0u;
+    } else if (cand1_aligned && bits != 0u && e0 + kSelPerThread <= n) {
+      // the group's pairs in four 16-byte loads (positions are the odd words)
+      const u32x4* g = reinterpret_cast<const u32x4*>(cand1 + e0);
+#pragma unroll
+      for (int q = 0; q < kSelPerThread / 2; ++q) {
+        const u32x4 w = g[q];
+        pv[2 * q] = w[1];
+        pv[2 * q + 1] = w[3];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSelPerThread; ++j) pv[j] = ((bits >> j) & 1u) ? cand1[e0 + j].y : 0u;
+    }
   };
   uint32_t wmin = 0xFFFFFFFFu, wmax = 0u;  // score order: this thread's winners' key range
   const int kk = block_topk_collect<NT>(
-      skey, n, k, sm.sel, pos_of, [&](int slot, uint32_t key, uint32_t pos) {
+      skey, n, k, sm.sel, pos_group, [&](int slot, uint32_t key, uint32_t pos) {
         if (OUT == kOutPart) {
           part[slot] = u32x2{key, pos};
         } else if (pos_order) {
