@@ -762,6 +762,30 @@ def test_full_size_prefill_layer_sampled_rows():
     assert err <= ATOL
 
 
+@pytest.mark.parametrize("B,Lq,Lk,q_pos0,rows", [
+    (1, 8192, 8192, 0, [0, 1, 511, 512, 2046, 2047, 2048, 4095, 6000, 8191]),  # single-layer rows
+    (64, 1, 65536, 65535, [0, 17, 40, 63]),  # decode rows: two stages, the final one ranks by buckets
+])
+def test_full_size_standalone_topk_sampled_rows(B, Lq, Lk, q_pos0, rows):
+    """idxc_topk at the benchmark's shapes and launch configuration, in both
+    orders; sampled rows against the oracle on the same fp32 scores."""
+    _say("full size standalone top-k B=%d Lq=%d Lk=%d" % (B, Lq, Lk))
+    k = 2048
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    s = torch.randn((B, Lq, Lk), generator=g, device="cuda")
+    got = idxc.idxc_topk(s, k, q_pos0=q_pos0)
+    got_pos = idxc.idxc_topk(s, k, q_pos0=q_pos0, order="position")
+    torch.cuda.synchronize()
+    for r in rows:
+        b, i = (r, 0) if Lq == 1 else (0, r)
+        want = oracle.topk(s[b:b + 1, i:i + 1].cpu().numpy(), k, q_pos0 + i)
+        assert np.array_equal(got[b, i].cpu().numpy(), want[0, 0]), "score order, row %d" % r
+        assert np.array_equal(got_pos[b, i].cpu().numpy(), oracle.position_order(want)[0, 0]), \
+            "position order, row %d" % r
+    del s
+
+
 def test_full_size_decode_layer_sampled_rows():
     cfg = gen.C4_12F   # 64 sequences x 65536 cached tokens, one query each
     _say("full size decode layer B=%d Lk=%d" % (cfg.B, cfg.Lk))
