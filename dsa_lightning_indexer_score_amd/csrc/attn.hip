@@ -253,6 +253,16 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
                                                          (ks * 2 + (lane >> 5)) * 16);
       s = mfma32(ka, qb[ks], s);
     }
+    // keep four K reads in flight ahead of the MFMA chain (the default
+    // schedule waits on each pair of reads): four reads, then MFMA and read
+    // alternating, then the last four MFMAs (1-2% faster per prefill layer)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 0x100: LDS reads
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 0x008: MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     return s;
   };
 
@@ -287,6 +297,9 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   int ix3 = raw_index(3), ix4 = raw_index(4);
   __syncthreads();
   f32x16 s_cur = qk(0);
+  // iteration 0 stages K(2) over K(0): every wave of the unit must have read
+  // K(0) first
+  __syncthreads();
 
   auto iteration = [&](int j, Rows& k_far, Rows& v_far, Rows& k_near, Rows& v_near) {
     // issued unconditionally (blocks past the end gather row 0, masked out):
