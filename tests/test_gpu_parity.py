@@ -839,3 +839,72 @@ def test_full_size_long_context_last_chunk_sampled_rows():
     want = _oracle_rows(q[:, rows].cpu(), kk.cpu(), w[:, rows].cpu(), [q_pos0 + r for r in rows],
                         k)
     _check_selection(got[0, rows].cpu().numpy(), want)
+
+
+# --------------------------------------------------------------------------- #
+# randomised shapes: each seed draws a shape, a k, a weight kind, an output
+# order and (for some seeds) per-row positions; integer inputs, so the indices
+# must equal the oracle's exactly
+# --------------------------------------------------------------------------- #
+def _random_case(seed):
+    r = np.random.default_rng(1000 + seed)
+    H_I, d_I = [(4, 32), (64, 128)][int(r.integers(0, 2))]
+    B = int(r.integers(1, 3))
+    Lk = int(r.choice([5, 130, 1000, 2049, 8191, 8193, 16384, 16385, 20000, 33000, 40000]))
+    Lq = int(min(Lk, r.choice([1, 2, 3, 8, 9, 33, 64])))
+    if Lq * Lk * H_I * B > 4e7:
+        Lq = max(1, int(4e7 // (Lk * H_I * B)))
+    q0 = int(r.integers(0, Lk - Lq + 1))
+    k = int(r.choice([1, 16, 100, 256, 1000, 2048]))
+    wk = str(r.choice(["quarter", "neg-quarter"]))
+    order = str(r.choice(["score", "position"]))
+    q_pos = (r.integers(-2, Lk + 3, size=(B, Lq)).astype(np.int32)
+             if r.random() < 0.4 else None)
+    return B, Lq, Lk, q0, H_I, d_I, k, wk, order, q_pos
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_indexer_topk_random_shapes_integer_exact(seed):
+    B, Lq, Lk, q0, H_I, d_I, k, wk, order, q_pos = _random_case(seed)
+    _say("indexer_topk random seed=%d B=%d Lq=%d Lk=%d q0=%d H_I=%d k=%d order=%s ragged=%s"
+         % (seed, B, Lq, Lk, q0, H_I, k, order, q_pos is not None))
+    q, kk, w = gen.indexer_inputs(B, Lq, Lk, H_I, d_I, kind="int", seed=500 + seed, w_kind=wk)
+    if q_pos is None:
+        got = idxc.idxc_indexer_topk(cu(q), cu(kk), cu(w), k, q_pos0=q0, order=order)
+        sc = oracle.indexer_scores(f64(q), f64(kk), f64(w), q0)
+        want = oracle.topk(sc, k, q0)
+    else:
+        got = idxc.idxc_indexer_topk_ragged(cu(q), cu(kk), cu(w), k, cu(torch.from_numpy(q_pos)),
+                                            order=order)
+        want = _ragged_ref(q, kk, w, q_pos, k)
+    torch.cuda.synchronize()
+    if order == "position":
+        want = oracle.position_order(want)
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_topk_random_shapes_exact(seed):
+    r = np.random.default_rng(2000 + seed)
+    Lk = int(r.choice([37, 300, 2049, 8191, 8192, 8193, 12000, 16385, 33000]))
+    Lq = int(min(Lk, r.integers(1, 4) if Lk > 20000 else r.integers(1, 40)))
+    B = int(r.integers(1, 3))
+    q0 = int(r.integers(0, Lk - Lq + 1))
+    k = int(r.choice([1, 7, 64, 256, 300, 511, 512, 1000, 2047, 2048]))
+    nch = -(-Lk // 8192)
+    if nch > 1 and nch * k > 16384:  # beyond the two-stage selection
+        k = 16384 // nch
+    kind = str(r.choice(["normal", "ties", "logspread", "ulps", "extremes"]))
+    if kind == "normal":
+        s = torch.from_numpy(r.standard_normal((B, Lq, Lk)).astype(np.float32))
+    elif kind == "ties":
+        s = torch.from_numpy(r.integers(-3, 4, size=(B, Lq, Lk)).astype(np.float32))
+    else:
+        s = _extreme_rows(kind, B, Lq, Lk, seed=seed)
+    _say("topk random seed=%d %s B=%d Lq=%d Lk=%d q0=%d k=%d" % (seed, kind, B, Lq, Lk, q0, k))
+    want = oracle.topk(s.numpy(), k, q0)
+    for order in ("score", "position"):
+        got = idxc.idxc_topk(cu(s), k, q_pos0=q0, order=order)
+        torch.cuda.synchronize()
+        exp = want if order == "score" else oracle.position_order(want)
+        assert np.array_equal(got.cpu().numpy(), exp)
