@@ -908,3 +908,31 @@ def test_topk_random_shapes_exact(seed):
         torch.cuda.synchronize()
         exp = want if order == "score" else oracle.position_order(want)
         assert np.array_equal(got.cpu().numpy(), exp)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_sparse_attn_random_shapes(seed):
+    # head counts off the 32-head blocks, both head dims, list lengths off the
+    # 32-key blocks, padding, and the split (few rows) and single-pass paths
+    r = np.random.default_rng(3000 + seed)
+    H = int(r.choice([1, 5, 32, 33, 40, 64]))
+    D = int(r.choice([64, 128]))
+    B = int(r.integers(1, 4))
+    Lk = int(r.choice([40, 700, 3000, 9000]))
+    Lq = int(min(Lk, r.choice([1, 2, 7, 64, 300])))
+    q0 = int(r.integers(0, Lk - Lq + 1))
+    k = int(r.choice([1, 31, 33, 100, 257, 1000, 2048]))
+    pad = float(r.choice([0.0, 0.0, 0.3, 0.9]))
+    ws = str(r.choice(["auto", "none"]))
+    _say("sparse_attn random seed=%d B=%d Lq=%d Lk=%d q0=%d H=%d D=%d k=%d pad=%.1f ws=%s"
+         % (seed, B, Lq, Lk, q0, H, D, k, pad, ws))
+    Q, K, V = gen.attn_inputs(B, Lq, Lk, H, D, seed=700 + seed)
+    idx = gen.index_sets(B, Lq, q0, k, seed=800 + seed, pad_frac=pad)
+    scale = D ** -0.5
+    got = idxc.idxc_sparse_attn(cu(Q), cu(K), cu(V), cu(idx), scale,
+                                workspace="auto" if ws == "auto" else None)
+    torch.cuda.synchronize()
+    want = oracle.sparse_attention(f64(Q), f64(K), f64(V), idx.numpy(), scale)
+    err = np.abs(got.float().cpu().numpy() - want).max()
+    _say("max abs err %.3e" % err)
+    assert err <= ATOL
