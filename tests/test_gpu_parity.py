@@ -936,3 +936,38 @@ def test_sparse_attn_random_shapes(seed):
     err = np.abs(got.float().cpu().numpy() - want).max()
     _say("max abs err %.3e" % err)
     assert err <= ATOL
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_stack_random_patterns_exact(seed):
+    # random F/S patterns (first layer F): one indexer call per F layer, each
+    # layer's cache equal to the oracle's set of the nearest F layer at or
+    # before it, attention within tolerance, the final cache = the last F's
+    import dataclasses
+    r = np.random.default_rng(4000 + seed)
+    n = int(r.integers(1, 10))
+    pattern = "F" + "".join(r.choice(["F", "S"], size=n - 1))
+    B = int(r.integers(1, 3))
+    L = int(r.choice([256, 600]))
+    k = int(r.choice([16, 100, 300]))
+    cfg = dataclasses.replace(gen.C1, name="rand%d" % seed, n_layers=n, pattern=pattern, B=B,
+                              Lq=L, Lk=L, q_pos0=0, k=k)
+    _say("stack random pattern=%s B=%d L=%d k=%d" % (pattern, B, L, k))
+    layers = _layers(cfg)
+    dev_layers = [{nm: cu(t) for nm, t in Ly.items()} for Ly in layers]
+    res = idxc.idxc_layer_stack_forward(pattern, dev_layers, k, cfg.scale, q_pos0=0,
+                                        debug_indices=True)
+    torch.cuda.synchronize()
+    ref = oracle.layer_stack(pattern, [{nm: f64(t) for nm, t in Ly.items()} for Ly in layers],
+                             k, cfg.scale, 0)
+    assert res["indexer_calls"] == ref["calls"] == pattern.count("F")
+    dbg = res["debug_indices"].cpu().numpy()
+    last_f = 0
+    for l in range(n):
+        if pattern[l] == "F":
+            last_f = l
+        assert np.array_equal(dbg[l], oracle.position_order(ref["indices"][l])), l
+        assert np.array_equal(dbg[l], dbg[last_f]), l
+        err = np.abs(res["out"][l].float().cpu().numpy() - ref["out"][l]).max()
+        assert err <= ATOL, (l, err)
+    assert np.array_equal(res["index_cache"].cpu().numpy(), dbg[last_f])
