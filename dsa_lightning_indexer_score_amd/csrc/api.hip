@@ -44,6 +44,11 @@ int hip_status(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The attention kernels take the softmax maximum over unscaled scores and
+// scale it afterwards, and mask padding with -inf before scaling: both need
+// a finite scale > 0.
+bool scale_ok(float scale) { return scale > 0.0f && scale <= 3.4028234663852886e38f; }
+
 #define REQUIRE_PTR(p, name)                                                          \
   do {                                                                                \
     if ((p) == nullptr) return fail(IDXC_ERR_INVALID_ARG, "%s is NULL", name);         \
@@ -98,9 +103,9 @@ int check_pattern(const char* pattern, int32_t n_layers, int32_t* n_full) {
   for (int l = 0; l < n_layers; ++l) {
     const char c = pattern[l];
     if (c == 'F') ++nf;
-    else if (c != 'S') return fail(IDXC_ERR_PATTERN, "role '%c' at layer %d is not F or S", c, l);
+    else if (c != 'S') return fail(IDXC_ERR_PATTERN, "unknown role '%c' at layer %d (only F and S)", c, l);
   }
-  if (pattern[0] != 'F') return fail(IDXC_ERR_PATTERN, "the first layer must be F");
+  if (pattern[0] != 'F') return fail(IDXC_ERR_PATTERN, "layer 0 has no earlier F layer to share from: it must be F");
   if (n_full) *n_full = nf;
   return IDXC_OK;
 }
@@ -438,7 +443,7 @@ int idxc_sparse_attn(const void* q, const void* k, const void* v, const int32_t*
   REQUIRE_PTR(v, "v");
   REQUIRE_PTR(indices, "indices");
   REQUIRE_PTR(out, "out");
-  if (!(scale == scale)) return fail(IDXC_ERR_INVALID_ARG, "scale is NaN");
+  if (!scale_ok(scale)) return fail(IDXC_ERR_INVALID_ARG, "scale = %g: must be finite and > 0", (double)scale);
   void* ws = nullptr;
   if (workspace != nullptr) {
     if (!aligned16(workspace)) return fail(IDXC_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
@@ -592,7 +597,7 @@ static int stack_forward(const char* pattern, int32_t n_layers, const idxc_layer
   REQUIRE_PTR(workspace, "workspace");
   if (debug_indices != nullptr && !aligned16(debug_indices))
     return fail(IDXC_ERR_INVALID_ARG, "debug_indices is not 16-byte aligned");
-  if (!(scale == scale)) return fail(IDXC_ERR_INVALID_ARG, "scale is NaN");
+  if (!scale_ok(scale)) return fail(IDXC_ERR_INVALID_ARG, "scale = %g: must be finite and > 0", (double)scale);
   const Plan p = plan_for(dims, true);
   if (workspace_bytes < p.min_bytes)
     return fail(IDXC_ERR_INVALID_ARG, "workspace of %zu bytes is below the minimum %zu",

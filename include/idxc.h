@@ -161,6 +161,8 @@ int idxc_indexer_topk(const void* q_idx, const void* k_idx, const void* w,
  * in [0, Lk)) of scale * q[b,i,h,:] . k[b,s,:], then the weighted sum of
  * v[b,s,:], written to out[b,i,h,:] as bf16. A row with no valid entry gets
  * zeros. Uses B, Lq, Lk, H, D, k. fp32 softmax and accumulation, bf16 P.
+ * scale must be finite and > 0 (a NaN, infinite, zero or negative scale is
+ * IDXC_ERR_INVALID_ARG).
  * workspace (optional, NULL = none): with at least
  * idxc_sparse_attn_workspace_bytes() bytes, calls with few query rows split
  * each index list over several workgroups and merge the partial results. */
@@ -187,7 +189,8 @@ int idxc_sparse_attn_workspace_bytes(const idxc_dims* dims, size_t* bytes);
  * debug_indices, if not NULL, is a DEVICE buffer [n_layers, B, Lq, k] that
  * receives each layer's cache contents (for tests). workspace as for
  * idxc_indexer_topk, plus room for attention partials; idxc_workspace_bytes
- * with H and D set gives the full-speed size. */
+ * with H and D set gives the full-speed size. scale as for idxc_sparse_attn
+ * (finite and > 0). */
 int idxc_layer_stack_forward(const char* pattern, int32_t n_layers,
                              const idxc_layer* layers, const idxc_dims* dims,
                              float scale, int32_t* index_cache, void* workspace,

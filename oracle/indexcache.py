@@ -62,9 +62,9 @@ def validate_pattern(pattern: str, n_layers: int) -> None:
         raise ValueError("need at least one layer")
     for c in pattern:
         if c not in ("F", "S"):
-            raise ValueError("role must be F or S, got %r" % c)
+            raise ValueError("unknown layer role %r (only 'F' and 'S' exist)" % c)
     if pattern[0] != "F":
-        raise ValueError("the first layer must compute a full index")
+        raise ValueError("layer 0 has no earlier F layer to share from; it has to be 'F'")
 
 
 def nearest_full(pattern: str) -> List[int]:
@@ -196,30 +196,26 @@ def sparse_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray,
 
 
 # --------------------------------------------------------------------------- #
-# a5 + a7: index cache and the F/S layer loop  ([W] state machine "refresh ->
-#          share -> refresh"; [J] "IndexCache 方法": compute and cache on F,
-#          read the cache on S)
+# a5 + a7: index cache and the F/S layer loop  ([W] "从 DSA 的成本分解开始": an
+#          F layer's top-k replaces the single cached index tensor, an S layer
+#          reuses it; [J] "IndexCache 方法": the f(l) rule)
 # --------------------------------------------------------------------------- #
 def schedule(layer_scores: Sequence[np.ndarray], pattern: str, k: int,
              q_pos0: int) -> Tuple[List[np.ndarray], int]:
-    """Run the index-cache state machine over precomputed per-layer scores.
+    """Index sets of every layer of a stack from precomputed per-layer scores.
 
     layer_scores[l] is [B,Lq,Lk] fp32 (only F layers' entries are read).
-    Returns (selected per layer, indexer_calls). F: cache = topk(score_l),
-    calls += 1. S: reuse the cache. Every layer reports the cache it used.
+    By definition an F layer l selects I_l = TopK(s_l, k) and an S layer l
+    uses I_{f(l)}, f(l) the nearest earlier F layer ([J] "IndexCache 方法");
+    the indexer therefore runs once per F layer. Returns (I_l for every
+    layer, number of indexer evaluations).
     """
     validate_pattern(pattern, len(layer_scores))
-    cache = None
-    calls = 0
-    selected = []
-    for score, role in zip(layer_scores, pattern):
-        if role == "F":
-            cache = topk(np.asarray(score), k, q_pos0)
-            calls += 1
-        if cache is None:  # unreachable after validation; kept for clarity
-            raise ValueError("no cached indices available for a shared layer")
-        selected.append(cache.copy())
-    return selected, calls
+    src = nearest_full(pattern)
+    own = {l: topk(np.asarray(layer_scores[l]), k, q_pos0)
+           for l in range(len(pattern)) if pattern[l] == "F"}
+    selected = [own[src[l]].copy() for l in range(len(pattern))]
+    return selected, len(own)
 
 
 def layer_stack(pattern: str, layers: Sequence[Dict[str, np.ndarray]], k: int,
@@ -228,25 +224,23 @@ def layer_stack(pattern: str, layers: Sequence[Dict[str, np.ndarray]], k: int,
     """Full hot path over a stack: per layer {indexer + top-k if F} + attention.
 
     layers[l] holds fp64 arrays q_idx, k_idx, w (read on F layers only) and
-    q, k, v. Returns dict(indices=[per layer], out=[per layer], calls=int,
-    scores=[per F layer or None]).
+    q, k, v. Every layer attends over I_{src(l)}, src(l) = l on F layers and
+    f(l) on S layers. Returns dict(indices=[per layer], out=[per layer],
+    calls=int, scores=[per F layer or None]).
     """
     validate_pattern(pattern, len(layers))
-    cache = None
-    calls = 0
-    sel_all, out_all, scores_all = [], [], []
-    for l, role in enumerate(pattern):
-        L = layers[l]
-        if role == "F":
-            sc = indexer_scores(L["q_idx"], L["k_idx"], L["w"], q_pos0, Lk, q_pos)
-            cache = topk(sc, k, q_pos0, q_pos)
-            calls += 1
-            scores_all.append(sc)
-        else:
-            scores_all.append(None)
-        sel_all.append(cache.copy())
-        out_all.append(sparse_attention(L["q"], L["k"], L["v"], cache, scale))
-    return dict(indices=sel_all, out=out_all, calls=calls, scores=scores_all)
+    src = nearest_full(pattern)
+    scores_all: List[Optional[np.ndarray]] = [None] * len(pattern)
+    own: Dict[int, np.ndarray] = {}
+    for l in range(len(pattern)):
+        if pattern[l] == "F":
+            L = layers[l]
+            scores_all[l] = indexer_scores(L["q_idx"], L["k_idx"], L["w"], q_pos0, Lk, q_pos)
+            own[l] = topk(scores_all[l], k, q_pos0, q_pos)
+    sel_all = [own[src[l]].copy() for l in range(len(pattern))]
+    out_all = [sparse_attention(layers[l]["q"], layers[l]["k"], layers[l]["v"], sel_all[l],
+                                scale) for l in range(len(pattern))]
+    return dict(indices=sel_all, out=out_all, calls=len(own), scores=scores_all)
 
 
 # --------------------------------------------------------------------------- #

@@ -122,7 +122,9 @@ def test_sparse_attn_argument_errors(lib):
     for bad, code in ((dict(D=96), 3), (dict(H=65), 3), (dict(k=0), 1), (dict(B=0), 1)):
         assert f(P(), P(), P(), P(), ctypes.byref(_dims(**bad)), 0.125, None, 0, P(), None) == code
     assert f(P(), None, P(), P(), ctypes.byref(_dims()), 0.125, None, 0, P(), None) == 1
-    assert f(P(), P(), P(), P(), ctypes.byref(_dims()), float("nan"), None, 0, P(), None) == 1
+    for bad_scale in (float("nan"), float("inf"), float("-inf"), 0.0, -0.0, -0.125):
+        assert f(P(), P(), P(), P(), ctypes.byref(_dims()), bad_scale, None, 0, P(), None) == 1
+        assert "scale" in lib.idxc_last_error().decode()
     # few rows: a split needs a workspace; a short one is rejected
     dec = _dims(B=64, Lq=1, Lk=65536, q_pos0=65535, H=64, D=128, k=2048)
     n = ctypes.c_size_t(0)
@@ -162,6 +164,11 @@ def test_stack_errors_before_launch(lib):
     assert f(*args(None, 4)) == _lib.IDXC_ERR_INVALID_ARG
     assert f(*args(b"FSSF", 4, ws=8)) == _lib.IDXC_ERR_INVALID_ARG
     assert f(*args(b"FSSF", 4, dd=_dims(k=0))) == _lib.IDXC_ERR_INVALID_ARG
+    for bad_scale in (float("nan"), float("inf"), 0.0, -1.0):
+        a = list(args(b"FSSF", 4))
+        a[4] = bad_scale
+        assert f(*a) == _lib.IDXC_ERR_INVALID_ARG
+        assert "scale" in lib.idxc_last_error().decode()
     # an F layer without indexer inputs is rejected, an S layer's are never read
     layers[3] = IdxcLayer(0, 0, 0, FAKE, FAKE, FAKE, FAKE)
     assert f(*args(b"FSSF", 4)) == _lib.IDXC_ERR_INVALID_ARG
