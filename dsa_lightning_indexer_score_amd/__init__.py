@@ -18,7 +18,8 @@ __all__ = ["idxc_version", "idxc_validate_pattern", "idxc_schedule", "idxc_index
            "idxc_topk", "idxc_topk_workspace_bytes", "idxc_workspace_bytes", "idxc_indexer_topk", "idxc_sparse_attn", "idxc_sparse_attn_workspace_bytes", "idxc_overlap",
            "idxc_layer_stack_forward", "idxc_overlap_matrix", "idxc_greedy_pattern",
            "idxc_overlap_proxy_loss", "idxc_indexer_topk_ragged",
-           "idxc_layer_stack_forward_ragged", "idxc_distill_loss", "make_dims", "IdxcError",
+           "idxc_layer_stack_forward_ragged", "idxc_layer_stack_forward_noalloc",
+           "idxc_distill_loss", "make_dims", "IdxcError",
            "StackCall"]
 
 
@@ -205,8 +206,18 @@ def idxc_layer_stack_forward_ragged(pattern: str, layers: Sequence[Dict[str, tor
                   stream)
 
 
+def idxc_layer_stack_forward_noalloc(pattern: str, layers: Sequence[Dict[str, torch.Tensor]],
+                                     k: int, scale: float, q_pos0: int = 0, index_cache=None,
+                                     debug_indices: bool = False, stream=None):
+    """The stack without a workspace: its scratch is the library's static
+    per-GPU array (sizes beyond it raise IdxcError). Same return value as
+    idxc_layer_stack_forward."""
+    return _stack(pattern, layers, k, scale, q_pos0, None, index_cache, None, debug_indices,
+                  stream, noalloc=True)
+
+
 def _stack(pattern, layers, k, scale, q_pos0, q_pos, index_cache, workspace, debug_indices,
-           stream):
+           stream, noalloc=False):
     lib = _lib.load()
     n = len(layers)
     ref = next(L for L in layers if L.get("q") is not None)
@@ -218,7 +229,7 @@ def _stack(pattern, layers, k, scale, q_pos0, q_pos, index_cache, workspace, deb
     dev = ref["q"].device
     if index_cache is None:
         index_cache = torch.empty((B, Lq, k), dtype=torch.int32, device=dev)
-    if workspace is None:
+    if workspace is None and not noalloc:
         workspace = _workspace(idxc_workspace_bytes(B, Lq, Lk, q_pos0, H_I, d_I, k, H, D), dev)
     dbg = torch.empty((n, B, Lq, k), dtype=torch.int32, device=dev) if debug_indices else None
     arr = (IdxcLayer * n)()
@@ -237,6 +248,12 @@ def _stack(pattern, layers, k, scale, q_pos0, q_pos, index_cache, workspace, deb
                            _ptr(o, "out", torch.bfloat16).value)
     calls = ctypes.c_int32(-1)
     head = [pattern.encode(), n, arr, ctypes.byref(d)]
+    if noalloc:
+        _lib.check(lib.idxc_layer_stack_forward_noalloc(
+            *head, float(scale), _ptr(index_cache, "index_cache"), ctypes.byref(calls),
+            _ptr(dbg, "debug_indices"), _stream(stream)))
+        return dict(out=outs, indexer_calls=calls.value, index_cache=index_cache,
+                    debug_indices=dbg)
     tail = [float(scale), _ptr(index_cache, "index_cache"), _ptr(workspace, "workspace"),
             workspace.numel() * workspace.element_size(), ctypes.byref(calls),
             _ptr(dbg, "debug_indices"), _stream(stream)]

@@ -35,7 +35,12 @@ EXPORTED = (
     "idxc_layer_stack_forward", "idxc_overlap", "idxc_overlap_matrix_workspace_bytes",
     "idxc_overlap_matrix", "idxc_greedy_pattern", "idxc_overlap_proxy_loss",
     "idxc_indexer_topk_ragged", "idxc_layer_stack_forward_ragged", "idxc_distill_loss",
+    "idxc_layer_stack_forward_noalloc",
 )
+
+# bytes of the device-resident scratch of idxc_layer_stack_forward_noalloc
+# (IDXC_NOALLOC_SCRATCH_BYTES in include/idxc.h)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # double loss(const char* pattern, void* user)
 LOSS_FN = ctypes.CFUNCTYPE(ctypes.c_double, ctypes.c_char_p, ctypes.c_void_p)
@@ -94,6 +99,9 @@ def load() -> ctypes.CDLL:
         "idxc_layer_stack_forward_ragged": ([ctypes.c_char_p, i32, P(IdxcLayer), P(IdxcDims), vp,
                                              ctypes.c_float, vp, vp, sz, P(i32), vp, vp],
                                             ctypes.c_int),
+        "idxc_layer_stack_forward_noalloc": ([ctypes.c_char_p, i32, P(IdxcLayer), P(IdxcDims),
+                                              ctypes.c_float, vp, P(i32), vp, vp],
+                                             ctypes.c_int),
         "idxc_overlap_matrix_workspace_bytes": ([i32], sz),
         "idxc_distill_loss": ([vp, vp, i32, P(IdxcDims), vp, vp, vp], ctypes.c_int),
         "idxc_overlap_matrix": ([vp, i32, P(IdxcDims), vp, sz, vp, vp], ctypes.c_int),

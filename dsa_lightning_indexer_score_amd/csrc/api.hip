@@ -11,6 +11,7 @@
 // and the loop of the "NLP——IndexCache" notes, section "IndexCache 方法"
 // (compute and cache on F, read the cache on S; f(l) = max{j < l : c_j = F}).
 #include <stdarg.h>
+#include <mutex>
 #include <stdio.h>
 #include <string.h>
 
@@ -276,6 +277,37 @@ AttnArgs attn_args(const void* q, const void* k, const void* v, const int32_t* i
   a.scale = scale;
   a.out = static_cast<uint16_t*>(out);
   return a;
+}
+
+// ---- device-resident scratch of idxc_layer_stack_forward_noalloc ----------
+// One copy per GPU, alive until the process ends. In host code `scratch` is
+// only a stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress (per device, with that device current) and is the only
+// form ever handed to a kernel or a copy.
+static_assert(IDXC_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) uint8_t scratch[IDXC_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up once per device).
+int current_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(IDXC_ERR_UNSUPPORTED, "device ordinal %d above %d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(IDXC_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return IDXC_OK;
 }
 
 }  // namespace
@@ -583,10 +615,10 @@ int idxc_greedy_pattern(int32_t n_layers, int32_t removals, idxc_loss_fn loss, v
   return ok();
 }
 
-static int stack_forward(const char* pattern, int32_t n_layers, const idxc_layer* layers,
-                         const idxc_dims* dims, const int32_t* q_pos, float scale,
-                         int32_t* index_cache, void* workspace, size_t workspace_bytes,
-                         int32_t* indexer_calls, int32_t* debug_indices, void* hip_stream) {
+// Every argument check of the stack entry points except the workspace's.
+static int stack_checks(const char* pattern, int32_t n_layers, const idxc_layer* layers,
+                        const idxc_dims* dims, float scale, int32_t* index_cache,
+                        int32_t* indexer_calls, int32_t* debug_indices) {
   int r = check_pattern(pattern, n_layers, nullptr);
   if (r != IDXC_OK) return r;
   r = check_dims(dims, 1 | 2 | 4);
@@ -594,14 +626,9 @@ static int stack_forward(const char* pattern, int32_t n_layers, const idxc_layer
   if (layers == nullptr) return fail(IDXC_ERR_INVALID_ARG, "layers is NULL");
   if (indexer_calls == nullptr) return fail(IDXC_ERR_INVALID_ARG, "indexer_calls is NULL");
   REQUIRE_PTR(index_cache, "index_cache");
-  REQUIRE_PTR(workspace, "workspace");
   if (debug_indices != nullptr && !aligned16(debug_indices))
     return fail(IDXC_ERR_INVALID_ARG, "debug_indices is not 16-byte aligned");
   if (!scale_ok(scale)) return fail(IDXC_ERR_INVALID_ARG, "scale = %g: must be finite and > 0", (double)scale);
-  const Plan p = plan_for(dims, true);
-  if (workspace_bytes < p.min_bytes)
-    return fail(IDXC_ERR_INVALID_ARG, "workspace of %zu bytes is below the minimum %zu",
-                workspace_bytes, p.min_bytes);
   for (int l = 0; l < n_layers; ++l) {
     const idxc_layer& L = layers[l];
     char name[64];
@@ -622,8 +649,14 @@ static int stack_forward(const char* pattern, int32_t n_layers, const idxc_layer
     snprintf(name, sizeof(name), "layers[%d].out", l);
     REQUIRE_PTR(L.out, name);
   }
+  return IDXC_OK;
+}
 
-  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+// The layer loop, after every check has passed.
+static int stack_run(const char* pattern, int32_t n_layers, const idxc_layer* layers,
+                     const idxc_dims* dims, const int32_t* q_pos, float scale,
+                     int32_t* index_cache, void* workspace, size_t workspace_bytes,
+                     int32_t* indexer_calls, int32_t* debug_indices, hipStream_t st) {
   const size_t cache_elems = (size_t)dims->B * dims->Lq * dims->k;
   int calls = 0;
   for (int l = 0; l < n_layers; ++l) {
@@ -658,12 +691,50 @@ static int stack_forward(const char* pattern, int32_t n_layers, const idxc_layer
   return ok();
 }
 
+static int stack_forward(const char* pattern, int32_t n_layers, const idxc_layer* layers,
+                         const idxc_dims* dims, const int32_t* q_pos, float scale,
+                         int32_t* index_cache, void* workspace, size_t workspace_bytes,
+                         int32_t* indexer_calls, int32_t* debug_indices, void* hip_stream) {
+  int r = stack_checks(pattern, n_layers, layers, dims, scale, index_cache, indexer_calls,
+                       debug_indices);
+  if (r != IDXC_OK) return r;
+  REQUIRE_PTR(workspace, "workspace");
+  const Plan p = plan_for(dims, true);
+  if (workspace_bytes < p.min_bytes)
+    return fail(IDXC_ERR_INVALID_ARG, "workspace of %zu bytes is below the minimum %zu",
+                workspace_bytes, p.min_bytes);
+  return stack_run(pattern, n_layers, layers, dims, q_pos, scale, index_cache, workspace,
+                   workspace_bytes, indexer_calls, debug_indices,
+                   static_cast<hipStream_t>(hip_stream));
+}
+
 int idxc_layer_stack_forward(const char* pattern, int32_t n_layers, const idxc_layer* layers,
                              const idxc_dims* dims, float scale, int32_t* index_cache,
                              void* workspace, size_t workspace_bytes, int32_t* indexer_calls,
                              int32_t* debug_indices, void* hip_stream) {
   return stack_forward(pattern, n_layers, layers, dims, nullptr, scale, index_cache, workspace,
                        workspace_bytes, indexer_calls, debug_indices, hip_stream);
+}
+
+int idxc_layer_stack_forward_noalloc(const char* pattern, int32_t n_layers,
+                                     const idxc_layer* layers, const idxc_dims* dims,
+                                     float scale, int32_t* index_cache, int32_t* indexer_calls,
+                                     int32_t* debug_indices, void* hip_stream) {
+  int r = stack_checks(pattern, n_layers, layers, dims, scale, index_cache, indexer_calls,
+                       debug_indices);
+  if (r != IDXC_OK) return r;
+  const Plan p = plan_for(dims, true);
+  if (p.min_bytes > (size_t)IDXC_NOALLOC_SCRATCH_BYTES)
+    return fail(IDXC_ERR_UNSUPPORTED,
+                "these sizes need %zu bytes of scratch, above the static %zu bytes",
+                p.min_bytes, (size_t)IDXC_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  r = current_scratch(&ws);
+  if (r != IDXC_OK) return r;
+  const size_t ws_bytes =
+      p.bytes < (size_t)IDXC_NOALLOC_SCRATCH_BYTES ? p.bytes : (size_t)IDXC_NOALLOC_SCRATCH_BYTES;
+  return stack_run(pattern, n_layers, layers, dims, nullptr, scale, index_cache, ws, ws_bytes,
+                   indexer_calls, debug_indices, static_cast<hipStream_t>(hip_stream));
 }
 
 int idxc_layer_stack_forward_ragged(const char* pattern, int32_t n_layers,

@@ -197,6 +197,34 @@ int idxc_layer_stack_forward(const char* pattern, int32_t n_layers,
                              size_t workspace_bytes, int32_t* indexer_calls,
                              int32_t* debug_indices, void* hip_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * stack as idxc_layer_stack_forward, same arguments, results and checks, but
+ * with no workspace argument. Its scratch (candidate lists, per-chunk top-k
+ * segments, attention partials) is a library-owned device array of
+ * IDXC_NOALLOC_SCRATCH_BYTES bytes per GPU, which each GPU the library runs
+ * on holds from the first call until the process ends. The call uses the
+ * array of the CURRENT device (hipGetDevice), so hip_stream must belong to
+ * that device. Nothing is allocated or freed, by the library or by any
+ * routine it calls.
+ *  - Sizes whose minimum workspace (what idxc_workspace_bytes reports at its
+ *    smallest, see idxc_indexer_topk) exceeds the array return
+ *    IDXC_ERR_UNSUPPORTED before anything runs. Decode batches (for instance
+ *    64 sequences of up to 196608 cached tokens at k = 2048) and short
+ *    prefills fit; a 32768-token prefill does not.
+ *  - Every call on one GPU shares that GPU's array: calls that overlap in time
+ *    on one GPU (on different streams or from different threads) race and
+ *    corrupt each other's results; serialise them. The array keeps the last
+ *    call's contents; no result depends on them.
+ *  - The first call on a device looks up the array's device address
+ *    (hipGetSymbolAddress) and may initialise the HIP runtime; make it before
+ *    a graph capture begins if the capture must see no runtime set-up. */
+#define IDXC_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int idxc_layer_stack_forward_noalloc(const char* pattern, int32_t n_layers,
+                                     const idxc_layer* layers, const idxc_dims* dims,
+                                     float scale, int32_t* index_cache, int32_t* indexer_calls,
+                                     int32_t* debug_indices, void* hip_stream);
+
 /* Ragged batches (per-sequence lengths and positions, as a serving batch
  * has them): like idxc_indexer_topk / idxc_layer_stack_forward, but query row
  * r = b*Lq + i sits at the absolute position q_pos[r] (DEVICE int32 [B*Lq])

@@ -307,3 +307,42 @@ def test_distill_argument_errors(lib):
     assert f(P(), P(), 2, ctypes.byref(_dims(Lq=8, Lk=4)), P(), P(), None) == \
         _lib.IDXC_ERR_INVALID_ARG
     assert f(P(), P(), 2, d, None, None, None) == _lib.IDXC_OK   # nothing requested: no launch
+
+
+def test_noalloc_scratch_constant_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+IDXC_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)(\d+)\s*<<\s*(\d+)\)", text)
+    assert m, "IDXC_NOALLOC_SCRATCH_BYTES not found"
+    assert int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_stack_checks_before_any_device_use(lib):
+    f = lib.idxc_layer_stack_forward_noalloc
+    layers = (IdxcLayer * 4)()
+    for l in range(4):
+        layers[l] = IdxcLayer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    calls = ctypes.c_int32(-7)
+
+    def call(pat=b"FSSF", n=4, dd=None, scale=0.125, cache=P(), dbg=None):
+        dd = dd if dd is not None else _dims()
+        return f(pat, n, layers, ctypes.byref(dd), scale, cache, ctypes.byref(calls), dbg, None)
+
+    assert call(pat=b"SFSF") == _lib.IDXC_ERR_PATTERN
+    assert call(pat=b"FSS") == _lib.IDXC_ERR_PATTERN
+    assert call(scale=0.0) == _lib.IDXC_ERR_INVALID_ARG
+    assert call(cache=None) == _lib.IDXC_ERR_INVALID_ARG
+    assert call(dbg=P(FAKE + 4)) == _lib.IDXC_ERR_INVALID_ARG
+    # a 32768-token prefill needs far more scratch than the static array
+    big = _dims(B=1, Lq=32768, Lk=32768, H_I=64, d_I=128, H=64, D=128, k=2048)
+    assert call(dd=big) == _lib.IDXC_ERR_UNSUPPORTED
+    msg = lib.idxc_last_error().decode()
+    assert "scratch" in msg and str(_lib.NOALLOC_SCRATCH_BYTES) in msg
+    # just above the limit: the smallest workspace is one byte too large
+    n = ctypes.c_size_t(0)
+    dec = _dims(B=64, Lq=1, Lk=65536, q_pos0=65535, H_I=64, d_I=128, H=64, D=128, k=2048)
+    assert lib.idxc_workspace_bytes(ctypes.byref(dec), ctypes.byref(n)) == 0
+    assert n.value <= _lib.NOALLOC_SCRATCH_BYTES  # the decode batch of the benchmark fits
+    layers[1] = IdxcLayer(0, 0, 0, FAKE, FAKE, FAKE, FAKE)
+    assert call(pat=b"FFSF") == _lib.IDXC_ERR_INVALID_ARG
+    assert "layers[1].q_idx" in lib.idxc_last_error().decode()
+    assert calls.value == -7  # nothing ran
