@@ -185,20 +185,9 @@ int cap_for(const idxc_dims* d, size_t ws_bytes) {
   return (int)cap;
 }
 
-// Scratch of the two-stage top-k for long materialised rows, at `base`.
+// Scratch of the top-k of long materialised rows (chunk histograms), at `base`.
 void set_parts(TopkArgs& ta, uint8_t* base, const idxc_dims* d) {
-  const int rows = d->B * d->Lq;
-  const int nch = topk_row_chunks(d->Lk);
-  if (nch <= 1) return;
-  ta.part = reinterpret_cast<u32x2_t*>(base);
-  ta.part_count = reinterpret_cast<int*>(base + (size_t)rows * nch * d->k * 8);
-}
-
-// Long materialised rows are selected in two stages; the second stage must
-// hold every chunk's winners in one workgroup.
-bool topk_rows_supported(const idxc_dims* d) {
-  const int nch = topk_row_chunks(d->Lk);
-  return nch <= 1 || (nch <= kMaxSegments && (long long)nch * d->k <= kMaxStagePairs);
+  if (topk_row_chunks(d->Lk) > 1) ta.ghist = base;
 }
 
 // Indexer + top-k for one layer into `indices`, using the workspace.
@@ -388,9 +377,6 @@ int idxc_topk(const float* scores, const idxc_dims* dims, int32_t order, void* w
     return fail(IDXC_ERR_INVALID_ARG, "order = %d is not an IDXC_ORDER_* value", order);
   REQUIRE_PTR(scores, "scores");
   REQUIRE_PTR(indices, "indices");
-  if (!topk_rows_supported(dims))
-    return fail(IDXC_ERR_UNSUPPORTED, "rows of %d scores with k = %d exceed the two-stage top-k",
-                dims->Lk, dims->k);
   const size_t need = topk_part_bytes(dims->B * dims->Lq, dims->Lk, dims->k);
   if (need > 0) {
     REQUIRE_PTR(workspace, "workspace");

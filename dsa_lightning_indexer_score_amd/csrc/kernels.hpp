@@ -47,9 +47,11 @@ struct TopkArgs {
   const u32x2_t* cand;
   const int* cand_count;
   int nseg, seg_cap, stage_cap;
-  // scratch for long materialised rows (two-stage selection)
+  // scratch of the per-group stage of many-segment candidate lists
   u32x2_t* part;
   int* part_count;
+  // scratch of long materialised rows: per (row, chunk) top-digit histograms
+  void* ghist;
   int rows, k;
   int32_t* out;  // [rows, k]
   // 0: score order (higher score, then lower position); 1: increasing
@@ -57,9 +59,11 @@ struct TopkArgs {
   int pos_order;
 };
 
-// Number of stage-1 chunks for materialised rows of length Lk (1 = single pass).
+// Number of kTopkChunk-score chunks of materialised rows of length Lk (1 =
+// one pass per row, no scratch).
 int topk_row_chunks(int Lk);
-// Scratch bytes launch_topk needs for materialised rows of length Lk.
+// Scratch bytes launch_topk needs for materialised rows of length Lk (4 KB
+// per chunk of every row).
 size_t topk_part_bytes(int rows, int Lk, int k);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 // Candidate rows of nseg segments of k: groups of segments selected first when

@@ -5,62 +5,46 @@
 // lower position, with -0.0 == +0.0, and rows shorter than k return all of
 // their t+1 positions followed by -1.
 //
-// Scores become order-preserving 32-bit keys. A workgroup stages its input in
-// LDS once (loads batched so many are in flight), selects the exact top-k in
-// position order (select.hpp: range-narrowing radix select plus an ordered
-// pass), and a bitonic sort of 64-bit (key, ~position) words puts the k
-// winners in score order (in the wide final stage of long rows, ranks from key
-// buckets when the scores are spread out); the index cache of a layer stack
-// keeps them in position order instead (gathers then sweep the keys in
-// order), which needs no sort.
+// Scores become order-preserving 32-bit keys held in registers (32 per thread
+// in 256-thread workgroups, one row each, for rows of up to 8192 scores; 16
+// per thread in 1024-thread workgroups for candidate lists of up to 16384
+// pairs). radix_topk.hpp finds the k-th best key digit by digit and emits the
+// winners in position order; score order then ranks the winners by value
+// buckets (a bitonic sort when scores bunch on few values).
 //
-// Inputs: a materialised score row (positions implicit), or candidate lists of
-// (order key, position) pairs in increasing position order, possibly split in
-// segments whose concatenation is position-ordered. Rows longer than one
-// workgroup's stage are cut into chunks; each chunk's exact top-k is written
-// as a position-ordered candidate segment (stage 1) and a second launch
-// selects from the concatenated segments (stage 2). Every entry of the final
-// top-k is in its chunk's top-k, so the result is the same.
+// Longer rows take two launches: one workgroup per (row, 8192-score chunk)
+// counts the top 11 bits of its keys into a global histogram slice, then one
+// 1024-thread workgroup per row sums its slices, resolves the top digit, and,
+// if the keys at or above that digit fit in LDS, gathers them there in
+// position order (refining first, in passes over the row, while they do not)
+// and finishes the selection on them.
+//
+// Candidate lists of (order key, position) pairs, in increasing position
+// order, come from the fused indexer (one list per row) or from the per-chunk
+// top-k of the decode indexer (several segments per row, whose concatenation
+// is position-ordered).
 #include "common.hpp"
 #include "kernels.hpp"
-#include "select.hpp"
+#include "radix_topk.hpp"
+
+#include <type_traits>
 
 namespace idxc {
 
 namespace {
 
-constexpr int kThreads = kSelThreads;
-// multi-segment selections (few rows, up to 16384 candidates each) use wider
-// workgroups: there are few of them, so latency per row is what counts
-constexpr int kThreadsWide = 1024;
-constexpr int kBatch = 8;  // staged loads in flight per thread
+constexpr int kRowThreads = 256;  // one row of up to kTopkChunk scores
+constexpr int kRowR = kTopkChunk / kRowThreads;
+constexpr int kWideThreads = 1024;  // long rows and multi-segment lists
+constexpr int kWideR = kMaxStagePairs / kWideThreads;
+constexpr int kLongCap = kMaxStagePairs;  // keys a long row gathers into LDS
+constexpr int kHistWords = kSelBins / 2;  // packed 16-bit level-0 histogram
+static_assert(kRowR % 4 == 0 && kWideR % 4 == 0, "groups of four elements");
 static_assert(kTopkChunk <= kSelMaxKeys && kMaxStagePairs <= kSelMaxKeys,
-              "selection histogram counts fit 16 bits");
+              "16-bit histogram counts");
 
-// LDS: segment offsets and selection scratch, then the staged keys, then
-// (multi-segment candidate lists only) the staged positions. Score-order
-// output sorts its winners in a buffer laid over the selection histogram
-// (which the winners' collection no longer reads), extended past the end of
-// the scratch, so the staged keys start after it. Position-order output needs
-// no sort buffer, and single-segment lists read their winners' positions
-// back from memory, so the common candidate case stages keys alone.
-template <int NT>
-struct Smem {
-  int seg_off[kMaxSegments + 1];
-  SelectSmemT<NT> sel;  // histogram last
-};
-template <int NT>
-constexpr size_t smem_bytes() {
-  return (sizeof(Smem<NT>) + 15) / 16 * 16;
-}
-template <int NT>
-constexpr size_t sort_off() {
-  return offsetof(Smem<NT>, sel) + offsetof(SelectSmemT<NT>, hist);
-}
-constexpr size_t kSortBytes = (size_t)kMaxK * 8;
-
-enum SrcKind { kSrcRow = 0, kSrcCand = 1, kSrcCand1 = 2 };
-enum OutKind { kOutFinal = 0, kOutPart = 1 };
+enum OutKind { kOutPos = 0, kOutScore = 1, kOutPart = 2 };
+enum SrcKind { kSrcCand1 = 0, kSrcCandSeg = 1 };
 
 // 64-bit word of lane (l ^ m) for m = 1 .. 32 (constant once unrolled).
 __device__ __forceinline__ uint64_t lane_xor64(uint64_t v, int m) {
@@ -134,404 +118,581 @@ __device__ __forceinline__ void sort2048_regs(uint64_t (&v)[8], uint64_t* lds, i
   }
 }
 
-// Score order by bucket ranks. The kk winners' 64-bit words (key, ~position)
-// sit in sortbuf in position order, and their keys span [wlo, whi]; split
-// that range into kSelBins buckets of one power-of-two width. A winner's rank
-// is the number of winners in higher buckets plus the number of larger words
-// in its own bucket (words are distinct: positions are). `scratch` (8 KB of
-// LDS) takes the packed 16-bit bucket cursors, then the buckets' members as
-// 16-bit slots. Returns false, having written no output, when a bucket holds
-// more than kMaxBucket winners (scores bunched on few values, or spread over
-// many binades): the caller then sorts.
-constexpr int kMaxBucket = 64;
-constexpr int kBucketScratchBytes = kSelBins / 2 * 4 + kMaxK * 2;
 
-template <int NT>
-__device__ bool bucket_rank_output(uint64_t* sortbuf, int kk, int k, uint32_t wlo,
-                                   uint32_t whi, uint32_t* scratch, SelectSmemT<NT>& sm,
-                                   int32_t* orow) {
-  constexpr int BPT = kSelBins / NT;  // buckets per thread
-  const int tid = threadIdx.x;
-  uint32_t* cur = scratch;  // kSelBins / 2 words, bucket b in half b % 2 of word b / 2
-  uint16_t* mem = reinterpret_cast<uint16_t*>(scratch + kSelBins / 2);
-  const int shift = max(0, (32 - __clz((int)(whi - wlo))) - kSelBinsLog2);
-  auto bucket_of = [&](uint64_t w) { return ((uint32_t)(w >> 32) - wlo) >> shift; };
-  for (int b = tid; b < kSelBins / 2; b += NT) cur[b] = 0u;
-  __syncthreads();
-  for (int sl = tid; sl < kk; sl += NT) {
-    const uint32_t b = bucket_of(sortbuf[sl]);
-    atomicAdd(&cur[b >> 1], 1u << ((b & 1u) << 4));
-  }
-  __syncthreads();
-  // bucket starts in descending bucket order: thread tid owns buckets
-  // top - q, q = 0..BPT-1 (top is odd: buckets top - q and top - q - 1 share
-  // a word for even q)
-  const int top = kSelBins - 1 - BPT * tid;
-  int cnts[BPT];
-  int local = 0;
-  uint32_t most = 0u, unused = 0xFFFFFFFFu;
-#pragma unroll
-  for (int q = 0; q < BPT; q += 2) {
-    const uint32_t w = cur[(top - q) >> 1];
-    cnts[q] = (int)(w >> 16);
-    cnts[q + 1] = (int)(w & 0xFFFFu);
-    local += cnts[q] + cnts[q + 1];
-    most = max(most, max(w >> 16, w & 0xFFFFu));
-  }
-  int total;
-  const int excl = sel_excl_scan<NT>(local, sm.scan, &total);
-  wave_minmax(unused, most);
-  if (lane_id() == 0) sm.kred[tid / kWave] = most;
-  __syncthreads();
-  uint32_t bmax = 0u;
-#pragma unroll
-  for (int w = 0; w < NT / kWave; ++w) bmax = max(bmax, sm.kred[w]);
-  if (bmax > (uint32_t)kMaxBucket) return false;  // block-uniform
-  int acc = excl;
-#pragma unroll
-  for (int q = 0; q < BPT; q += 2) {
-    const uint32_t start_hi = (uint32_t)acc;
-    acc += cnts[q];
-    cur[(top - q) >> 1] = (start_hi << 16) | (uint32_t)acc;
-    acc += cnts[q + 1];
-  }
-  __syncthreads();
-  for (int sl = tid; sl < kk; sl += NT) {
-    const uint32_t b = bucket_of(sortbuf[sl]);
-    const uint32_t sh = (b & 1u) << 4;
-    const uint32_t old = atomicAdd(&cur[b >> 1], 1u << sh);
-    mem[(old >> sh) & 0xFFFFu] = (uint16_t)sl;
-  }
-  __syncthreads();
-  // each cursor now holds its bucket's end; bucket b starts where bucket b+1
-  // (the next higher one) ends
-  auto end_of = [&](uint32_t b) { return (cur[b >> 1] >> ((b & 1u) << 4)) & 0xFFFFu; };
-  constexpr int EPT = kMaxK / NT;  // winners per thread at most
-  uint32_t rk[EPT], pv[EPT];
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) {
-    const int sl = tid + i * NT;
-    rk[i] = 0u;
-    pv[i] = 0u;
-    if (sl < kk) {
-      const uint64_t w = sortbuf[sl];
-      const uint32_t b = bucket_of(w);
-      const uint32_t e = end_of(b);
-      const uint32_t st = b + 1 < (uint32_t)kSelBins ? end_of(b + 1) : 0u;
-      uint32_t rank = st;
-      for (uint32_t j = st; j < e; ++j) rank += sortbuf[mem[j]] > w ? 1u : 0u;
-      rk[i] = rank;
-      pv[i] = ~(uint32_t)(w & 0xFFFFFFFFull);
-    }
-  }
-  // the row in rank order through LDS (over the words, all read by now), so
-  // that it is written with coalesced stores
-  __syncthreads();
-  uint32_t* obuf = reinterpret_cast<uint32_t*>(sortbuf);
-#pragma unroll
-  for (int i = 0; i < EPT; ++i)
-    if (tid + i * NT < kk) obuf[rk[i]] = pv[i];
-  __syncthreads();
-  for (int j = tid; j < k; j += NT) orow[j] = j < kk ? (int32_t)obuf[j] : -1;
-  return true;
+// Score rows are read through a buffer resource whose size is the row's
+// valid part: reads past it return 0 instead of faulting, so every load is
+// issued unconditionally. A 16-byte-aligned row is read 16 bytes (one group
+// of four scores) at a time; its last group, when partly valid, is read again
+// one score at a time. Rows that are not 16-byte aligned are read one score
+// at a time.
+struct RowSrc {
+  __amdgpu_buffer_rsrc_t rs;
+  int n;
+  bool vec;
+};
+
+__device__ __forceinline__ RowSrc row_src(const float* src, int n) {
+  RowSrc r;
+  r.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(src), (short)0, n * 4, 0x00020000);
+  r.n = n;
+  r.vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
+  return r;
 }
 
-// One workgroup = one (row, chunk). SRC kSrcRow: positions [c0, c1) of a score
-// row. SRC kSrcCand: the concatenation of nseg segments of a row (positions
-// staged too). SRC kSrcCand1: one segment (positions read back for winners).
-// The staged input starts at byte stage_off of the dynamic LDS.
-template <int SRC, int OUT, int NT>
-__global__ __launch_bounds__(NT)
-void topk_kernel(TopkArgs a, int chunk_len, int nchunks, int stage_off, int stage_bytes) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
-  Smem<NT>& sm = *reinterpret_cast<Smem<NT>*>(dyn);
-  uint32_t* skey = reinterpret_cast<uint32_t*>(dyn + stage_off);
-  uint32_t* spos = nullptr;  // SRC kSrcCand: positions after the keys
-  uint64_t* sortbuf = reinterpret_cast<uint64_t*>(dyn + sort_off<NT>());
+__device__ __forceinline__ uint32_t row_load1(const RowSrc& s, int e) {
+  return __builtin_amdgcn_raw_buffer_load_b32(s.rs, e * 4, 0, 0);
+}
 
+// Raw bits of group g (scores 4g .. 4g+3; 0 past n).
+__device__ __forceinline__ u32x4 row_load4(const RowSrc& s, int g) {
+  if (s.vec) return __builtin_amdgcn_raw_buffer_load_b128(s.rs, g * 16, 0, 0);
+  return u32x4{row_load1(s, 4 * g), row_load1(s, 4 * g + 1), row_load1(s, 4 * g + 2),
+               row_load1(s, 4 * g + 3)};
+}
+
+// The partly valid last group of an aligned row, one score at a time.
+__device__ __forceinline__ void row_fix_tail(const RowSrc& s, int g, u32x4& raw) {
+  if (s.vec && (s.n & 3) != 0 && g == (s.n >> 2)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) raw[j] = row_load1(s, 4 * g + j);
+  }
+}
+
+// Keys of one score row (n scores) into registers, group v of this thread
+// being row group tid + NT*v, and the least / greatest valid key of the
+// thread (UINT32_MAX / 0 if none).
+template <int NT, int R>
+__device__ __forceinline__ void load_row_keys(const float* src, int n, uint32_t (&key)[R],
+                                              uint32_t& kmin, uint32_t& kmax) {
+  const RowSrc rs = row_src(src, n);
   const int tid = threadIdx.x;
-  const int k = a.k;
-  const int row = blockIdx.x / nchunks;
-  const int chunk = blockIdx.x % nchunks;
+  const int nvg = rdx_live_groups<NT>(n);
+  u32x4 raw[R / 4];
+#pragma unroll
+  for (int v = 0; v < R / 4; ++v)
+    raw[v] = v < nvg ? row_load4(rs, tid + NT * v) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int v = 0; v < R / 4; ++v)
+    if (v < nvg) row_fix_tail(rs, tid + NT * v, raw[v]);
+  kmin = 0xFFFFFFFFu;
+  kmax = 0u;
+#pragma unroll
+  for (int v = 0; v < R / 4; ++v) {
+    if (v >= nvg) continue;  // workgroup-uniform
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * (tid + NT * v) + j;
+      const uint32_t kv = order_key(__uint_as_float(raw[v][j]));
+      key[4 * v + j] = kv;
+      if (e < n) {
+        kmin = min(kmin, kv);
+        kmax = max(kmax, kv);
+      }
+    }
+  }
+}
 
-  // ---- stage the input in LDS (keys, and positions for candidate lists),
-  // noting the range of the keys this thread stores
-  int n;
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  int pos0 = 0;  // kSrcRow: position of entry 0
-  if (SRC == kSrcRow) {
-    const int i = row % a.Lq;
-    const int len = min(a.q_pos0 + i + 1, a.Lk);
-    pos0 = chunk * chunk_len;
-    n = max(0, min(len, pos0 + chunk_len) - pos0);
-    const float* src = a.scores + (size_t)row * a.Lk + pos0;
-    int done = 0;
-    if ((reinterpret_cast<uintptr_t>(src) & 15) == 0) {
-      // 16-byte loads (4 keys each), kBatch of them in flight per thread
-      const int n4 = n >> 2;
-      const f32x4* src4 = reinterpret_cast<const f32x4*>(src);
-      for (int base = 0; base < n4; base += NT * kBatch) {
-        f32x4 v[kBatch];
+template <int NT>
+__device__ __forceinline__ int elem_of(int r) {
+  return 4 * ((int)threadIdx.x + NT * (r >> 2)) + (r & 3);
+}
+
+// Score-order finish: the kk winners' words are in `words`, their key range
+// in [wmin, wmax] per thread. Ranks them (or sorts them) into orow.
+template <int NT, int NGRP>
+__device__ void score_order_output(uint64_t* words, uint16_t* slots, int kk, int k,
+                                   uint32_t wmin, uint32_t wmax, RdxSmem<NT, NGRP>& sm,
+                                   int32_t* orow) {
+  const int tid = threadIdx.x;
+  wave_minmax(wmin, wmax);
+  if (lane_id() == 0) {
+    sm.red[tid / kWave] = wmin;
+    sm.red[NT / kWave + tid / kWave] = wmax;
+  }
+  __syncthreads();  // also: every word is written
+  uint32_t wlo = sm.red[0], whi = sm.red[NT / kWave];
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          const int e = base + j * NT + tid;
-          v[j] = e < n4 ? src4[e] : f32x4{};
+  for (int w = 1; w < NT / kWave; ++w) {
+    wlo = min(wlo, sm.red[w]);
+    whi = max(whi, sm.red[NT / kWave + w]);
+  }
+  __syncthreads();  // red is reused below
+  if (rdx_rank_output<NT, NGRP>(words, kk, k, wlo, whi, slots, sm, orow)) return;
+  // bitonic sort of the kk winners padded with zero words (every winner's word
+  // is nonzero, so they sort last); the first 256 threads hold the words
+  static_assert(kMaxK == 8 * 256 && NT % 256 == 0, "register sort layout");
+  const bool act = tid < 256;
+  uint64_t v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int idx = tid * 8 + j;
+    v[j] = (act && idx < kk) ? words[idx] : 0ull;
+  }
+  sort2048_regs(v, words, tid, act);
+  if (act) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int idx = tid * 8 + j;
+      if (idx < k) orow[idx] = (idx < kk) ? (int32_t)(~(uint32_t)(v[j] & 0xFFFFFFFFull)) : -1;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Rows of up to kTopkChunk materialised scores, one 256-thread workgroup per
+// row, longest rows first. Row r = b*Lq + i holds candidates 0..t, t =
+// q_pos0 + i (never more than Lk).
+// ---------------------------------------------------------------------------
+template <int OUT>
+__global__ __launch_bounds__(kRowThreads)
+void topk_rows_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, int q_pos0, int k,
+                      int32_t* __restrict__ out) {
+  constexpr int NT = kRowThreads, R = kRowR, NGRP = R / 4;
+  __shared__ RdxSmem<NT, NGRP> sm;
+  __shared__ uint64_t words[OUT == kOutScore ? kMaxK : 2];
+  __shared__ uint16_t slots[OUT == kOutScore ? kMaxK : 2];
+  const int tid = threadIdx.x;
+  const int i = Lq - 1 - (int)(blockIdx.x / (unsigned)B);
+  const int b = (int)(blockIdx.x % (unsigned)B);
+  const size_t row = (size_t)b * Lq + i;
+  const int n = min(q_pos0 + i + 1, Lk);
+  int32_t* orow = out + row * k;
+  if (OUT == kOutPos && n <= k) {  // every candidate, in position order
+    for (int j = tid; j < k; j += NT) orow[j] = j < n ? j : -1;
+    return;
+  }
+  rdx_clear(sm, kHistWords);
+  uint32_t key[R], kmin, kmax, lo, hi;
+  load_row_keys<NT, R>(scores + row * Lk, n, key, kmin, kmax);
+  rdx_key_range(kmin, kmax, sm, lo, hi);  // its barrier also ends the clear
+  auto valid = [&](int r) { return elem_of<NT>(r) < n; };
+#pragma unroll
+  for (int r = 0; r < R; ++r) key[r] = valid(r) ? key[r] - lo : 0u;  // rel, padded
+  RdxState st = rdx_start(n, k, lo, hi);
+  rdx_search_regs<NT, NGRP, R>(key, n, sm, st);
+  if (OUT == kOutPos) {
+    const int kk = rdx_emit_regs<NT, NGRP, 4, R>(
+        key, n, valid, st, sm, 0, [&](int slot, uint32_t, int r) { orow[slot] = elem_of<NT>(r); });
+    for (int j = kk + tid; j < k; j += NT) orow[j] = -1;
+  } else {
+    uint32_t wmin = 0xFFFFFFFFu, wmax = 0u;
+    const int kk = rdx_emit_regs<NT, NGRP, 4, R>(key, n, valid, st, sm, 0,
+                                                 [&](int slot, uint32_t rv, int r) {
+                                                   const uint32_t kv = rv + lo;
+                                                   words[slot] = ((uint64_t)kv << 32) |
+                                                                 (uint64_t)(~(uint32_t)elem_of<NT>(r));
+                                                   wmin = min(wmin, kv);
+                                                   wmax = max(wmax, kv);
+                                                 });
+    score_order_output<NT, NGRP>(words, slots, kk, k, wmin, wmax, sm, orow);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Long rows, first launch: one workgroup per (row, kTopkChunk-score chunk)
+// writes the packed 16-bit histogram of its keys' top 11 bits to
+// ghist[(row * nch + chunk) * kHistWords ..]. Chunks past the row's end write
+// nothing (the second launch reads only the row's own chunks).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kRowThreads)
+void topk_chunk_hist_kernel(const float* __restrict__ scores, int Lq, int Lk, int q_pos0,
+                            int nch, uint32_t* __restrict__ ghist) {
+  constexpr int NT = kRowThreads, R = kRowR;
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kHistWords];
+  const int tid = threadIdx.x;
+  const size_t row = blockIdx.x / (unsigned)nch;
+  const int c = (int)(blockIdx.x % (unsigned)nch);
+  const int i = (int)(row % (size_t)Lq);
+  const int n = min(q_pos0 + i + 1, Lk);
+  const int c0 = c * kTopkChunk;
+  if (c0 >= n) return;
+  const int m = min(kTopkChunk, n - c0);
+  for (int w = tid; w < kHistWords; w += NT) hist[w] = 0u;
+  uint32_t key[R], kmin, kmax;
+  load_row_keys<NT, R>(scores + row * Lk + c0, m, key, kmin, kmax);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (elem_of<NT>(r) < m) hist16_add(hist, key[r] >> 21);  // the top 11 bits
+  __syncthreads();
+  u32x4* dst = reinterpret_cast<u32x4*>(ghist + (row * nch + c) * kHistWords);
+  const u32x4* srch = reinterpret_cast<const u32x4*>(hist);
+  for (int w = tid; w < kHistWords / 4; w += NT) dst[w] = srch[w];
+}
+
+// Streaming count of level st.level over a whole score row into the 32-bit
+// histogram, then its resolution (par: the level's slot parity).
+template <int NT, int NGRP>
+__device__ void stream_level(const float* src, int n, RdxSmem<NT, NGRP>& sm, RdxState& st,
+                             int par) {
+  const RowSrc rs = row_src(src, n);
+  const int ng = (n + 3) / 4;
+  const int L = st.level;
+  constexpr int BATCH = 4;
+  for (int g0 = 0; g0 < ng; g0 += NT * BATCH) {
+    u32x4 raw[BATCH];
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) raw[q] = row_load4(rs, g0 + q * NT + (int)threadIdx.x);
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) {
+      const int g = g0 + q * NT + (int)threadIdx.x;
+      row_fix_tail(rs, g, raw[q]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t kv = order_key(__uint_as_float(raw[q][j]));
+        if (4 * g + j < n && rdx_match(st, L, kv)) atomicAdd(&sm.hist[rdx_digit(st, L, kv)], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  rdx_resolve<NT, NGRP, false>(sm, st, par);
+}
+
+// ---------------------------------------------------------------------------
+// Long rows, second launch: one 1024-thread workgroup per row (longest rows
+// first). Rows of at most kLongCap scores are loaded straight into registers.
+// Longer rows: the row's chunk histograms give the top digit; while the keys
+// at or above the digits found so far exceed kLongCap, one more digit is
+// resolved by a pass over the row; then a pass gathers those keys (for a
+// fully resolved key: the keys above it and the first `rem` equal to it) into
+// LDS in position order, and the selection finishes on them in registers.
+// Dynamic LDS: RdxSmem, then kLongCap keys and kLongCap positions (the
+// score-order words and rank slots reuse the keys' area).
+// ---------------------------------------------------------------------------
+template <int OUT>
+__global__ __launch_bounds__(kWideThreads)
+void topk_long_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, int q_pos0, int k,
+                      int nch, const uint32_t* __restrict__ ghist, int32_t* __restrict__ out) {
+  constexpr int NT = kWideThreads, R = kWideR, NGRP = R / 4, NW = NT / kWave;
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
+  RdxSmem<NT, NGRP>& sm = *reinterpret_cast<RdxSmem<NT, NGRP>*>(dyn);
+  constexpr size_t kOffKeys = (sizeof(RdxSmem<NT, NGRP>) + 15) / 16 * 16;
+  uint32_t* ckey = reinterpret_cast<uint32_t*>(dyn + kOffKeys);
+  uint32_t* cpos = ckey + kLongCap;
+  uint64_t* words = reinterpret_cast<uint64_t*>(ckey);  // score order, after the keys are read
+  uint16_t* slots = reinterpret_cast<uint16_t*>(words + kMaxK);
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  const int i = Lq - 1 - (int)(blockIdx.x / (unsigned)B);
+  const int b = (int)(blockIdx.x % (unsigned)B);
+  const size_t row = (size_t)b * Lq + i;
+  const int n = min(q_pos0 + i + 1, Lk);
+  const float* src = scores + row * Lk;
+  int32_t* orow = out + row * k;
+  if (OUT == kOutPos && n <= k) {
+    for (int j = tid; j < k; j += NT) orow[j] = j < n ? j : -1;
+    return;
+  }
+  uint32_t key[R], pos[R], kmin, kmax;
+  int m;  // elements held in registers
+  if (n <= kLongCap) {
+    rdx_clear(sm, kHistWords);
+    load_row_keys<NT, R>(src, n, key, kmin, kmax);
+#pragma unroll
+    for (int r = 0; r < R; ++r) pos[r] = (uint32_t)elem_of<NT>(r);
+    m = n;
+  } else {
+    // level 0 (the top 11 bits) from the chunk histograms, as 32-bit sums
+    RdxState st = rdx_start(n, k, 0u, 0xFFFFFFFFu);
+    const int nc = (n + kTopkChunk - 1) / kTopkChunk;
+    for (int w = tid; w < kHistWords; w += NT) {
+      uint32_t lo = 0u, hi = 0u;
+      for (int c = 0; c < nc; ++c) {
+        const uint32_t v = ghist[(row * nch + c) * kHistWords + w];
+        lo += v & 0xFFFFu;
+        hi += v >> 16;
+      }
+      sm.hist[2 * w] = lo;
+      sm.hist[2 * w + 1] = hi;
+    }
+    __syncthreads();
+    int par = 0;
+    int cnt = rdx_resolve<NT, NGRP, false>(sm, st, par);
+    // refine over the row while the keys at or above the digits found do
+    // not fit in LDS
+    while (!st.done && st.level < 3 && (k - st.rem) + cnt > kLongCap) {
+      par ^= 1;
+      stream_level<NT, NGRP>(src, n, sm, st, par);
+      cnt = sm.bc[par][2];
+    }
+    // gather the keys at or above the digits found (a fully resolved key
+    // with ties: those above it and the first `rem` equal to it), in
+    // position order, four groups per thread between barriers
+    const bool exact = st.level == 3 && !st.done;
+    const uint32_t t = st.prefix;  // lo = 0: the threshold key itself
+    const RowSrc rs = row_src(src, n);
+    const int ng = (n + 3) / 4;
+    int above_tot = 0, eq_tot = 0, buf = 0;
+    constexpr int BATCH = NGRP;
+    u32x4 raw[BATCH];
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) raw[q] = row_load4(rs, q * NT + tid);
+    for (int g0 = 0; g0 < ng; g0 += NT * BATCH) {
+      uint32_t kv[BATCH][4], keep[BATCH], eqm[BATCH];
+      int cntq[BATCH], inc[BATCH];
+#pragma unroll
+      for (int q = 0; q < BATCH; ++q) {
+        row_fix_tail(rs, g0 + q * NT + tid, raw[q]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kv[q][j] = order_key(__uint_as_float(raw[q][j]));
+      }
+      // the next batch's loads, in flight while this one is gathered
+#pragma unroll
+      for (int q = 0; q < BATCH; ++q) raw[q] = row_load4(rs, g0 + NT * BATCH + q * NT + tid);
+#pragma unroll
+      for (int q = 0; q < BATCH; ++q) {
+        const int g = g0 + q * NT + tid;
+        keep[q] = 0u;
+        eqm[q] = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (4 * g + j < n) {
+            const uint32_t kj = kv[q][j];
+            if (exact ? kj > t : kj >= t) keep[q] |= 1u << j;
+            else if (exact && kj == t) eqm[q] |= 1u << j;
+          }
         }
+        cntq[q] = __popc(keep[q]) | (__popc(eqm[q]) << 16);
+        inc[q] = wave_incl_scan(cntq[q]);
+        if (lane == kWave - 1) sm.wtot[buf][q * NW + wave] = inc[q];
+      }
+      __syncthreads();
+      int base = 0;
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          const int e = base + j * NT + tid;
-          if (e < n4) {
-            const u32x4 kv = u32x4{order_key(v[j][0]), order_key(v[j][1]),
-                                   order_key(v[j][2]), order_key(v[j][3])};
-            *reinterpret_cast<u32x4*>(skey + 4 * e) = kv;
-            kmin = min(min(kmin, min(kv[0], kv[1])), min(kv[2], kv[3]));
-            kmax = max(max(kmax, max(kv[0], kv[1])), max(kv[2], kv[3]));
+      for (int q = 0; q < BATCH; ++q) {
+        int before = base, tot = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const int x = sm.wtot[buf][q * NW + w];
+          if (w < wave) before += x;
+          tot += x;
+        }
+        base += tot;
+        const int excl = before + inc[q] - cntq[q];
+        int eq_before = eq_tot + (excl >> 16);
+        int slot = above_tot + (excl & 0xFFFF) + min(eq_before, st.rem);
+        const int g = g0 + q * NT + tid;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if ((keep[q] >> j) & 1u) {
+            ckey[slot] = kv[q][j];
+            cpos[slot] = (uint32_t)(4 * g + j);
+            ++slot;
+          } else if ((eqm[q] >> j) & 1u) {
+            if (eq_before < st.rem) {
+              ckey[slot] = kv[q][j];
+              cpos[slot] = (uint32_t)(4 * g + j);
+              ++slot;
+            }
+            ++eq_before;
           }
         }
       }
-      done = n4 * 4;
+      above_tot += base & 0xFFFF;
+      eq_tot += base >> 16;
+      buf ^= 1;
     }
-    // the rest: a tail of up to 3 keys, or a row that is not 16-byte aligned
-    for (int base = done; base < n; base += NT * kBatch) {
-      float v[kBatch];
+    m = above_tot + (exact ? min(eq_tot, st.rem) : 0);
+    __syncthreads();  // the gathered keys are in LDS
+    kmin = 0xFFFFFFFFu;
+    kmax = 0u;
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int e = base + j * NT + tid;
-        v[j] = e < n ? src[e] : 0.0f;
-      }
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int e = base + j * NT + tid;
-        if (e < n) {
-          const uint32_t key = order_key(v[j]);
-          skey[e] = key;
-          kmin = min(kmin, key);
-          kmax = max(kmax, key);
-        }
+    for (int r = 0; r < R; ++r) {
+      const int e = elem_of<NT>(r);
+      key[r] = e < m ? ckey[e] : 0u;
+      pos[r] = e < m ? cpos[e] : 0u;
+      if (e < m) {
+        kmin = min(kmin, key[r]);
+        kmax = max(kmax, key[r]);
       }
     }
-  } else if (SRC == kSrcCand1) {
+    // the selection restarts on the gathered keys (a superset of the row's
+    // top-k holding every key equal to its least member) with digits over
+    // their own range; rdx_resolve left the histogram zero
+  }
+  uint32_t lo, hi;
+  rdx_key_range(kmin, kmax, sm, lo, hi);  // also: every gathered key is read
+  auto valid = [&](int r) { return elem_of<NT>(r) < m; };
+#pragma unroll
+  for (int r = 0; r < R; ++r) key[r] = valid(r) ? key[r] - lo : 0u;  // rel, padded
+  RdxState st = rdx_start(m, k, lo, hi);
+  rdx_search_regs<NT, NGRP, R>(key, m, sm, st);
+  if (OUT == kOutPos) {
+    const int kk = rdx_emit_regs<NT, NGRP, 4, R>(
+        key, m, valid, st, sm, 0, [&](int slot, uint32_t, int r) { orow[slot] = (int32_t)pos[r]; });
+    for (int j = kk + tid; j < k; j += NT) orow[j] = -1;
+  } else {
+    uint32_t wmin = 0xFFFFFFFFu, wmax = 0u;
+    const int kk = rdx_emit_regs<NT, NGRP, 4, R>(
+        key, m, valid, st, sm, 0, [&](int slot, uint32_t rv, int r) {
+          const uint32_t kv = rv + lo;
+          words[slot] = ((uint64_t)kv << 32) | (uint64_t)(~pos[r]);
+          wmin = min(wmin, kv);
+          wmax = max(wmax, kv);
+        });
+    score_order_output<NT, NGRP>(words, slots, kk, k, wmin, wmax, sm, orow);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Candidate lists. SRC kSrcCand1: row r's list at cand + r*seg_cap, count
+// cand_count[r] (<= NT*R). SRC kSrcCandSeg: segments s0..s0+ns-1 of the row
+// (all of them, or group `grp` of nseg / ngroups consecutive ones), whose
+// concatenation is position-ordered. OUT: final indices (position or score
+// order, a.pos_order) or, kOutPart, the group's winners as (key, position)
+// pairs into a.part (count in a.part_count).
+// ---------------------------------------------------------------------------
+template <int SRC, int OUT, int NT, int R>
+__global__ __launch_bounds__(NT)
+void topk_pairs_kernel(TopkArgs a, int ngroups) {
+  constexpr int NGRP = R / 4;
+  __shared__ RdxSmem<NT, NGRP> sm;
+  __shared__ uint64_t words[OUT == kOutScore ? kMaxK : 2];
+  __shared__ uint16_t slots[OUT == kOutScore ? kMaxK : 2];
+  __shared__ int seg_off[kMaxSegments + 1];
+  const int tid = threadIdx.x;
+  const int row = (int)(blockIdx.x / (unsigned)ngroups);
+  const int grp = (int)(blockIdx.x % (unsigned)ngroups);
+  const int k = a.k;
+  rdx_clear(sm, kHistWords);
+  uint32_t key[R], pos[R];
+  int n;
+  if (SRC == kSrcCand1) {
+    // the list through a buffer resource of its n pairs (reads past them
+    // return 0): two 16-byte loads per group of four pairs, issued
+    // unconditionally; a partly valid last group is read again pair by pair
     n = a.cand_count[row];
     const u32x2* src = a.cand + (size_t)row * a.seg_cap;
-    int done = 0;
-    if ((reinterpret_cast<uintptr_t>(src) & 15) == 0) {
-      // 16-byte loads (2 pairs each), kBatch of them in flight per thread
-      const int n2 = n >> 1;
-      const u32x4* src2 = reinterpret_cast<const u32x4*>(src);
-      for (int base = 0; base < n2; base += NT * kBatch) {
-        u32x4 v[kBatch];
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u32x2*>(src), (short)0, n * 8, 0x00020000);
+    u32x4 p0[NGRP], p1[NGRP];
+    const int nvg = rdx_live_groups<NT>(n);
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          const int e = base + j * NT + tid;
-          v[j] = e < n2 ? src2[e] : u32x4{};
-        }
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          const int e = base + j * NT + tid;
-          if (e < n2) {
-            *reinterpret_cast<u32x2*>(skey + 2 * e) = u32x2{v[j][0], v[j][2]};
-            kmin = min(kmin, min(v[j][0], v[j][2]));
-            kmax = max(kmax, max(v[j][0], v[j][2]));
-          }
-        }
+    for (int v = 0; v < NGRP; ++v) {
+      const int g = tid + NT * v;
+      p0[v] = p1[v] = u32x4{0u, 0u, 0u, 0u};
+      if (v < nvg) {  // workgroup-uniform
+        p0[v] = __builtin_amdgcn_raw_buffer_load_b128(rs, g * 32, 0, 0);
+        p1[v] = __builtin_amdgcn_raw_buffer_load_b128(rs, g * 32 + 16, 0, 0);
       }
-      done = n2 * 2;
     }
-    for (int base = done; base < n; base += NT * kBatch) {
-      uint32_t v[kBatch];
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int e = base + j * NT + tid;
-        v[j] = e < n ? src[e].x : 0u;
+    for (int v = 0; v < NGRP; ++v) {
+      const int g = tid + NT * v;
+      if ((n & 3) != 0 && g == (n >> 2)) {
+        const u32x2 q0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, g * 32, 0, 0));
+        const u32x2 q1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, g * 32 + 8, 0, 0));
+        const u32x2 q2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, g * 32 + 16, 0, 0));
+        p0[v] = u32x4{q0[0], q0[1], q1[0], q1[1]};
+        p1[v] = u32x4{q2[0], q2[1], 0u, 0u};
       }
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int e = base + j * NT + tid;
-        if (e < n) {
-          skey[e] = v[j];
-          kmin = min(kmin, v[j]);
-          kmax = max(kmax, v[j]);
-        }
-      }
+      key[4 * v + 0] = p0[v][0];
+      pos[4 * v + 0] = p0[v][1];
+      key[4 * v + 1] = p0[v][2];
+      pos[4 * v + 1] = p0[v][3];
+      key[4 * v + 2] = p1[v][0];
+      pos[4 * v + 2] = p1[v][1];
+      key[4 * v + 3] = p1[v][2];
+      pos[4 * v + 3] = p1[v][3];
     }
   } else {
-    // segments [s0, s1) of the row: all of them (nchunks = 1), or group
-    // `chunk` of ceil(nseg / nchunks) consecutive segments (a stage of a
-    // two-level selection); consecutive segments keep position order
-    const int per_group = (a.nseg + nchunks - 1) / nchunks;
-    const int s0 = min(a.nseg, chunk * per_group);
+    const int per_group = (a.nseg + ngroups - 1) / ngroups;
+    const int s0 = min(a.nseg, grp * per_group);
     const int ns = min(a.nseg, s0 + per_group) - s0;
     if (tid == 0) {
       int off = 0;
       for (int s = 0; s < ns; ++s) {
-        sm.seg_off[s] = off;
-        off += a.cand_count[row * a.nseg + s0 + s];
+        seg_off[s] = off;
+        off += a.cand_count[(size_t)row * a.nseg + s0 + s];
       }
-      sm.seg_off[ns] = off;
+      seg_off[ns] = off;
     }
     __syncthreads();
-    n = sm.seg_off[ns];
-    spos = skey + a.stage_cap;
-    for (int s = 0; s < ns; ++s) {
-      const int off = sm.seg_off[s];
-      const int cnt = sm.seg_off[s + 1] - off;
-      const u32x2* src = a.cand + ((size_t)row * a.nseg + s0 + s) * a.seg_cap;
-      for (int base = 0; base < cnt; base += NT * kBatch) {
-        u32x2 v[kBatch];
+    n = seg_off[ns];
+    const u32x2* base = a.cand + ((size_t)row * a.nseg + s0) * a.seg_cap;
+    int s = 0;  // elements grow with r: the segment search resumes
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          const int e = base + j * NT + tid;
-          v[j] = e < cnt ? src[e] : u32x2{0u, 0u};
-        }
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          const int e = base + j * NT + tid;
-          if (e < cnt) {
-            skey[off + e] = v[j].x;
-            kmin = min(kmin, v[j].x);
-            kmax = max(kmax, v[j].x);
-            spos[off + e] = v[j].y;
-          }
-        }
+    for (int r = 0; r < R; ++r) {
+      const int e = elem_of<NT>(r);
+      u32x2 p = u32x2{0u, 0u};
+      if (e < n) {
+        while (s + 1 < ns && seg_off[s + 1] <= e) ++s;
+        p = base[(size_t)s * a.seg_cap + (e - seg_off[s])];
       }
+      key[r] = p[0];
+      pos[r] = p[1];
     }
   }
-  sel_store_key_range<NT>(kmin, kmax, sm.sel);
-  __syncthreads();
-
-  u32x2* part = nullptr;
-  if (OUT == kOutPart) part = a.part + ((size_t)row * nchunks + chunk) * a.k;
-  int32_t* orow = a.out + (size_t)row * k;
-  const bool pos_order = OUT == kOutFinal && a.pos_order;
-  const u32x2* cand1 = (SRC == kSrcCand1) ? a.cand + (size_t)row * a.seg_cap : nullptr;
-  // positions of a group of kSelPerThread consecutive entries (those of `bits`)
-  const bool cand1_aligned =
-      SRC == kSrcCand1 && (reinterpret_cast<uintptr_t>(cand1) & 15) == 0;
-  auto pos_group = [&](int e0, unsigned bits, uint32_t (&pv)[kSelPerThread]) {
-    if (SRC == kSrcRow) {
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, lo, hi;
 #pragma unroll
-      for (int j = 0; j < kSelPerThread; ++j) pv[j] = (uint32_t)(pos0 + e0 + j);
-    } else if (SRC == kSrcCand) {
-#pragma unroll
-      for (int j = 0; j < kSelPerThread; ++j) pv[j] = ((bits >> j) & 1u) ? spos[e0 + j] : 0u;
-    } else if (cand1_aligned && bits != 0u && e0 + kSelPerThread <= n) {
-      // the group's pairs in four 16-byte loads (positions are the odd words)
-      const u32x4* g = reinterpret_cast<const u32x4*>(cand1 + e0);
-#pragma unroll
-      for (int q = 0; q < kSelPerThread / 2; ++q) {
-        const u32x4 w = g[q];
-        pv[2 * q] = w[1];
-        pv[2 * q + 1] = w[3];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kSelPerThread; ++j) pv[j] = ((bits >> j) & 1u) ? cand1[e0 + j].y : 0u;
+  for (int r = 0; r < R; ++r) {
+    if (elem_of<NT>(r) < n) {
+      kmin = min(kmin, key[r]);
+      kmax = max(kmax, key[r]);
     }
-  };
-  uint32_t wmin = 0xFFFFFFFFu, wmax = 0u;  // score order: this thread's winners' key range
-  const int kk = block_topk_collect<NT>(
-      skey, n, k, sm.sel, pos_group, [&](int slot, uint32_t key, uint32_t pos) {
-        if (OUT == kOutPart) {
-          part[slot] = u32x2{key, pos};
-        } else if (pos_order) {
-          orow[slot] = (int32_t)pos;
-        } else {
-          sortbuf[slot] = (((uint64_t)key) << 32) | (uint64_t)(~pos);
-          wmin = min(wmin, key);
-          wmax = max(wmax, key);
-        }
-      },
-      /*range_ready=*/true);
+  }
+  rdx_key_range(kmin, kmax, sm, lo, hi);  // its barrier also ends the clear
+  auto valid = [&](int r) { return elem_of<NT>(r) < n; };
+#pragma unroll
+  for (int r = 0; r < R; ++r) key[r] = valid(r) ? key[r] - lo : 0u;  // rel, padded
+  RdxState st = rdx_start(n, k, lo, hi);
+  rdx_search_regs<NT, NGRP, R>(key, n, sm, st);
   if (OUT == kOutPart) {
-    if (tid == 0) a.part_count[row * nchunks + chunk] = kk;
+    u32x2* part = a.part + ((size_t)row * ngroups + grp) * k;
+    const int kk = rdx_emit_regs<NT, NGRP, 4, R>(
+        key, n, valid, st, sm, 0,
+        [&](int slot, uint32_t rv, int r) { part[slot] = u32x2{rv + lo, pos[r]}; });
+    if (tid == 0) a.part_count[(size_t)row * ngroups + grp] = kk;
     return;
   }
-  if (pos_order) {  // winners are emitted in position order: no sort
+  int32_t* orow = a.out + (size_t)row * k;
+  if (OUT == kOutPos) {
+    const int kk = rdx_emit_regs<NT, NGRP, 4, R>(
+        key, n, valid, st, sm, 0, [&](int slot, uint32_t, int r) { orow[slot] = (int32_t)pos[r]; });
     for (int j = kk + tid; j < k; j += NT) orow[j] = -1;
-    return;
-  }
-
-  // ---- score order. Wide workgroups (the final stage of long rows) rank by
-  // buckets when the scores are spread out, with every wave busy (the staged
-  // keys are no longer read, so their LDS is the scratch); otherwise, and in
-  // 256-thread workgroups, where it measured faster, a bitonic sort,
-  // descending, of the kk winners padded to a power of two.
-  if (NT > kThreads && kk >= 512 && stage_bytes >= kBucketScratchBytes) {
-    sel_store_key_range<NT>(wmin, wmax, sm.sel);
-    __syncthreads();
-    uint32_t wlo = sm.sel.kred[0], whi = sm.sel.kred[NT / kWave];
-#pragma unroll
-    for (int w = 1; w < NT / kWave; ++w) {
-      wlo = min(wlo, sm.sel.kred[w]);
-      whi = max(whi, sm.sel.kred[NT / kWave + w]);
-    }
-    if (bucket_rank_output<NT>(sortbuf, kk, k, wlo, whi, skey, sm.sel, orow)) return;
-  }
-  int P = 1;
-  while (P < kk) P <<= 1;
-  static_assert(kMaxK == 8 * kThreads && NT % kThreads == 0, "register sort layout");
-  if (P >= 512) {
-    // the register sort of all 2048 slots, the ones past kk zero (every
-    // winner's word is nonzero, so they sort last)
-    const bool act = NT == kThreads || tid < kThreads;
-    __syncthreads();
-    uint64_t v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int idx = tid * 8 + j;
-      v[j] = (act && idx < kk) ? sortbuf[idx] : 0ull;
-    }
-    sort2048_regs(v, sortbuf, tid, act);
-    if (act) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int idx = tid * 8 + j;
-        if (idx < k) orow[idx] = (idx < kk) ? (int32_t)(~(uint32_t)(v[j] & 0xFFFFFFFFull)) : -1;
-      }
-    }
-    return;
-  }
-  for (int e = kk + tid; e < P; e += NT) sortbuf[e] = 0ull;
-  __syncthreads();
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < (P >> 1); i += NT) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const uint64_t x = sortbuf[lo], y = sortbuf[hi];
-        const bool desc = (lo & size) == 0;
-        if ((x < y) == desc) {
-          sortbuf[lo] = y;
-          sortbuf[hi] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
-
-  for (int j = tid; j < k; j += NT) {
-    orow[j] = (j < kk) ? (int32_t)(~(uint32_t)(sortbuf[j] & 0xFFFFFFFFull)) : -1;
+  } else {
+    uint32_t wmin = 0xFFFFFFFFu, wmax = 0u;
+    const int kk = rdx_emit_regs<NT, NGRP, 4, R>(
+        key, n, valid, st, sm, 0, [&](int slot, uint32_t rv, int r) {
+          const uint32_t kv = rv + lo;
+          words[slot] = ((uint64_t)kv << 32) | (uint64_t)(~pos[r]);
+          wmin = min(wmin, kv);
+          wmax = max(wmax, kv);
+        });
+    score_order_output<NT, NGRP>(words, slots, kk, k, wmin, wmax, sm, orow);
   }
 }
 
-// stage_bytes: the staged input, after the scratch or, for score-order
-// output, after the sort buffer laid over the histogram
-template <int SRC, int OUT, int NT = kThreads>
-hipError_t launch_one(const TopkArgs& a, int chunk_len, int nchunks, size_t stage_bytes,
-                      hipStream_t st) {
-  static_assert(sort_off<NT>() % 16 == 0, "aligned sort buffer");
-  const bool need_sort = OUT == kOutFinal && !a.pos_order;
-  size_t stage_off = smem_bytes<NT>();
-  if (need_sort && sort_off<NT>() + kSortBytes > stage_off) stage_off = sort_off<NT>() + kSortBytes;
-  const size_t shmem = stage_off + (stage_bytes + 15) / 16 * 16;
-  auto fn = topk_kernel<SRC, OUT, NT>;
-  if (shmem > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(fn, dim3((unsigned)(a.rows * nchunks)), dim3(NT), shmem, st, a,
-                     chunk_len, nchunks, (int)stage_off, (int)stage_bytes);
+template <int SRC, int OUT, int NT, int R>
+hipError_t launch_pairs(const TopkArgs& a, int ngroups, hipStream_t st) {
+  hipLaunchKernelGGL((topk_pairs_kernel<SRC, OUT, NT, R>), dim3((unsigned)(a.rows * ngroups)),
+                     dim3(NT), 0, st, a, ngroups);
+  return hipGetLastError();
+}
+
+template <int SRC, int NT, int R>
+hipError_t launch_pairs_final(const TopkArgs& a, int ngroups, hipStream_t st) {
+  return a.pos_order ? launch_pairs<SRC, kOutPos, NT, R>(a, ngroups, st)
+                     : launch_pairs<SRC, kOutScore, NT, R>(a, ngroups, st);
+}
+
+size_t long_lds_bytes() {
+  constexpr size_t off =
+      (sizeof(RdxSmem<kWideThreads, kWideR / 4>) + 15) / 16 * 16;
+  return off + (size_t)kLongCap * 8;
+}
+
+template <int OUT>
+hipError_t launch_long(const TopkArgs& a, int nch, hipStream_t st) {
+  const size_t shmem = long_lds_bytes();
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_long_kernel<OUT>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+  if (e != hipSuccess) return e;
+  const int B = a.rows / a.Lq;
+  hipLaunchKernelGGL((topk_long_kernel<OUT>), dim3((unsigned)a.rows), dim3(kWideThreads), shmem,
+                     st, a.scores, B, a.Lq, a.Lk, a.q_pos0, a.k, nch,
+                     reinterpret_cast<const uint32_t*>(a.ghist), a.out);
   return hipGetLastError();
 }
 
@@ -540,9 +701,10 @@ hipError_t launch_one(const TopkArgs& a, int chunk_len, int nchunks, size_t stag
 int topk_row_chunks(int Lk) { return (Lk + kTopkChunk - 1) / kTopkChunk; }
 
 size_t topk_part_bytes(int rows, int Lk, int k) {
+  (void)k;
   const int nch = topk_row_chunks(Lk);
   if (nch <= 1) return 0;
-  return (size_t)rows * nch * k * 8 + (size_t)rows * nch * 4 + 256;
+  return (size_t)rows * nch * kHistWords * 4;
 }
 
 int topk_segment_groups(int nseg, int k) {
@@ -558,53 +720,45 @@ size_t topk_group_bytes(int rows, int nseg, int k) {
   return (size_t)rows * g * k * 8 + (size_t)rows * g * 4 + 256;
 }
 
-hipError_t launch_topk(const TopkArgs& a0, hipStream_t st) {
-  TopkArgs a = a0;
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.cand) {
-    // candidate lists (one or more position-ordered segments per row); keys,
-    // then positions when there are several segments, each area a multiple
-    // of 16 bytes
     if (a.nseg == 1) {
-      a.stage_cap = (a.stage_cap + 3) / 4 * 4;
-      return launch_one<kSrcCand1, kOutFinal>(a, 0, 1, (size_t)a.stage_cap * 4, st);
+      // one position-ordered list per row (the fused indexer's candidates)
+      if (a.stage_cap <= kTopkChunk) return launch_pairs_final<kSrcCand1, kRowThreads, kRowR>(a, 1, st);
+      return launch_pairs_final<kSrcCand1, kWideThreads, kWideR>(a, 1, st);
     }
     const int groups = topk_segment_groups(a.nseg, a.k);
-    if (groups <= 1) {
-      a.stage_cap = (a.stage_cap + 3) / 4 * 4;
-      return launch_one<kSrcCand, kOutFinal, kThreadsWide>(a, 0, 1, (size_t)a.stage_cap * 8,
-                                                           st);
-    }
+    if (groups <= 1) return launch_pairs_final<kSrcCandSeg, kWideThreads, kWideR>(a, 1, st);
     // too many segments for one workgroup: the exact top-k of each group of
     // consecutive segments (into a.part), then of the groups' winners (every
     // key of the row's top-k is in its group's top-k)
-    TopkArgs g = a;
-    const int per_group = (a.nseg + groups - 1) / groups;
-    g.stage_cap = (per_group * a.k + 3) / 4 * 4;
-    hipError_t e = launch_one<kSrcCand, kOutPart, kThreadsWide>(g, 0, groups,
-                                                                (size_t)g.stage_cap * 8, st);
+    hipError_t e = launch_pairs<kSrcCandSeg, kOutPart, kWideThreads, kWideR>(a, groups, st);
     if (e != hipSuccess) return e;
     TopkArgs f = a;
     f.cand = a.part;
     f.cand_count = a.part_count;
     f.nseg = groups;
     f.seg_cap = a.k;
-    f.stage_cap = (groups * a.k + 3) / 4 * 4;
-    return launch_one<kSrcCand, kOutFinal, kThreadsWide>(f, 0, 1, (size_t)f.stage_cap * 8, st);
+    return launch_pairs_final<kSrcCandSeg, kWideThreads, kWideR>(f, 1, st);
   }
+  const int B = a.rows / a.Lq;
   const int nch = topk_row_chunks(a.Lk);
   if (nch <= 1) {
-    return launch_one<kSrcRow, kOutFinal>(a, kTopkChunk, 1, (size_t)kTopkChunk * 4, st);
+    if (a.pos_order)
+      hipLaunchKernelGGL((topk_rows_kernel<kOutPos>), dim3((unsigned)a.rows), dim3(kRowThreads), 0,
+                         st, a.scores, B, a.Lq, a.Lk, a.q_pos0, a.k, a.out);
+    else
+      hipLaunchKernelGGL((topk_rows_kernel<kOutScore>), dim3((unsigned)a.rows),
+                         dim3(kRowThreads), 0, st, a.scores, B, a.Lq, a.Lk, a.q_pos0, a.k, a.out);
+    return hipGetLastError();
   }
-  // long rows: exact top-k per chunk, then top-k of the chunks' winners
-  hipError_t e = launch_one<kSrcRow, kOutPart>(a, kTopkChunk, nch, (size_t)kTopkChunk * 4, st);
+  // long rows: per-chunk histograms of the top digit, then one workgroup per row
+  hipLaunchKernelGGL(topk_chunk_hist_kernel, dim3((unsigned)((size_t)a.rows * nch)),
+                     dim3(kRowThreads), 0, st, a.scores, a.Lq, a.Lk, a.q_pos0, nch,
+                     reinterpret_cast<uint32_t*>(a.ghist));
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  TopkArgs b = a;
-  b.cand = a.part;
-  b.cand_count = a.part_count;
-  b.nseg = nch;
-  b.seg_cap = a.k;
-  b.stage_cap = (nch * a.k + 3) / 4 * 4;
-  return launch_one<kSrcCand, kOutFinal, kThreadsWide>(b, 0, 1, (size_t)b.stage_cap * 8, st);
+  return a.pos_order ? launch_long<kOutPos>(a, nch, st) : launch_long<kOutScore>(a, nch, st);
 }
 
 }  // namespace idxc
