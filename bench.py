@@ -44,9 +44,11 @@ def parse():
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--only", default="",
-                    help="prefill-12f | prefill-allf | decode | sweep | pmc (profiling)")
+                    help="prefill-12f | prefill-allf | decode | sweep | pmc | dispatch (profiling)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CMD_F", "CMD_W"),
                     help="write profiles/hbm_traffic.md from the two counter passes (no GPU)")
+    ap.add_argument("--dispatch-summary", nargs=2, metavar=("TRACE_CSV", "CMD"),
+                    help="write profiles/dispatch_counts.md from a --only dispatch kernel trace")
     return ap.parse_args()
 
 
@@ -369,50 +371,222 @@ def standalone_topk(B, Lq, Lk, q_pos0, k, seed=0, order="score"):
 
 
 # --------------------------------------------------------------------------- #
-# CPU oracle baseline on a bounded sample
+# CPU oracle baseline on bounded samples (the only leg that runs the oracle)
 # --------------------------------------------------------------------------- #
+def host_info():
+    """Host cores, CPU model and the BLAS build numpy runs on."""
+    info = {"nproc": os.cpu_count()}
+    try:
+        info["affinity_cpus"] = len(os.sched_getaffinity(0))
+    except Exception:
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+    except Exception:
+        pass
+    try:
+        import numpy as np
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = "%s %s (%s), %d threads" % (
+                blas[0].get("internal_api"), blas[0].get("version"),
+                blas[0].get("architecture"), int(blas[0].get("num_threads", 1)))
+            info["blas_threads"] = int(blas[0].get("num_threads", 1))
+        info["numpy"] = np.__version__
+    except Exception:
+        pass
+    return info
+
+
+def _oracle_row_times(q_idx, k_idx, w, Q, K, V, rows, k, scale, q_pos0, attn=True):
+    """Oracle time per sampled query row (indexer + top-k, and attention), and
+    the oracle's index sets of those rows. Row j of q_idx / w / Q is query
+    position q_pos0 + rows[j] of keys k_idx / K / V (all fp64, batch 1)."""
+    import oracle
+    t_idx = t_att = 0.0
+    sets = []
+    for j, i in enumerate(rows):
+        t = q_pos0 + int(i)
+        t0 = time.perf_counter()
+        sc = oracle.indexer_scores(q_idx[:, j:j + 1], k_idx, w[:, j:j + 1], t)
+        idx = oracle.topk(sc, k, t)
+        t1 = time.perf_counter()
+        if attn:
+            oracle.sparse_attention(Q[:, j:j + 1], K, V, idx, scale)
+        t2 = time.perf_counter()
+        t_idx += t1 - t0
+        t_att += t2 - t1
+        sets.append(idx[0, 0])
+    n = max(1, len(rows))
+    return t_idx / n, t_att / n, sets
+
+
+def _gpu_overlap(gpu_rows, oracle_rows):
+    import oracle
+    import numpy as np
+    ovs = [oracle.overlap(g, w) for g, w in zip(gpu_rows, oracle_rows)]
+    return {"rows": len(ovs), "mean": float(np.mean(ovs)), "min": float(np.min(ovs))}
+
+
 def cpu_baseline(cfg, n_rows=4096):
     """Time the oracle (as it stands) on n_rows query rows of one F layer and
-    one S layer of the prefill stack, then compose the 47-layer stack time."""
+    one S layer of the prefill stack, then compose the 47-layer stack time.
+    The same rows give the GPU-against-oracle top-k overlap of that layer (the
+    GPU runs on copies of the same inputs)."""
     import numpy as np
     import torch
     import idxc_inputs as gen
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    import dsa_lightning_indexer_score_amd as idxc
+    host = host_info()
     L = gen.layer_inputs(cfg, 0, device="cpu")
     rows = np.unique(np.linspace(0, cfg.Lq - 1, n_rows).astype(int))
-    k_idx = gen.to_f64(L["k_idx"])
-    Kf, Vf = gen.to_f64(L["k"]), gen.to_f64(L["v"])
-    t_f = t_s = 0.0
-    for i in rows:
-        q_idx = gen.to_f64(L["q_idx"][:, i:i + 1])
-        w = gen.to_f64(L["w"][:, i:i + 1])
-        Q = gen.to_f64(L["q"][:, i:i + 1])
-        t0 = time.perf_counter()
-        sc = oracle.indexer_scores(q_idx, k_idx, w, cfg.q_pos0 + int(i), cfg.Lk)
-        idx = oracle.topk(sc, cfg.k, cfg.q_pos0 + int(i))
-        t1 = time.perf_counter()
-        oracle.sparse_attention(Q, Kf, Vf, idx, cfg.scale)
-        t2 = time.perf_counter()
-        t_f += t1 - t0
-        t_s += t2 - t1
-    # rows are spread uniformly over positions, so the mean per-row time times
-    # Lq estimates one layer
-    per_row_idx = t_f / len(rows)
-    per_row_att = t_s / len(rows)
+    f = gen.to_f64
+    t_idx, t_att, sets = _oracle_row_times(
+        f(L["q_idx"][:, rows]), f(L["k_idx"]), f(L["w"][:, rows]), f(L["q"][:, rows]), f(L["k"]),
+        f(L["v"]), rows, cfg.k, cfg.scale, cfg.q_pos0)
+    # per-row times of rows spread evenly over the positions, times Lq, give a layer
     nF = cfg.pattern.count("F")
-    stack_s = cfg.B * cfg.Lq * (nF * per_row_idx + cfg.n_layers * per_row_att)
+    stack_s = cfg.B * cfg.Lq * (nF * t_idx + cfg.n_layers * t_att)
+    allf_s = cfg.B * cfg.Lq * cfg.n_layers * (t_idx + t_att)
+    # GPU selection of the same layer (same tensors) on the same rows
+    gi = idxc.idxc_indexer_topk(L["q_idx"].cuda(), L["k_idx"].cuda(), L["w"].cuda(), cfg.k,
+                                q_pos0=cfg.q_pos0)
+    ov = _gpu_overlap(gi[0, rows].cpu().numpy(), sets)
+    del gi
+    torch.cuda.empty_cache()
+    cores = host.get("blas_threads") or os.cpu_count() or 1
     return dict(value=cfg.B * cfg.Lq / stack_s, unit="tokens/s", cores=int(cores), kind="oracle",
                 sample="%d query rows (evenly spaced over positions 0..%d) of one F layer "
                        "(indexer+top-k+attention) and attention of one S layer of %s; "
                        "per-row times composed to the 47-layer stack (%d F, %d layers); "
                        "measured %.1f s" % (len(rows), cfg.Lq - 1, cfg.name, nF, cfg.n_layers,
-                                           t_f + t_s),
-                composed_stack_seconds=stack_s)
+                                           len(rows) * (t_idx + t_att)),
+                composed_stack_seconds=stack_s,
+                allF_tokens_per_s_composed=cfg.B * cfg.Lq / allf_s,
+                host=host, gpu_vs_oracle_topk_overlap=ov)
+
+
+def cpu_baselines_other():
+    """The oracle on the other configurations, each on a bounded sample:
+    the single 8192-token layer (1024 sampled rows, composed to the layer),
+    the 47-layer decode step (8 sequences of 65536 cached tokens, composed per
+    sequence to 64 sequences and 47 layers, 12-F and all-F), and the
+    196608-token indexer + top-k in 4096-query chunks (8 rows of the first and
+    8 of the last chunk; the per-row cost, linear in the row's keys, is fitted
+    and summed over all rows: extrapolated). GPU-against-oracle top-k overlap
+    on the same rows of the single layer and the decode batch."""
+    import numpy as np
+    import torch
+    import idxc_inputs as gen
+    import dsa_lightning_indexer_score_amd as idxc
+    f = gen.to_f64
+    out = {}
+    # ---- single layer, L = 8192
+    c2 = gen.C2
+    L = gen.layer_inputs(c2, 0, device="cpu")
+    rows = np.unique(np.linspace(0, c2.Lq - 1, 1024).astype(int))
+    t0 = time.perf_counter()
+    ti, ta, sets = _oracle_row_times(f(L["q_idx"][:, rows]), f(L["k_idx"]), f(L["w"][:, rows]),
+                                     f(L["q"][:, rows]), f(L["k"]), f(L["v"]), rows, c2.k,
+                                     c2.scale, 0)
+    layer_s = c2.Lq * (ti + ta)
+    gi = idxc.idxc_indexer_topk(L["q_idx"].cuda(), L["k_idx"].cuda(), L["w"].cuda(), c2.k)
+    out[c2.name] = {"tokens_per_s": c2.Lq / layer_s, "kind": "composed",
+                    "sample": "%d evenly spaced rows of the layer, per-row times x %d rows"
+                              % (len(rows), c2.Lq),
+                    "measured_s": time.perf_counter() - t0,
+                    "gpu_vs_oracle_topk_overlap": _gpu_overlap(gi[0, rows].cpu().numpy(), sets)}
+    del gi, L
+    # ---- decode step: 8 sequences of the 64 (same distributions, own seeds)
+    c4 = gen.C4_12F
+    nb = 8
+    q, kk, w = gen.indexer_inputs(nb, 1, c4.Lk, c4.H_I, c4.d_I, kind="normal", seed=100)
+    Q, K, V = gen.attn_inputs(nb, 1, c4.Lk, c4.H, c4.D, seed=101)
+    t0 = time.perf_counter()
+    ti = ta = 0.0
+    sets = []
+    for b in range(nb):
+        a, bb, st = _oracle_row_times(f(q[b:b + 1]), f(kk[b:b + 1]), f(w[b:b + 1]),
+                                      f(Q[b:b + 1]), f(K[b:b + 1]), f(V[b:b + 1]), [0], c4.k,
+                                      c4.scale, c4.q_pos0)
+        ti += a / nb
+        ta += bb / nb
+        sets.append(st[0])
+    step12 = c4.B * (12 * ti + 47 * ta)
+    stepF = c4.B * 47 * (ti + ta)
+    gi = idxc.idxc_indexer_topk(q.cuda(), kk.cuda(), w.cuda(), c4.k, q_pos0=c4.q_pos0)
+    out["stack47-decode-B64-Lk65536"] = {
+        "tokens_per_s_12F": c4.B / step12, "tokens_per_s_allF": c4.B / stepF,
+        "kind": "composed",
+        "sample": "%d sequences; per-sequence F-layer (indexer+top-k+attention) and S-layer "
+                  "(attention) times composed to 64 sequences x 47 layers" % nb,
+        "measured_s": time.perf_counter() - t0,
+        "gpu_vs_oracle_topk_overlap": _gpu_overlap(gi[:, 0].cpu().numpy(), sets)}
+    del q, kk, w, Q, K, V, gi
+    # ---- long context: rows of the first and the last 4096-query chunk
+    Lc, chunk = gen.C5_L, gen.C5_CHUNK
+    kf = f(gen.indexer_inputs(1, 1, Lc, 64, 128, kind="normal", seed=200)[1])
+    t0 = time.perf_counter()
+    pts = []
+    for c0 in (0, Lc - chunk):
+        rows = np.linspace(0, chunk - 1, 8).astype(int)
+        qq, _, ww = gen.indexer_inputs(1, len(rows), Lc, 64, 128, kind="normal", seed=201 + c0)
+        ti, _, _ = _oracle_row_times(f(qq), kf, f(ww), None, None, None, rows, 2048, 0.0, c0,
+                                     attn=False)
+        pts.append((c0 + chunk / 2.0, ti))
+    (x0, y0), (x1, y1) = pts
+    slope = (y1 - y0) / (x1 - x0)
+    inter = y0 - slope * x0
+    total = Lc * inter + slope * Lc * (Lc + 1) / 2.0
+    out["long-context-L196608-indexer-topk"] = {
+        "tokens_per_s": Lc / total, "kind": "extrapolated", "seconds": total,
+        "sample": "8 rows of the first and 8 of the last 4096-query chunk; per-row time "
+                  "fitted linear in the row position and summed over all %d rows" % Lc,
+        "measured_s": time.perf_counter() - t0}
+    return out
+
+
+def overlap_records():
+    """Cross-layer agreement of the layers' own selections (what an S layer
+    would keep of its own top-k if it reused another layer's), for the 7
+    distinct synthetic layers the benchmark cycles: idxc_overlap_matrix over
+    each layer's own top-k of the last 1024 prefill rows (L = 32768) and of
+    the 64 decode rows. Synthetic layers are independent draws, so these
+    measure the chance agreement of i.i.d. layers (about k / t), not the
+    pages' trained-model overlap."""
+    import numpy as np
+    import torch
+    import idxc_inputs as gen
+    import dsa_lightning_indexer_score_amd as idxc
+    res = {}
+    for cfg, nrows in ((gen.C3_12F, 1024), (gen.C4_12F, None)):
+        sel = []
+        for s in range(N_SETS):
+            L = gen.layer_inputs(cfg, s, device="cuda")
+            if nrows:
+                q0 = cfg.Lq - nrows
+                sel.append(idxc.idxc_indexer_topk(L["q_idx"][:, q0:], L["k_idx"], L["w"][:, q0:],
+                                                  cfg.k, q_pos0=q0, order="position"))
+            else:
+                sel.append(idxc.idxc_indexer_topk(L["q_idx"], L["k_idx"], L["w"], cfg.k,
+                                                  q_pos0=cfg.q_pos0, order="position"))
+            del L
+        sel = torch.stack(sel).contiguous()
+        m = idxc.idxc_overlap_matrix(sel, cfg.Lk).cpu().numpy()
+        order = [l % N_SETS for l in range(cfg.n_layers)]
+        adj = [float(m[order[l], order[l + 1]]) for l in range(cfg.n_layers - 1)
+               if order[l] != order[l + 1]]
+        res[cfg.name.rsplit("-", 1)[0]] = {
+            "rows": int(sel.shape[1] * sel.shape[2]), "layers": N_SETS,
+            "adjacent_layer_overlap_mean": float(np.mean(adj)),
+            "matrix": [[round(float(x), 5) for x in r] for r in m]}
+        del sel
+        torch.cuda.empty_cache()
+    return res
 
 
 # --------------------------------------------------------------------------- #
@@ -541,10 +715,125 @@ def pmc_summary(fetch_csv, write_csv, command_fetch, command_write):
 
 
 # --------------------------------------------------------------------------- #
+# dispatch counts: rocprofv3 --kernel-trace --output-format csv -- python3 bench.py --only dispatch
+# --------------------------------------------------------------------------- #
+DISPATCH_PHASES = ["prefill 12-F step", "prefill all-F step", "decode 12-F step",
+                   "decode all-F step", "long-context pass (48 chunks of 4096)"]
+
+
+def dispatch_launches():
+    """One step of each stack configuration and one long-context pass, each
+    preceded by a marker kernel (a fill), for a kernel trace that counts the
+    indexer dispatches per step."""
+    import torch
+    import idxc_inputs as gen
+    import dsa_lightning_indexer_score_amd as idxc
+
+    def mark(i):
+        torch.cuda.synchronize()
+        torch.full((1024 * (i + 1),), float(i), device="cuda")
+        torch.cuda.synchronize()
+
+    steps = []
+    for c12, cF in ((gen.C3_12F, gen.C3_ALLF), (gen.C4_12F, gen.C4_ALLF)):
+        layers, sets = build_stack(c12, N_SETS)
+        ws = torch.empty(idxc.idxc_workspace_bytes(c12.B, c12.Lq, c12.Lk, c12.q_pos0, c12.H_I,
+                                                   c12.d_I, c12.k, c12.H, c12.D),
+                         dtype=torch.uint8, device="cuda")
+        cache = torch.empty((c12.B, c12.Lq, c12.k), dtype=torch.int32, device="cuda")
+        for c in (c12, cF):
+            call = idxc.StackCall(c.pattern, layers, c.k, c.scale, c.q_pos0, index_cache=cache,
+                                  workspace=ws)
+            call()  # warm-up (not traced apart: the markers delimit the counted step)
+            steps.append((call, layers, sets, ws, cache))
+    Lc, chunk = gen.C5_L, gen.C5_CHUNK
+    q, kk, w = gen.indexer_inputs(1, Lc, Lc, 64, 128, kind="normal", seed=0, device="cuda")
+    wsl = torch.empty(idxc.idxc_workspace_bytes(1, chunk, Lc, Lc - chunk, 64, 128, 2048),
+                      dtype=torch.uint8, device="cuda")
+    outl = torch.empty((1, chunk, 2048), dtype=torch.int32, device="cuda")
+
+    def long_pass():
+        for c in range(Lc // chunk):
+            idxc.idxc_indexer_topk(q[:, c * chunk:(c + 1) * chunk], kk[:, :(c + 1) * chunk],
+                                   w[:, c * chunk:(c + 1) * chunk], 2048, q_pos0=c * chunk,
+                                   workspace=wsl, out=outl)
+    long_pass()
+    calls = [st[0] for st in steps]
+    for i, fn in enumerate(calls + [long_pass]):
+        mark(i)
+        n = fn()
+        torch.cuda.synchronize()
+        log("dispatch phase %d (%s) done%s" % (i, DISPATCH_PHASES[i],
+                                              "" if n is None else ", indexer_calls=%d" % n))
+    mark(len(calls) + 1)
+
+
+def dispatch_summary(trace_csv, command):
+    """Write profiles/dispatch_counts.md from the kernel trace of --only dispatch."""
+    import csv
+    import idxc_inputs as gen
+    rows = list(csv.DictReader(open(trace_csv)))
+    key = lambda r: int(r.get("Dispatch_Id") or r.get("Correlation_Id") or 0)
+    rows.sort(key=key)
+    names = [r["Kernel_Name"] for r in rows]
+    marks = [i for i, n in enumerate(names) if "FillFunctor" in n]
+    # the last len(DISPATCH_PHASES)+1 fills delimit the phases
+    marks = marks[-(len(DISPATCH_PHASES) + 1):]
+    assert len(marks) == len(DISPATCH_PHASES) + 1, "markers not found"
+
+    def kind(n):
+        n = n.replace("(anonymous namespace)::", "")
+        if "indexer_" in n:
+            return "indexer"
+        if "topk_" in n:
+            return "top-k selection"
+        if "attn_merge" in n:
+            return "attention merge"
+        if "attn" in n:
+            return "attention"
+        return None
+
+    expect_f = [gen.C3_12F.pattern.count("F"), 47, gen.C4_12F.pattern.count("F"), 47,
+                gen.C5_L // gen.C5_CHUNK]
+    lines = ["# Indexer dispatches per step (rocprofv3 kernel trace)", "",
+             "Command: `%s`" % command, "",
+             "Each phase is one step of the stack (or one pass of the long context) between "
+             "two marker kernels; S layers launch no indexer work, so the indexer dispatches "
+             "of a step equal its F layers (12 of 47 for the 12-F pattern, 47 for all-F), "
+             "and a 196608-token pass in 4096-query chunks dispatches one indexer launch per "
+             "chunk (48).", "",
+             "| phase | F layers (or chunks) | indexer | top-k selection | attention | "
+             "attention merge | indexer = F |", "|---|---|---|---|---|---|---|"]
+    ok_all = True
+    rec = {}
+    for p in range(len(DISPATCH_PHASES)):
+        cnt = {}
+        for n in names[marks[p] + 1:marks[p + 1]]:
+            k = kind(n)
+            if k:
+                cnt[k] = cnt.get(k, 0) + 1
+        ok = cnt.get("indexer", 0) == expect_f[p]
+        ok_all &= ok
+        rec[DISPATCH_PHASES[p]] = cnt
+        lines.append("| %s | %d | %d | %d | %d | %d | %s |" % (
+            DISPATCH_PHASES[p], expect_f[p], cnt.get("indexer", 0), cnt.get("top-k selection", 0),
+            cnt.get("attention", 0), cnt.get("attention merge", 0), "yes" if ok else "NO"))
+    lines += ["", "All phases: indexer dispatches = F layers (chunks): %s" % ("yes" if ok_all
+                                                                             else "NO"),
+              "", "dispatch-json: " + json.dumps(rec, sort_keys=True), ""]
+    path = os.path.join(ROOT, "profiles", "dispatch_counts.md")
+    open(path, "w").write("\n".join(lines))
+    print("\n".join(lines))
+
+
+# --------------------------------------------------------------------------- #
 def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return
+    if args.dispatch_summary:
+        dispatch_summary(*args.dispatch_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -560,6 +849,9 @@ def main():
     log("library %s on %s" % (idxc.idxc_version(), torch.cuda.get_device_name(0)))
     if args.only == "pmc":
         pmc_launches()
+        return
+    if args.only == "dispatch":
+        dispatch_launches()
         return
     if args.only == "sweep":
         print(json.dumps({"context_sweep": context_sweep(), "distill_loss": distill_rate()}),
@@ -670,6 +962,12 @@ def main():
                tk["decode_rows_position_order"]["GBs"], tk["prefill_rows_position_order"]["GBs"]))
         extra["standalone_topk"] = tk
         torch.cuda.empty_cache()
+        extra["cross_layer_overlap"] = overlap_records()
+        log("cross-layer overlap of the 7 synthetic layers' own selections: prefill %.4f, "
+            "decode %.4f (adjacent layers, mean)"
+            % (extra["cross_layer_overlap"]["stack47-prefill-L32768"]["adjacent_layer_overlap_mean"],
+               extra["cross_layer_overlap"]["stack47-decode-B64-Lk65536"]["adjacent_layer_overlap_mean"]))
+        torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ report
     cfg = gen.C3_12F
@@ -737,7 +1035,15 @@ def main():
     if not args.skip_cpu:
         log("timing the CPU oracle on a bounded sample ...")
         cpu = cpu_baseline(cfg)
-        log("cpu oracle: %.3g tokens/s on %d threads" % (cpu["value"], cpu["cores"]))
+        log("cpu oracle: %.3g tokens/s on %d threads; GPU-vs-oracle overlap on %d rows: mean "
+            "%.5f min %.5f" % (cpu["value"], cpu["cores"], cpu["gpu_vs_oracle_topk_overlap"]["rows"],
+                               cpu["gpu_vs_oracle_topk_overlap"]["mean"],
+                               cpu["gpu_vs_oracle_topk_overlap"]["min"]))
+        if args.only == "":
+            extra["cpu_baseline_other"] = cpu_baselines_other()
+            log("cpu oracle, other configurations: %s" % json.dumps(
+                {k: v.get("tokens_per_s", v.get("tokens_per_s_12F"))
+                 for k, v in extra["cpu_baseline_other"].items()}))
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
