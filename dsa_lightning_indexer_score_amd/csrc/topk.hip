@@ -396,15 +396,25 @@ void topk_long_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, i
     // level 0 (the top 11 bits) from the chunk histograms, as 32-bit sums
     RdxState st = rdx_start(n, k, 0u, 0xFFFFFFFFu);
     const int nc = (n + kTopkChunk - 1) / kTopkChunk;
-    for (int w = tid; w < kHistWords; w += NT) {
+    static_assert(kHistWords == NT, "one histogram word per thread");
+    {
+      // the chunks' words, kSumBatch loads in flight per thread
+      constexpr int kSumBatch = 8;
+      const uint32_t* gw = ghist + row * nch * kHistWords + tid;
       uint32_t lo = 0u, hi = 0u;
-      for (int c = 0; c < nc; ++c) {
-        const uint32_t v = ghist[(row * nch + c) * kHistWords + w];
-        lo += v & 0xFFFFu;
-        hi += v >> 16;
+      for (int c0 = 0; c0 < nc; c0 += kSumBatch) {
+        uint32_t v[kSumBatch];
+#pragma unroll
+        for (int q = 0; q < kSumBatch; ++q)
+          v[q] = c0 + q < nc ? gw[(size_t)(c0 + q) * kHistWords] : 0u;
+#pragma unroll
+        for (int q = 0; q < kSumBatch; ++q) {
+          lo += v[q] & 0xFFFFu;
+          hi += v[q] >> 16;
+        }
       }
-      sm.hist[2 * w] = lo;
-      sm.hist[2 * w + 1] = hi;
+      sm.hist[2 * tid] = lo;
+      sm.hist[2 * tid + 1] = hi;
     }
     __syncthreads();
     int par = 0;
