@@ -159,8 +159,33 @@ __device__ __forceinline__ void row_fix_tail(const RowSrc& s, int g, u32x4& raw)
 }
 
 // Keys of one score row (n scores) into registers, group v of this thread
-// being row group tid + NT*v, and the least / greatest valid key of the
-// thread (UINT32_MAX / 0 if none).
+// being row group tid + NT*v; elements past the row get key 0.
+template <int NT, int R>
+__device__ __forceinline__ void load_row_keys(const float* src, int n, uint32_t (&key)[R]) {
+  const RowSrc rs = row_src(src, n);
+  const int tid = threadIdx.x;
+  const int nvg = rdx_live_groups<NT>(n);
+  u32x4 raw[R / 4];
+#pragma unroll
+  for (int v = 0; v < R / 4; ++v)
+    raw[v] = v < nvg ? row_load4(rs, tid + NT * v) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int v = 0; v < R / 4; ++v) {
+    if (v >= nvg) continue;  // workgroup-uniform
+    const int g = tid + NT * v;
+    row_fix_tail(rs, g, raw[v]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) key[4 * v + j] = order_key(__uint_as_float(raw[v][j]));
+    if (4 * g + 3 >= n) {  // the row's last group (or past the row)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * g + j >= n) key[4 * v + j] = 0u;
+    }
+  }
+}
+
+// The same, with the least / greatest valid key of the thread (UINT32_MAX / 0
+// if none).
 template <int NT, int R>
 __device__ __forceinline__ void load_row_keys(const float* src, int n, uint32_t (&key)[R],
                                               uint32_t& kmin, uint32_t& kmax) {
@@ -262,13 +287,15 @@ void topk_rows_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, i
     return;
   }
   rdx_clear(sm, kHistWords);
-  uint32_t key[R], kmin, kmax, lo, hi;
-  load_row_keys<NT, R>(scores + row * Lk, n, key, kmin, kmax);
-  rdx_key_range(kmin, kmax, sm, lo, hi);  // its barrier also ends the clear
+  // A full score row spans most of the key space, so the digits are taken of
+  // the keys themselves (base 0): no key range to find. Elements past the row
+  // get key 0, below the key of every finite score.
+  uint32_t key[R];
+  load_row_keys<NT, R>(scores + row * Lk, n, key);
+  __syncthreads();  // the histogram is clear
   auto valid = [&](int r) { return elem_of<NT>(r) < n; };
-#pragma unroll
-  for (int r = 0; r < R; ++r) key[r] = valid(r) ? key[r] - lo : 0u;  // rel, padded
-  RdxState st = rdx_start(n, k, lo, hi);
+  constexpr uint32_t lo = 0u;
+  RdxState st = rdx_start(n, k, 0u, 0xFFFFFFFFu);
   rdx_search_regs<NT, NGRP, R>(key, n, sm, st);
   if (OUT == kOutPos) {
     const int kk = rdx_emit_regs<NT, NGRP, 4, R>(
