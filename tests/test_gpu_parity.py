@@ -317,6 +317,37 @@ def test_sparse_attn_split_equals_single_pass():
     assert (split.float() - single.float()).abs().max().item() <= ATOL
 
 
+@pytest.mark.parametrize("B,H,k", [(8, 64, 2048), (128, 32, 1024), (256, 32, 512), (3, 40, 700)])
+def test_sparse_attn_split_merge_repeated_calls(B, H, k):
+    # Split index lists and their merge: a workspace full of garbage, three
+    # calls in a row (the second on fewer rows), every call equal to the
+    # first and to the oracle; shapes with 2 to 8 slices per row, 32 to 64
+    # heads (one or two head blocks) and a partly filled head block.
+    Lk, D = 5000, 128
+    _say("sparse_attn split merge B=%d H=%d k=%d" % (B, H, k))
+    Q, K, V = gen.attn_inputs(B, 1, Lk, H, D, seed=21)
+    idx = gen.index_sets(B, 1, Lk - 1, k, seed=22, pad_frac=0.1)
+    nb = idxc.idxc_sparse_attn_workspace_bytes(B, 1, Lk, H, D, k)
+    assert nb > 0
+    ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda")
+    scale = D ** -0.5
+    first = idxc.idxc_sparse_attn(cu(Q), cu(K), cu(V), cu(idx), scale, workspace=ws).clone()
+    half = max(1, B // 2)
+    sub = idxc.idxc_sparse_attn(cu(Q[:half]), cu(K[:half]), cu(V[:half]), cu(idx[:half]), scale,
+                                workspace=ws).clone()
+    again = idxc.idxc_sparse_attn(cu(Q), cu(K), cu(V), cu(idx), scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(again, first)
+    single_half = idxc.idxc_sparse_attn(cu(Q[:half]), cu(K[:half]), cu(V[:half]), cu(idx[:half]),
+                                        scale, workspace=None)
+    torch.cuda.synchronize()
+    assert (sub.float() - single_half.float()).abs().max().item() <= ATOL
+    want = oracle.sparse_attention(f64(Q), f64(K), f64(V), idx.numpy(), scale)
+    err = np.abs(first.float().cpu().numpy() - want).max()
+    _say("max abs err %.3e" % err)
+    assert err <= ATOL
+
+
 def test_sparse_attn_single_key_is_exact_copy():
     B, L, H, D, k = 1, 200, 64, 128, 8
     Q, K, V = gen.attn_inputs(B, L, L, H, D, seed=10)
