@@ -222,6 +222,50 @@ __device__ __forceinline__ int elem_of(int r) {
   return 4 * ((int)threadIdx.x + NT * (r >> 2)) + (r & 3);
 }
 
+// A position-ordered list of n (key, position) pairs into registers (element
+// r of this thread at elem_of<NT>(r); zeros past the list), through a buffer
+// resource of its n pairs (reads past them return 0): two 16-byte loads per
+// group of four pairs, issued unconditionally; a partly valid last group is
+// read again pair by pair.
+template <int NT, int R>
+__device__ __forceinline__ void load_pair_list(const u32x2* src, int n, uint32_t (&key)[R],
+                                               uint32_t (&pos)[R]) {
+  constexpr int NGRP = R / 4;
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u32x2*>(src), (short)0, n * 8, 0x00020000);
+  u32x4 p0[NGRP], p1[NGRP];
+  const int nvg = rdx_live_groups<NT>(n);
+#pragma unroll
+  for (int v = 0; v < NGRP; ++v) {
+    const int g = tid + NT * v;
+    p0[v] = p1[v] = u32x4{0u, 0u, 0u, 0u};
+    if (v < nvg) {  // workgroup-uniform
+      p0[v] = __builtin_amdgcn_raw_buffer_load_b128(rs, g * 32, 0, 0);
+      p1[v] = __builtin_amdgcn_raw_buffer_load_b128(rs, g * 32 + 16, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < NGRP; ++v) {
+    const int g = tid + NT * v;
+    if ((n & 3) != 0 && g == (n >> 2)) {
+      const u32x2 q0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, g * 32, 0, 0));
+      const u32x2 q1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, g * 32 + 8, 0, 0));
+      const u32x2 q2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, g * 32 + 16, 0, 0));
+      p0[v] = u32x4{q0[0], q0[1], q1[0], q1[1]};
+      p1[v] = u32x4{q2[0], q2[1], 0u, 0u};
+    }
+    key[4 * v + 0] = p0[v][0];
+    pos[4 * v + 0] = p0[v][1];
+    key[4 * v + 1] = p0[v][2];
+    pos[4 * v + 1] = p0[v][3];
+    key[4 * v + 2] = p1[v][0];
+    pos[4 * v + 2] = p1[v][1];
+    key[4 * v + 3] = p1[v][2];
+    pos[4 * v + 3] = p1[v][3];
+  }
+}
+
 // Score-order finish: the kk winners' words are in `words`, their key range
 // in [wmin, wmax] per thread. Ranks them (or sorts them) into orow.
 template <int NT, int NGRP>
@@ -347,6 +391,99 @@ void topk_chunk_hist_kernel(const float* __restrict__ scores, int Lq, int Lk, in
   for (int w = tid; w < kHistWords / 4; w += NT) dst[w] = srch[w];
 }
 
+// ---------------------------------------------------------------------------
+// Rows of more than kLongCap scores, second launch: one workgroup per (row,
+// chunk). Every workgroup of a row sums the row's chunk histograms and
+// resolves the top digit of the row's k-th best key (all of them reach the
+// same digit). The row's keys at or above that digit (at least k of them)
+// form its candidate list when they number at most kLongCap: each workgroup
+// writes its chunk's share in position order, at the slot where the earlier
+// chunks' shares end (their counts read off their histograms). lcnt[row]
+// receives the list's length, or -1 when it would not fit (the last launch
+// then refines the digit over the row itself).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kRowThreads)
+void topk_chunk_gather_kernel(const float* __restrict__ scores, int Lq, int Lk, int q_pos0, int k,
+                              int nch, const uint32_t* __restrict__ ghist,
+                              u32x2* __restrict__ lcand, int* __restrict__ lcnt) {
+  constexpr int NT = kRowThreads, R = kRowR, NGRP = R / 4, NW = NT / kWave;
+  constexpr int BPT = kSelBins / NT;  // bins summed per thread: BPT / 2 histogram words
+  static_assert(BPT == 8, "two 16-byte histogram loads per chunk and thread");
+  __shared__ RdxSmem<NT, NGRP> sm;
+  const int tid = threadIdx.x;
+  const size_t row = blockIdx.x / (unsigned)nch;
+  const int c = (int)(blockIdx.x % (unsigned)nch);
+  const int i = (int)(row % (size_t)Lq);
+  const int n = min(q_pos0 + i + 1, Lk);
+  const int c0 = c * kTopkChunk;
+  if (n <= kLongCap || c0 >= n) return;  // rows the last launch loads whole; chunks past the row
+  const int nc = (n + kTopkChunk - 1) / kTopkChunk;
+  // the row's counts of bins 8 tid .. 8 tid + 7 (and those of the chunks
+  // before this one), the chunks' words in batches of loads
+  uint32_t tot[BPT], bef[BPT];
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) tot[q] = bef[q] = 0u;
+  const u32x4* gw = reinterpret_cast<const u32x4*>(ghist + row * nch * kHistWords) + tid;
+  constexpr int kBatch = 8;
+  for (int cc0 = 0; cc0 < nc; cc0 += kBatch) {
+    u32x4 v[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q)
+      v[q] = cc0 + q < nc ? gw[(size_t)(cc0 + q) * (kHistWords / 4)] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const bool before = cc0 + q < c;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t lo16 = v[q][w] & 0xFFFFu, hi16 = v[q][w] >> 16;  // bins 2w, 2w + 1
+        tot[2 * w] += lo16;
+        tot[2 * w + 1] += hi16;
+        if (before) {
+          bef[2 * w] += lo16;
+          bef[2 * w + 1] += hi16;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) sm.hist[BPT * tid + q] = tot[q];  // 32-bit counts
+  __syncthreads();
+  RdxState st = rdx_start(n, k, 0u, 0xFFFFFFFFu);
+  const int cnt = rdx_resolve<NT, NGRP, false>(sm, st, 0);
+  const uint32_t bin = st.prefix >> st.sh0;  // the top digit (21-bit shift)
+  const int m = (k - st.rem) + cnt;          // keys at or above it
+  if (m > kLongCap) {  // block-uniform
+    if (c == 0 && tid == 0) lcnt[row] = -1;
+    return;
+  }
+  if (c == 0 && tid == 0) lcnt[row] = m;
+  // this chunk's first slot: such keys in the earlier chunks
+  int mine = 0;
+#pragma unroll
+  for (int q = 0; q < BPT; ++q)
+    if ((uint32_t)(BPT * tid + q) >= bin) mine += (int)bef[q];
+  const int wsum = wave_sum(mine);
+  if (lane_id() == 0) sm.scan[1][tid / kWave] = wsum;
+  // the chunk's keys; a key is kept when its top digit is at least `bin`
+  // (bin > 0 here, as m < n: elements past the chunk, key 0, are never kept)
+  const int mc = min(kTopkChunk, n - c0);
+  uint32_t key[R];
+  load_row_keys<NT, R>(scores + row * Lk + c0, mc, key);
+  __syncthreads();
+  int off = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) off += sm.scan[1][w];
+  RdxState keep = st;
+  keep.prefix = bin << st.sh0;
+  keep.done = true;
+  keep.all = false;
+  auto valid = [&](int r) { return elem_of<NT>(r) < mc; };
+  u32x2* dst = lcand + row * kLongCap + off;
+  rdx_emit_regs<NT, NGRP, 4, R>(key, mc, valid, keep, sm, 0, [&](int slot, uint32_t kv, int r) {
+    dst[slot] = u32x2{kv, (uint32_t)(c0 + elem_of<NT>(r))};
+  });
+}
+
 // Streaming count of level st.level over a whole score row into the 32-bit
 // histogram, then its resolution (par: the level's slot parity).
 template <int NT, int NGRP>
@@ -376,9 +513,10 @@ __device__ void stream_level(const float* src, int n, RdxSmem<NT, NGRP>& sm, Rdx
 }
 
 // ---------------------------------------------------------------------------
-// Long rows, second launch: one 1024-thread workgroup per row (longest rows
-// first). Rows of at most kLongCap scores are loaded straight into registers.
-// Longer rows: the row's chunk histograms give the top digit; while the keys
+// Long rows, last launch: one 1024-thread workgroup per row (longest rows
+// first). Rows of at most kLongCap scores are loaded straight into registers;
+// longer ones take the candidate list of the chunk-gather launch when it fit.
+// Otherwise: the row's chunk histograms give the top digit; while the keys
 // at or above the digits found so far exceed kLongCap, one more digit is
 // resolved by a pass over the row; then a pass gathers those keys (for a
 // fully resolved key: the keys above it and the first `rem` equal to it) into
@@ -389,7 +527,9 @@ __device__ void stream_level(const float* src, int n, RdxSmem<NT, NGRP>& sm, Rdx
 template <int OUT>
 __global__ __launch_bounds__(kWideThreads)
 void topk_long_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, int q_pos0, int k,
-                      int nch, const uint32_t* __restrict__ ghist, int32_t* __restrict__ out) {
+                      int nch, const uint32_t* __restrict__ ghist,
+                      const u32x2* __restrict__ lcand, const int* __restrict__ lcnt,
+                      int32_t* __restrict__ out) {
   constexpr int NT = kWideThreads, R = kWideR, NGRP = R / 4, NW = NT / kWave;
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   RdxSmem<NT, NGRP>& sm = *reinterpret_cast<RdxSmem<NT, NGRP>*>(dyn);
@@ -419,6 +559,21 @@ void topk_long_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, i
 #pragma unroll
     for (int r = 0; r < R; ++r) pos[r] = (uint32_t)elem_of<NT>(r);
     m = n;
+  } else if (lcnt[row] >= 0) {
+    // the row's candidate list from the previous launch (position-ordered,
+    // a superset of the top-k holding every key equal to its least member)
+    m = lcnt[row];
+    rdx_clear(sm, kHistWords);  // the key-range barrier below ends the clear
+    load_pair_list<NT, R>(lcand + row * kLongCap, m, key, pos);
+    kmin = 0xFFFFFFFFu;
+    kmax = 0u;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (elem_of<NT>(r) < m) {
+        kmin = min(kmin, key[r]);
+        kmax = max(kmax, key[r]);
+      }
+    }
   } else {
     // level 0 (the top 11 bits) from the chunk histograms, as 32-bit sums
     RdxState st = rdx_start(n, k, 0u, 0xFFFFFFFFu);
@@ -596,43 +751,8 @@ void topk_pairs_kernel(TopkArgs a, int ngroups) {
   uint32_t key[R], pos[R];
   int n;
   if (SRC == kSrcCand1) {
-    // the list through a buffer resource of its n pairs (reads past them
-    // return 0): two 16-byte loads per group of four pairs, issued
-    // unconditionally; a partly valid last group is read again pair by pair
     n = a.cand_count[row];
-    const u32x2* src = a.cand + (size_t)row * a.seg_cap;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<u32x2*>(src), (short)0, n * 8, 0x00020000);
-    u32x4 p0[NGRP], p1[NGRP];
-    const int nvg = rdx_live_groups<NT>(n);
-#pragma unroll
-    for (int v = 0; v < NGRP; ++v) {
-      const int g = tid + NT * v;
-      p0[v] = p1[v] = u32x4{0u, 0u, 0u, 0u};
-      if (v < nvg) {  // workgroup-uniform
-        p0[v] = __builtin_amdgcn_raw_buffer_load_b128(rs, g * 32, 0, 0);
-        p1[v] = __builtin_amdgcn_raw_buffer_load_b128(rs, g * 32 + 16, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int v = 0; v < NGRP; ++v) {
-      const int g = tid + NT * v;
-      if ((n & 3) != 0 && g == (n >> 2)) {
-        const u32x2 q0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, g * 32, 0, 0));
-        const u32x2 q1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, g * 32 + 8, 0, 0));
-        const u32x2 q2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, g * 32 + 16, 0, 0));
-        p0[v] = u32x4{q0[0], q0[1], q1[0], q1[1]};
-        p1[v] = u32x4{q2[0], q2[1], 0u, 0u};
-      }
-      key[4 * v + 0] = p0[v][0];
-      pos[4 * v + 0] = p0[v][1];
-      key[4 * v + 1] = p0[v][2];
-      pos[4 * v + 1] = p0[v][3];
-      key[4 * v + 2] = p1[v][0];
-      pos[4 * v + 2] = p1[v][1];
-      key[4 * v + 3] = p1[v][2];
-      pos[4 * v + 3] = p1[v][3];
-    }
+    load_pair_list<NT, R>(a.cand + (size_t)row * a.seg_cap, n, key, pos);
   } else {
     const int per_group = (a.nseg + ngroups - 1) / ngroups;
     const int s0 = min(a.nseg, grp * per_group);
@@ -714,6 +834,16 @@ hipError_t launch_pairs_final(const TopkArgs& a, int ngroups, hipStream_t st) {
                      : launch_pairs<SRC, kOutScore, NT, R>(a, ngroups, st);
 }
 
+// Scratch of long materialised rows, in a.ghist: the chunk histograms, then
+// (rows longer than kLongCap) kLongCap candidate pairs and a count per row.
+size_t hist_bytes(int rows, int nch) { return (size_t)rows * nch * kHistWords * 4; }
+u32x2* topk_lcand(const TopkArgs& a, int nch) {
+  return reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(a.ghist) + hist_bytes(a.rows, nch));
+}
+int* topk_lcnt(const TopkArgs& a, int nch) {
+  return reinterpret_cast<int*>(topk_lcand(a, nch) + (size_t)a.rows * kLongCap);
+}
+
 size_t long_lds_bytes() {
   constexpr size_t off =
       (sizeof(RdxSmem<kWideThreads, kWideR / 4>) + 15) / 16 * 16;
@@ -729,7 +859,8 @@ hipError_t launch_long(const TopkArgs& a, int nch, hipStream_t st) {
   const int B = a.rows / a.Lq;
   hipLaunchKernelGGL((topk_long_kernel<OUT>), dim3((unsigned)a.rows), dim3(kWideThreads), shmem,
                      st, a.scores, B, a.Lq, a.Lk, a.q_pos0, a.k, nch,
-                     reinterpret_cast<const uint32_t*>(a.ghist), a.out);
+                     reinterpret_cast<const uint32_t*>(a.ghist), topk_lcand(a, nch),
+                     topk_lcnt(a, nch), a.out);
   return hipGetLastError();
 }
 
@@ -741,7 +872,9 @@ size_t topk_part_bytes(int rows, int Lk, int k) {
   (void)k;
   const int nch = topk_row_chunks(Lk);
   if (nch <= 1) return 0;
-  return (size_t)rows * nch * kHistWords * 4;
+  size_t b = hist_bytes(rows, nch);
+  if (Lk > kLongCap) b += (size_t)rows * kLongCap * 8 + (size_t)rows * 4;
+  return b;
 }
 
 int topk_segment_groups(int nseg, int k) {
@@ -795,6 +928,16 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
                      reinterpret_cast<uint32_t*>(a.ghist));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.Lk > kLongCap) {
+    // rows longer than kLongCap: each chunk adds its share of the row's
+    // candidate list
+    hipLaunchKernelGGL(topk_chunk_gather_kernel, dim3((unsigned)((size_t)a.rows * nch)),
+                       dim3(kRowThreads), 0, st, a.scores, a.Lq, a.Lk, a.q_pos0, a.k, nch,
+                       reinterpret_cast<const uint32_t*>(a.ghist), topk_lcand(a, nch),
+                       topk_lcnt(a, nch));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   return a.pos_order ? launch_long<kOutPos>(a, nch, st) : launch_long<kOutScore>(a, nch, st);
 }
 

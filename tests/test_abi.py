@@ -107,13 +107,18 @@ def test_topk_argument_errors(lib):
     long_rows = _dims(Lq=1, Lk=65536, q_pos0=65535, k=2048)
     n = ctypes.c_size_t(0)
     assert lib.idxc_topk_workspace_bytes(ctypes.byref(long_rows), ctypes.byref(n)) == 0
-    assert n.value == 8 * 4096  # one 2048-bin histogram of 16-bit counts per 8192-score chunk
+    # one 2048-bin histogram of 16-bit counts per 8192-score chunk, and for
+    # rows past 16384 scores a list of 16384 (key, position) pairs and a count
+    assert n.value == 8 * 4096 + 16384 * 8 + 4
     assert f(P(), ctypes.byref(long_rows), None, 0, P(), None) == _lib.IDXC_ERR_INVALID_ARG
     assert f(P(), ctypes.byref(long_rows), P(), n.value - 1, P(), None) == _lib.IDXC_ERR_INVALID_ARG
     # rows of any length up to Lk = 2^24 are supported given the workspace
     longest = _dims(B=2, Lq=3, Lk=1 << 24, q_pos0=(1 << 24) - 3, k=2048)
     assert lib.idxc_topk_workspace_bytes(ctypes.byref(longest), ctypes.byref(n)) == 0
-    assert n.value == 6 * 2048 * 4096
+    assert n.value == 6 * 2048 * 4096 + 6 * (16384 * 8 + 4)
+    two_chunks = _dims(Lq=1, Lk=16384, q_pos0=16383, k=2048)
+    assert lib.idxc_topk_workspace_bytes(ctypes.byref(two_chunks), ctypes.byref(n)) == 0
+    assert n.value == 2 * 4096
     assert f(P(), ctypes.byref(longest), P(), n.value - 16, P(), None) == _lib.IDXC_ERR_INVALID_ARG
     short = _dims(Lq=1, Lk=8192, q_pos0=8191, k=2048)
     assert lib.idxc_topk_workspace_bytes(ctypes.byref(short), ctypes.byref(n)) == 0

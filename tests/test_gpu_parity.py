@@ -104,6 +104,7 @@ def test_indexer_scores_split_path_integer_exact():
     ("normal", 1, 3, 40000, 39997, 300),    # many chunks, small k
     ("normal", 2, 2, 20000, 19998, 100),    # two stages, final sort in LDS (k < 257)
     ("normal", 1, 20, 20, 0, 2048),         # every row shorter than k
+    ("normal", 1, 4, 20000, 16382, 2048),   # rows on both sides of 16384 scores in one launch
 ])
 def test_topk_exact(kind, B, Lq, Lk, q_pos0, k):
     _say("topk %s B=%d Lq=%d Lk=%d q_pos0=%d k=%d" % (kind, B, Lq, Lk, q_pos0, k))
@@ -155,6 +156,31 @@ def test_topk_extreme_key_ranges_exact(kind, B, Lq, Lk, q_pos0, k):
     want = oracle.topk(s.numpy(), k, q_pos0)
     assert np.array_equal(got.cpu().numpy(), want)
     assert np.array_equal(got_pos.cpu().numpy(), oracle.position_order(want))
+
+
+@pytest.mark.parametrize("n_mid", [15384, 15385])
+def test_topk_long_row_candidate_list_capacity_exact(n_mid):
+    # Rows past 16384 scores: the keys at or above the top digit of the k-th
+    # best key form a per-row candidate list when they are at most 16384.
+    # 1000 scores of 5.0 and n_mid of 2.0 (each value alone in its top digit)
+    # put the k-th best key in the 2.0 digit: 16384 listed keys (the list
+    # just fits) or 16385 (the row is refined over its scores instead); the
+    # ties keep the lowest positions.
+    B, Lk, k = 2, 40000, 2048
+    rng = np.random.default_rng(n_mid)
+    s = rng.uniform(-1.0, 1.0, size=(B, 1, Lk)).astype(np.float32)
+    for b in range(B):
+        perm = rng.permutation(Lk)
+        s[b, 0, perm[:1000]] = 5.0
+        s[b, 0, perm[1000:1000 + n_mid]] = 2.0
+    _say("topk long-row list capacity n_mid=%d" % n_mid)
+    st = torch.from_numpy(s)
+    want = oracle.topk(s, k, Lk - 1)
+    for order in ("score", "position"):
+        got = idxc.idxc_topk(cu(st), k, q_pos0=Lk - 1, order=order)
+        torch.cuda.synchronize()
+        exp = want if order == "score" else oracle.position_order(want)
+        assert np.array_equal(got.cpu().numpy(), exp)
 
 
 def test_decode_indexer_all_equal_scores_exact():
