@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--only", default="",
-                    help="prefill-12f | prefill-allf | decode | sweep | pmc | dispatch (profiling)")
+                    help="prefill-12f | prefill-allf | decode | sweep | pmc | dispatch | topk "
+                         "(profiling)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CMD_F", "CMD_W"),
                     help="write profiles/hbm_traffic.md from the two counter passes (no GPU)")
     ap.add_argument("--dispatch-summary", nargs=2, metavar=("TRACE_CSV", "CMD"),
@@ -595,11 +596,50 @@ def overlap_records():
 CAL_BYTES = 1 << 30         # the calibration kernels read / write exactly this much
 TRAFFIC_SOURCES = {
     "attention_prefill": ["attn.hip", "common.hpp", "kernels.hpp"],
-    "indexer_topk_prefill": ["indexer.hip", "topk.hip", "select.hpp", "common.hpp", "kernels.hpp",
-                             "api.hip"],
-    "indexer_topk_decode": ["indexer.hip", "topk.hip", "select.hpp", "common.hpp", "kernels.hpp",
-                            "api.hip"],
+    "indexer_topk_prefill": ["indexer.hip", "topk.hip", "radix_topk.hpp", "select.hpp",
+                             "common.hpp", "kernels.hpp", "api.hip"],
+    "indexer_topk_decode": ["indexer.hip", "topk.hip", "radix_topk.hpp", "select.hpp",
+                            "common.hpp", "kernels.hpp", "api.hip"],
 }
+
+
+def calibration_launches():
+    """The counter-scaling kernels: a fill that writes CAL_BYTES and an
+    elementwise negation that reads CAL_BYTES (and writes CAL_BYTES)."""
+    import torch
+    src = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def topk_launches():
+    """Standalone idxc_topk for a kernel trace or a counter pass: the
+    calibration kernels, then 8192 causal rows of 8192 scores and 64 decode
+    rows of 65536 (k = 2048), each in position and in score order, twice,
+    each launch between synchronisations."""
+    import torch
+    import dsa_lightning_indexer_score_amd as idxc
+    calibration_launches()
+    for name, (B, Lq, Lk, q0) in (("8192 causal rows of 8192", (1, 8192, 8192, 0)),
+                                  ("64 decode rows of 65536", (64, 1, 65536, 65535))):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(0)
+        s = torch.randn((B, Lq, Lk), generator=g, device="cuda")
+        ws_n = idxc.idxc_topk_workspace_bytes(B, Lq, Lk, q0, 2048)
+        ws = torch.empty((max(ws_n, 256),), dtype=torch.uint8, device="cuda")
+        out = torch.empty((B, Lq, 2048), dtype=torch.int32, device="cuda")
+        for order in ("position", "score"):
+            for _ in range(2):
+                torch.cuda.synchronize()
+                idxc.idxc_topk(s, 2048, q_pos0=q0, workspace=ws, out=out, order=order)
+                torch.cuda.synchronize()
+            log("topk launches: %s, %s order done" % (name, order))
+        del s, ws, out
+        torch.cuda.empty_cache()
 
 
 def pmc_launches():
@@ -610,13 +650,7 @@ def pmc_launches():
     import torch
     import idxc_inputs as gen
     import dsa_lightning_indexer_score_amd as idxc
-    src = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    torch.cuda.synchronize()
-    torch.neg(src, out=dst)
-    torch.cuda.synchronize()
-    del src, dst
-    torch.cuda.empty_cache()
+    calibration_launches()
     for cfg in (gen.C3_12F, gen.C4_12F):
         L = gen.layer_inputs(cfg, 0, device="cuda")
         ws = torch.empty(idxc.idxc_workspace_bytes(cfg.B, cfg.Lq, cfg.Lk, cfg.q_pos0, cfg.H_I,
@@ -853,6 +887,9 @@ def main():
     if args.only == "dispatch":
         dispatch_launches()
         return
+    if args.only == "topk":
+        topk_launches()
+        return
     if args.only == "sweep":
         print(json.dumps({"context_sweep": context_sweep(), "distill_loss": distill_rate()}),
               flush=True)
@@ -982,7 +1019,7 @@ def main():
         # dominant kernel of the headline workload by total time per step
         idx_total, att_total = nF * idx_ms, cfg.n_layers * att_ms
         att_tflops = attn_flops(cfg) / (att_ms * 1e-3) / 1e12
-        roof_idx = {"kernel": "indexer_rows_kernel + topk_kernel (fused indexer + top-k of one F "
+        roof_idx = {"kernel": "indexer_rows_kernel + topk_pairs_kernel (fused indexer + top-k of one F "
                               "layer, idxc_indexer_topk)",
                     "bound": "mfma", "achieved": idx_tflops, "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": idx_tflops / PEAK_BF16_TFLOPS,
