@@ -249,10 +249,16 @@ hipError_t run_indexer_topk(const void* q_idx, const void* k_idx, const void* w,
   return launch_topk(ta, st);
 }
 
+// prefix: the lists are the stack's own top-k output (valid entries first,
+// min(k, t + 1) of them; t from q_pos0 or q_pos).
 AttnArgs attn_args(const void* q, const void* k, const void* v, const int32_t* indices,
-                   const idxc_dims* d, float scale, void* out, void* workspace) {
+                   const idxc_dims* d, float scale, void* out, void* workspace,
+                   bool prefix = false, const int32_t* q_pos = nullptr) {
   AttnArgs a{};
   a.workspace = workspace;
+  a.prefix_lists = prefix ? 1 : 0;
+  a.q_pos0 = d->q_pos0;
+  a.q_pos = q_pos;
   a.q = static_cast<const uint16_t*>(q);
   a.key = static_cast<const uint16_t*>(k);
   a.val = static_cast<const uint16_t*>(v);
@@ -658,8 +664,9 @@ static int stack_run(const char* pattern, int32_t n_layers, const idxc_layer* la
       }
       ++calls;
     }
+    // the cache is the stack's own top-k output: its padding blocks are skipped
     hipError_t e = launch_sparse_attn(
-        attn_args(L.q, L.k, L.v, index_cache, dims, scale, L.out, workspace), st);
+        attn_args(L.q, L.k, L.v, index_cache, dims, scale, L.out, workspace, true, q_pos), st);
     if (e != hipSuccess) {
       *indexer_calls = calls;
       return hip_status(e, "stack attention launch");

@@ -32,6 +32,7 @@ namespace {
 constexpr int kAttnWaves = 4;
 constexpr float kLazyLog2 = 8.0f;   // rescale threshold (exp2 domain)
 constexpr int kMaxAttnSplits = 32;
+constexpr int kXcdChunk = 64;  // consecutive workgroups an XCD takes at a time
 
 // One gathered 32-key block in LDS: whole K rows SK bytes apart, then whole V
 // rows SV bytes apart. The padding spreads the MFMA operand reads over the
@@ -136,7 +137,8 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
                         const uint16_t* __restrict__ vmat, const int32_t* __restrict__ indices,
                         int B, int Lq, int Lk, int H, int k, int nsplit, float sl2,
                         uint16_t* __restrict__ out, uint16_t* __restrict__ part_o,
-                        float* __restrict__ part_ml) {
+                        float* __restrict__ part_ml, int prefix_lists, int q_pos0,
+                        const int32_t* __restrict__ q_pos) {
   using BL = Blk<D>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -150,12 +152,24 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   const int hb = wave % HB;
   const int rows = B * Lq;
   // Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD
-  // b % 8); renumber them so that each XCD takes a contiguous range of rows
-  // and its L2 sees the index lists of neighbouring rows (a bijection:
-  // XCD x holds counts nwg/8 (+1 for x < nwg % 8)).
+  // b % 8). Renumber them so that each XCD takes chunks of kXcdChunk
+  // consecutive workgroups (neighbouring rows: its L2 sees their index lists
+  // and gathers together), the chunks dealt to the XCDs in turn, so that
+  // every XCD gets an equal share of short rows (padding blocks skipped).
+  // A bijection: the first nwg rounded down to 8 chunks go chunk-wise, the
+  // rest keep their number; grids of fewer than 8 chunks give each XCD one
+  // contiguous range (XCD x holds nwg/8, +1 for x < nwg % 8).
   const int nwg = (int)gridDim.x;
   const int xcd = (int)(blockIdx.x % 8);
-  const int wg = xcd * (nwg / 8) + min(xcd, nwg % 8) + (int)(blockIdx.x / 8);
+  const int pos = (int)(blockIdx.x / 8);  // order within the XCD
+  int wg;
+  if (nwg < 8 * kXcdChunk) {
+    wg = xcd * (nwg / 8) + min(xcd, nwg % 8) + pos;
+  } else if ((int)blockIdx.x < nwg / (8 * kXcdChunk) * (8 * kXcdChunk)) {
+    wg = ((pos / kXcdChunk) * 8 + xcd) * kXcdChunk + pos % kXcdChunk;
+  } else {
+    wg = (int)blockIdx.x;
+  }
   const int unit = wg * UPW + ul;
   const int rowq = unit / nsplit;
   const int split = unit % nsplit;
@@ -164,6 +178,27 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   const int kbeg = min(k, split * per);
   const int kend = min(k, kbeg + per);
   const int nblk = per / 32;  // same for every unit: keeps the barriers aligned
+  // Blocks the workgroup runs: all nblk, or, for prefix-valid lists, up to
+  // the last block holding a valid entry of any of its units (every wave
+  // computes the same count, so the barriers stay aligned).
+  int nrun = nblk;
+  if (prefix_lists) {
+    nrun = 0;
+#pragma unroll
+    for (int u = 0; u < UPW; ++u) {
+      const int uu = wg * UPW + u;
+      const int rq = uu / nsplit;
+      if (rq >= rows) continue;
+      int t = q_pos0 + rq % Lq;
+      if (q_pos != nullptr) {
+        const int p = q_pos[rq];
+        t = p < 0 ? -1 : min(p, Lk - 1);
+      }
+      const int b0 = min(k, (uu % nsplit) * per);
+      const int e = min(min(k, b0 + per), min(k, t + 1));
+      nrun = max(nrun, e > b0 ? (e - b0 + 31) / 32 : 0);
+    }
+  }
   const int b = active ? rowq / Lq : 0;
   const uint16_t* kb = kmat + (size_t)b * Lk * D;
   const uint16_t* vb = vmat + (size_t)b * Lk * D;
@@ -329,9 +364,9 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     s_cur = s_nxt;
     __syncthreads();
   };
-  for (int j = 0; j < nblk; j += 2) {
+  for (int j = 0; j < nrun; j += 2) {
     iteration(j, ka_, va_, kb_, vb_);
-    if (j + 1 < nblk) iteration(j + 1, kb_, vb_, ka_, va_);
+    if (j + 1 < nrun) iteration(j + 1, kb_, vb_, ka_, va_);
   }
 
   if (!active || h >= H) return;
@@ -434,7 +469,7 @@ hipError_t launch(const AttnArgs& a, int nsplit, hipStream_t st) {
                           : nullptr;
   hipLaunchKernelGGL((sparse_attn_kernel<D, HB>), dim3(grid), dim3(kAttnWaves * kWave), shmem, st,
                      a.q, a.key, a.val, a.indices, a.B, a.Lq, a.Lk, a.H, a.topk, nsplit, sl2,
-                     a.out, po, pml);
+                     a.out, po, pml, a.prefix_lists, a.q_pos0, a.q_pos);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
   const int hgroups = (a.H + kMergeHeads - 1) / kMergeHeads;

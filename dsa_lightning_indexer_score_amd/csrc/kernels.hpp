@@ -81,6 +81,14 @@ struct AttnArgs {
   float scale;
   uint16_t* out;
   void* workspace;  // NULL: one pass per row; else partials of split rows
+  // Nonzero when the lists are the library's own top-k output: row r's valid
+  // entries are then its first min(k, t_r + 1), t_r = q_pos0 + (r % Lq) (or
+  // q_pos[r], negative = none, past the keys = the last key), and the rest
+  // are -1, so blocks past them hold only padding and are skipped (the
+  // result is the same: padding adds exact zeros). 0: any list.
+  int prefix_lists;
+  int q_pos0;
+  const int32_t* q_pos;
 };
 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st);

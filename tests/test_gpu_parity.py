@@ -570,6 +570,35 @@ def test_ragged_uniform_positions_equal_uniform_call():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("B,Lq,Lk,q_pos0,k,ragged", [
+    (1, 2600, 2600, 0, 2048, False),   # prefill rows t < k-1: lists end in padding blocks
+    (2, 3, 3000, 1200, 2048, False),   # few rows: split lists, slices wholly padding
+    (6, 1, 3000, 2999, 2048, True),    # per-row positions: none, short, past the keys
+])
+def test_stack_attention_equals_per_layer_attention(B, Lq, Lk, q_pos0, k, ragged):
+    # The stack skips the attention blocks past each row's valid entries (its
+    # cache is its own top-k output); the outputs must equal, bit for bit,
+    # the standalone attention (which runs every block) on the same caches.
+    cfg = dataclasses.replace(gen.C1, name="skip", n_layers=2, pattern="FS", B=B, Lq=Lq,
+                              Lk=Lk, q_pos0=q_pos0, H_I=8, d_I=64, k=k, H=64, D=128)
+    _say("stack vs per-layer attention B=%d Lq=%d Lk=%d q_pos0=%d ragged=%s"
+         % (B, Lq, Lk, q_pos0, ragged))
+    layers = [{n: cu(t) for n, t in L.items()} for L in _layers(cfg)]
+    if ragged:
+        q_pos = torch.tensor([[-1], [0], [100], [2046], [2047], [5000]][:B], dtype=torch.int32)
+        res = idxc.idxc_layer_stack_forward_ragged(cfg.pattern, layers, k, cfg.scale,
+                                                   cu(q_pos), debug_indices=True)
+    else:
+        res = idxc.idxc_layer_stack_forward(cfg.pattern, layers, k, cfg.scale,
+                                            q_pos0=q_pos0, debug_indices=True)
+    torch.cuda.synchronize()
+    dbg = res["debug_indices"]
+    for l, L in enumerate(layers):
+        ref = idxc.idxc_sparse_attn(L["q"], L["k"], L["v"], dbg[l].contiguous(), cfg.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(res["out"][l], ref), l
+
+
 def test_ragged_decode_stack_matches_oracle():
     # a 3-layer FSF decode step over sequences of different lengths
     lens = [700, 64, 3000, 1]
