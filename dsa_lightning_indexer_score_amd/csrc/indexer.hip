@@ -316,7 +316,7 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
   // the ReLU / head-weight reduction of block j, so this wave's vector work
   // overlaps its own matrix work (the waves of a workgroup run in step
   // between the per-tile barriers and cannot cover each other).
-  auto tile_vals = [&](int buf, bool both, float (&vals)[2]) {
+  auto tile_vals = [&](int buf, bool both, float (&vals)[2], auto after_reads) {
     const uint8_t* tl = tile_lds[buf];
     f32x16 acc[2][HB];
     float sc[4];
@@ -358,10 +358,12 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
       issue(2);
       reduce(1);
       issue(3);
+      after_reads();  // the tile's last operand reads are issued
       reduce(2);
       reduce(3);
       vals[1] = ((lane < 32) ? sc[2] : sc[3]) + 0.0f;
     } else {
+      after_reads();
       reduce(1);
     }
     vals[0] = ((lane < 32) ? sc[0] : sc[1]) + 0.0f;
@@ -397,9 +399,17 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
     tile_ready();
 
     for (int v = 0; v < nv; ++v) {
-      // tile v is in LDS buffer v&1; tile v+1 streams into the other buffer
-      // (last read in tile v-1, before the barrier that ended it)
-      if (v + 1 < nv) load_tile(tile_start(v + 1), (v + 1) & 1);
+      // Tile v is in LDS buffer v&1; tile v+1 streams into the other buffer
+      // (last read in tile v-1, before the barrier that ended it). Its loads
+      // are issued after this wave's last operand read of tile v: the
+      // compiler cannot tell the two buffers apart and waits for every
+      // outstanding global-to-LDS load before an LDS read, so loads issued
+      // before the reads would be waited for before the tile is scored.
+      bool next_issued = false;
+      auto next_tile = [&]() {
+        if (v + 1 < nv) load_tile(tile_start(v + 1), (v + 1) & 1);
+        next_issued = true;
+      };
       if (MODE == 1 && v == nsamp && nsamp > 0 && compute_row) {
         // threshold = m-th largest sampled order key (binary search on bits)
         const int nkeys = nsamp * kKeyTile;
@@ -422,7 +432,7 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
         // sampled keys are all <= t_first <= t
         if (compute_row) {
           float vals[2];
-          tile_vals(v & 1, true, vals);
+          tile_vals(v & 1, true, vals, next_tile);
 #pragma unroll
           for (int half = 0; half < 2; ++half)
             my_samp[v * kKeyTile + half * 64 + lane] = order_key(vals[half]);
@@ -431,7 +441,7 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
         // the second half is skipped when it lies wholly above this row
         const bool both = tile_s0 + 64 <= t;
         float vals[2];
-        tile_vals(v & 1, both, vals);
+        tile_vals(v & 1, both, vals, next_tile);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int s = tile_s0 + half * 64 + lane;
@@ -468,6 +478,7 @@ void indexer_rows_kernel(const uint16_t* __restrict__ q_idx,
           if (s < Lk) my_scores[s] = -INFINITY;
         }
       }
+      if (!next_issued) next_tile();  // this wave scored no key of tile v
       tile_ready();
     }
 
