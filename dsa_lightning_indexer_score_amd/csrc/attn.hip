@@ -364,10 +364,17 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     s_cur = s_nxt;
     __syncthreads();
   };
-  for (int j = 0; j < nrun; j += 2) {
+  // Pairs of iterations, then a last single one: the loop's back edge
+  // follows only the second of a pair, so the loads the first one issues are
+  // never pending at the top of the loop (a path from the first straight
+  // back to the top made the compiler wait there for them, a whole iteration
+  // before they are staged).
+  int j = 0;
+  for (; j + 1 < nrun; j += 2) {
     iteration(j, ka_, va_, kb_, vb_);
-    if (j + 1 < nrun) iteration(j + 1, kb_, vb_, ka_, va_);
+    iteration(j + 1, kb_, vb_, ka_, va_);
   }
+  if (j < nrun) iteration(j, ka_, va_, kb_, vb_);
 
   if (!active || h >= H) return;
   const float lt = pair_sum(lsum);
