@@ -613,8 +613,15 @@ void indexer_split_topk_kernel(const uint16_t* __restrict__ q_idx,
                                u32x2* __restrict__ part, int* __restrict__ part_count,
                                const int32_t* __restrict__ q_pos) {
   constexpr int KS = DI / 16;
+  constexpr int NCH = DI / 8;         // 16-byte chunks per key row
+  constexpr int RPI = kWave / NCH;    // key rows per load instruction
+  constexpr int ROW_BYTES = DI * 2;
+  static_assert(32 / RPI == KS, "one load instruction per MFMA k-step");
   __shared__ __attribute__((aligned(16))) uint32_t skey[kDecChunk];
   __shared__ SelectSmemT<kDecWaves * kWave> sel;
+  // per wave: one 32-key block of k_I rows, XOR-swizzled like the row
+  // kernel's tiles (position p of row r holds chunk p ^ (r % NCH))
+  __shared__ __attribute__((aligned(16))) uint8_t blk_lds[kDecWaves][32 * ROW_BYTES];
   const int chunk = blockIdx.x % nchunks;
   const size_t row = blockIdx.x / nchunks;  // b * Lq + i
   const int b = (int)(row / Lq);
@@ -651,20 +658,40 @@ void indexer_split_topk_kernel(const uint16_t* __restrict__ q_idx,
   const int e_end = min(e_begin + kDecKeysPerWave, n);
   const int nb = e_end > e_begin ? (e_end - e_begin + 31) / 32 : 0;
 
+  // A block's k_I rows are read in row layout (NCH lanes cover one row, so
+  // each load instruction covers whole 128-byte lines) with non-temporal
+  // loads (the stream has no reuse), then pass through the wave's LDS block
+  // into the MFMA operand layout. (Loads straight into the operand layout
+  // read each line in four instructions: the line must then stay cached,
+  // and marked non-temporal it is fetched again.)
   // Loads are issued unconditionally, at the last key for rows past the
   // keys (blocks past the wave's range included): their scores are never
   // stored, and loads under a branch would make the compiler wait for every
   // outstanding load at the top of the loop instead of for the oldest block.
   auto load_b = [&](int j, bf16x8* dst) {
-    const int s = min(c0 + e_begin + j * 32 + (lane & 31), Lk - 1);
+#pragma unroll
+    for (int q = 0; q < KS; ++q) {
+      const int s = min(c0 + e_begin + j * 32 + q * RPI + lane / NCH, Lk - 1);
+      dst[q] = __builtin_nontemporal_load(
+          reinterpret_cast<const bf16x8*>(kbase + (size_t)s * DI + (lane % NCH) * 8));
+    }
+  };
+  uint8_t* my_blk = blk_lds[wave];
+  auto to_operand = [&](bf16x8* b) {
+#pragma unroll
+    for (int q = 0; q < KS; ++q) {
+      const int r = q * RPI + lane / NCH, c = lane % NCH;
+      *reinterpret_cast<bf16x8*>(my_blk + r * ROW_BYTES + ((c ^ (r % NCH)) * 16)) = b[q];
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int c = ks * 2 + (lane >> 5);
-      dst[ks] = *reinterpret_cast<const bf16x8*>(kbase + (size_t)s * DI + c * 8);
+      const int r = lane & 31, c = ks * 2 + (lane >> 5);
+      b[ks] = *reinterpret_cast<const bf16x8*>(my_blk + r * ROW_BYTES + ((c ^ (r % NCH)) * 16));
     }
   };
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;  // range of the keys this lane stores
-  auto score_block = [&](int j, const bf16x8* bop) {
+  auto score_block = [&](int j, bf16x8* bop) {
+    to_operand(bop);
     float part0 = 0.0f, part1 = 0.0f;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
