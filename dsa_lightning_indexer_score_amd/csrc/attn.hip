@@ -204,6 +204,22 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   const uint16_t* vb = vmat + (size_t)b * Lk * D;
   const int32_t* irow = indices + (size_t)(active ? rowq : 0) * k;
 
+  // the row's index list through a buffer resource (a 32-bit offset, no
+  // 64-bit address registers): every load is issued unconditionally, at
+  // entry 0 when it lies outside the unit's slice
+  const __amdgpu_buffer_rsrc_t irsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(irow), (short)0, k * 4, 0x00020000);
+  auto raw_index = [&](int j) {
+    const int e = kbeg + j * 32 + (lane & 31);
+    const bool in = active && j < nblk && e < kend;
+    const int v = __builtin_amdgcn_raw_buffer_load_b32(irsrc, (in ? e : 0) * 4, 0, 0);
+    return in ? v : -1;
+  };
+  // the first blocks' index loads go out before the Q loads: loads complete
+  // in issue order, so the gathers that wait on the indices do not also wait
+  // for Q
+  const int rx0 = raw_index(0), rx1 = raw_index(1), rx2 = raw_index(2), rx3 = raw_index(3),
+            rx4 = raw_index(4);
   // Q^T (this wave's 32 heads) as the B operand of S^T = K . Q^T
   const int h = hb * 32 + (lane & 31);
   bf16x8 qb[KS];
@@ -262,17 +278,6 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   };
   // index of key (lane % 32) of block j; invalid entries gather row 0 and are
   // masked out of the softmax
-  // the row's index list through a buffer resource (a 32-bit offset, no
-  // 64-bit address registers): every load is issued unconditionally, at
-  // entry 0 when it lies outside the unit's slice
-  const __amdgpu_buffer_rsrc_t irsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(irow), (short)0, k * 4, 0x00020000);
-  auto raw_index = [&](int j) {
-    const int e = kbeg + j * 32 + (lane & 31);
-    const bool in = active && j < nblk && e < kend;
-    const int v = __builtin_amdgcn_raw_buffer_load_b32(irsrc, (in ? e : 0) * 4, 0, 0);
-    return in ? v : -1;
-  };
   auto resolve = [&](int idx, uint32_t* vmask) {
     const bool valid = idx >= 0 && idx < Lk;
     *vmask = (uint32_t)(ballot(valid) & 0xFFFFFFFFull);
@@ -317,9 +322,9 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   Rows ka_, kb_, va_, vb_;  // alternate register sets: (kb_, vb_) near, (ka_, va_) far
   Off off_prev;             // row offsets of the block whose K was issued last
   {
-    const Off o0 = offsets(resolve(raw_index(0), &vm0));
-    const Off o1 = offsets(resolve(raw_index(1), &vm1));
-    off_prev = offsets(resolve(raw_index(2), &vm2));
+    const Off o0 = offsets(resolve(rx0, &vm0));
+    const Off o1 = offsets(resolve(rx1, &vm1));
+    off_prev = offsets(resolve(rx2, &vm2));
     gather(kb8, o0, ka_);
     gather(vb8, o0, va_);
     gather(kb8, o1, kb_);
@@ -329,7 +334,7 @@ void sparse_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     stage_k(kb_, 1);
     gather(kb8, off_prev, kb_);  // K(2) in flight; vb_ holds V(1)
   }
-  int ix3 = raw_index(3), ix4 = raw_index(4);
+  int ix3 = rx3, ix4 = rx4;
   __syncthreads();
   f32x16 s_cur = qk(0);
   // iteration 0 stages K(2) over K(0): every wave of the unit must have read
