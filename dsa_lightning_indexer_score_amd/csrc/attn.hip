@@ -22,6 +22,11 @@
 // A unit covering only a slice of the list writes a partial result (bf16
 // output normalised by its own sum, plus that sum and the max); a second
 // kernel combines the slices of each row.
+//
+// For the stack's own caches (valid entries first, min(k, t+1) of them) the
+// blocks past a row's valid entries are skipped. Workgroups are dealt to the
+// XCDs in chunks of consecutive rows, every XCD taking chunks from the whole
+// range.
 #include "common.hpp"
 #include "kernels.hpp"
 

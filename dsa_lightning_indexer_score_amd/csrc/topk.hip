@@ -12,12 +12,15 @@
 // winners in position order; score order then ranks the winners by value
 // buckets (a bitonic sort when scores bunch on few values).
 //
-// Longer rows take two launches: one workgroup per (row, 8192-score chunk)
-// counts the top 11 bits of its keys into a global histogram slice, then one
-// 1024-thread workgroup per row sums its slices, resolves the top digit, and,
-// if the keys at or above that digit fit in LDS, gathers them there in
-// position order (refining first, in passes over the row, while they do not)
-// and finishes the selection on them.
+// Longer rows take two or three launches: one workgroup per (row,
+// 8192-score chunk) counts the top 11 bits of its keys into a global
+// histogram slice; past 16384 scores, one workgroup per (row, chunk) then
+// resolves the row's top digit from the slices and writes its chunk's keys
+// at or above it into the row's candidate list (position order, slots from
+// the earlier chunks' counts); last, one 1024-thread workgroup per row
+// selects from that list, or from the row itself when it holds at most
+// 16384 scores, or, when the list would not fit, refines the digit in passes
+// over the row and gathers the survivors into LDS itself.
 //
 // Candidate lists of (order key, position) pairs, in increasing position
 // order, come from the fused indexer (one list per row) or from the per-chunk
