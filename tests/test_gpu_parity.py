@@ -658,6 +658,31 @@ def test_distill_loss_matches_oracle(n, B, Lq, Lk, q_pos0):
     assert np.abs(grad.cpu().numpy() - wg).max() <= 2e-6
 
 
+@pytest.mark.parametrize("n,B,Lq,Lk,q_pos0", [
+    (3, 1, 12, 20000, 8186),   # last partial group crosses a 2048-key register boundary
+    (4, 2, 5, 32768, 32763),   # full rows of the longest register-held length
+    (2, 1, 9, 4100, 2040),     # tails 1, 2, 3 and none at one register width
+    (5, 1, 6, 600, 590),       # more teachers than the register path takes
+    (2, 1, 3, 33000, 32990),   # rows longer than the register path takes
+])
+def test_distill_loss_row_layouts(n, B, Lq, Lk, q_pos0):
+    g = torch.Generator().manual_seed(Lk + n)
+    logits = (torch.randn((B, Lq, Lk), generator=g) * 2.0).float()
+    P = _teachers(n, B, Lq, Lk, q_pos0, seed=Lk)
+    dl, dP = cu(logits), cu(P)
+    junk = torch.full((B, Lq, Lk), float("nan"), device="cuda")   # the gradient's memory
+    del junk                                                     # reused: zeros must be written
+    _say("distill layouts n=%d B=%d Lq=%d Lk=%d q_pos0=%d" % (n, B, Lq, Lk, q_pos0))
+    loss, grad = idxc.idxc_distill_loss(dl, dP, q_pos0)
+    loss_only, none = idxc.idxc_distill_loss(dl, dP, q_pos0, grad=False)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(loss, loss_only)
+    wl, wg = oracle.distill_loss(logits.double().numpy(), P.double().numpy(), q_pos0)
+    assert np.allclose(loss.cpu().numpy(), wl, rtol=1e-4, atol=1e-4)
+    assert np.abs(grad.cpu().numpy() - wg).max() <= 2e-6
+
+
 def test_distill_loss_zero_when_teachers_equal_student():
     B, Lq, Lk = 1, 40, 40
     g = torch.Generator().manual_seed(9)
