@@ -1002,6 +1002,32 @@ def test_full_size_single_layer_stack_sampled_rows():
     assert same <= ATOL and e2e <= E2E_ATOL
 
 
+def test_full_size_distill_loss_sampled_rows():
+    """idxc_distill_loss on the timed chunk (the last 2048 queries of a
+    32768-token context, an F layer and the three S layers it serves as
+    teachers); sampled rows against the oracle one by one."""
+    Lq, Lk, n = 2048, 32768, 4
+    q_pos0 = Lk - Lq
+    _say("full size distillation loss Lq=%d Lk=%d teachers=%d" % (Lq, Lk, n))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    logits = torch.randn((1, Lq, Lk), generator=g, device="cuda") * 2.0
+    P = torch.rand((n, 1, Lq, Lk), generator=g, device="cuda")
+    causal = torch.arange(Lk, device="cuda").view(1, Lk) <= (q_pos0 + torch.arange(
+        Lq, device="cuda")).view(Lq, 1)
+    P *= causal
+    P /= P.sum(-1, keepdim=True)
+    loss, grad = idxc.idxc_distill_loss(logits, P, q_pos0)
+    torch.cuda.synchronize()
+    for i in (0, 1, 2, 3, 511, 1024, 2045, 2047):
+        t = q_pos0 + i
+        wl, wg = oracle.distill_loss(logits[:, i:i + 1].double().cpu().numpy(),
+                                     P[:, :, i:i + 1].double().cpu().numpy(), t)
+        assert abs(loss[0, i].item() - wl[0, 0]) <= 1e-4 * (1 + abs(wl[0, 0])), i
+        assert np.abs(grad[0, i].cpu().numpy() - wg[0, 0]).max() <= 2e-6, i
+    del logits, P, grad
+
+
 def test_full_size_long_context_last_chunk_sampled_rows():
     # the last 4096-query chunk of a 196608-token context against all keys
     L_all, chunk, k = gen.C5_L, gen.C5_CHUNK, 2048
