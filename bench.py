@@ -987,6 +987,10 @@ def main():
         log("distillation loss (4 teachers, 2048 x 32768 chunk): %.3f ms, %.0f GB/s"
             % (dl["ms"], dl["GBs"]))
         extra["distill_loss"] = dl
+        dll = distill_rate(Lq=512, Lk=131072)
+        log("distillation loss (4 teachers, 512 x 131072 chunk, streamed rows): %.3f ms, %.0f GB/s"
+            % (dll["ms"], dll["GBs"]))
+        extra["distill_loss_long_rows"] = dll
         tk = {"decode_rows": standalone_topk(64, 1, 65536, 65535, 2048),
               "prefill_rows": standalone_topk(1, 8192, 8192, 0, 2048),
               "decode_rows_position_order": standalone_topk(64, 1, 65536, 65535, 2048,

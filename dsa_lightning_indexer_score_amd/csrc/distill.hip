@@ -15,8 +15,10 @@
 // serves under the usual patterns) keep the row's logits in registers: each
 // logit is read once, each teacher entry once, each gradient entry written
 // once. Pass 1 takes the log-sum-exp of the held logits (keys 0..t); pass 2
-// streams the teachers and writes the gradient. Other rows run the same two
-// passes reading the logits twice. The row's loss
+// streams the teachers and writes the gradient. Other aligned rows (longer,
+// or more teachers) run the same two passes streamed, reading the logits
+// twice; rows that are not 16-byte aligned, one key per thread at a time.
+// The row's loss
 // sum_s [ (1/n) sum_j p_j log p_j - p_bar log q ] (terms with p = 0 are 0) is
 // reduced in a fixed order (per thread, then per wave, then over the waves).
 #include "common.hpp"
@@ -37,13 +39,12 @@ __device__ __forceinline__ void lse_merge(float& m, float& z, float m2, float z2
   m = M;
 }
 
-// Per-thread work on 4 consecutive keys at a time (16-byte loads) when rows
-// start 16-byte aligned (VEC: Lk % 4 == 0), single keys otherwise.
-template <bool VEC>
+// Rows that do not start 16-byte aligned (Lk % 4 != 0): the two passes one
+// key per thread at a time, the logits read twice.
 __global__ __launch_bounds__(kDistThreads)
-void distill_kernel(const float* __restrict__ logits, const float* __restrict__ teachers,
-                    int n_teachers, int Lq, int Lk, int q_pos0, size_t teacher_stride,
-                    float* __restrict__ row_loss, float* __restrict__ grad) {
+void distill_scalar_kernel(const float* __restrict__ logits, const float* __restrict__ teachers,
+                           int n_teachers, int Lq, int Lk, int q_pos0, size_t teacher_stride,
+                           float* __restrict__ row_loss, float* __restrict__ grad) {
   __shared__ float red_m[kDistWaves], red_z[kDistWaves], red_l[kDistWaves];
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -51,27 +52,19 @@ void distill_kernel(const float* __restrict__ logits, const float* __restrict__ 
   const size_t row = blockIdx.x;
   const int t = q_pos0 + (int)(row % Lq);
   const int n = min(t + 1, Lk);
-  const int nv = VEC ? (n & ~3) : 0;  // keys handled 4 at a time
   const float* x = logits + row * Lk;
 
   // ---- pass 1: log-sum-exp of the row's logits
   float m = -INFINITY, z = 0.0f;
-  auto add = [&](float v) {
+  for (int s = tid; s < n; s += kDistThreads) {
+    const float v = x[s];
     if (v > m) {
       z = z * __expf(m - v) + 1.0f;
       m = v;
     } else {
       z += __expf(v - m);
     }
-  };
-  for (int s = tid * 4; s < nv; s += kDistThreads * 4) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(x + s);
-    add(v[0]);
-    add(v[1]);
-    add(v[2]);
-    add(v[3]);
   }
-  for (int s = nv + tid; s < n; s += kDistThreads) add(x[s]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     const float m2 = __shfl_xor(m, off, kWave);
@@ -94,39 +87,16 @@ void distill_kernel(const float* __restrict__ logits, const float* __restrict__ 
   float acc = 0.0f;
   const float* prow = teachers + row * Lk;
   float* grow = grad ? grad + row * Lk : nullptr;
-  for (int s = tid * 4; s < nv; s += kDistThreads * 4) {
-    const f32x4 lv = *reinterpret_cast<const f32x4*>(x + s);
-    f32x4 pbar = {0.0f, 0.0f, 0.0f, 0.0f};
-    float plogp = 0.0f;
-    for (int j = 0; j < n_teachers; ++j) {
-      const f32x4 p = *reinterpret_cast<const f32x4*>(prow + (size_t)j * teacher_stride + s);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        pbar[c] += p[c];
-        if (p[c] > 0.0f) plogp += p[c] * __logf(p[c]);
-      }
-    }
-    f32x4 gv;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float lq = lv[c] - lse;
-      const float pb = pbar[c] * inv_n;
-      acc -= pb * lq;
-      gv[c] = __expf(lq) - pb;
-    }
-    acc += plogp * inv_n;
-    if (grow) *reinterpret_cast<f32x4*>(grow + s) = gv;
-  }
-  for (int s = nv + tid; s < n; s += kDistThreads) {
+  for (int s = tid; s < n; s += kDistThreads) {
     const float lq = x[s] - lse;
     float pbar = 0.0f, plogp = 0.0f;
     for (int j = 0; j < n_teachers; ++j) {
-      const float p = prow[(size_t)j * teacher_stride + s];
+      const float p = __builtin_nontemporal_load(prow + (size_t)j * teacher_stride + s);
       pbar += p;
       if (p > 0.0f) plogp += p * __logf(p);
     }
     pbar *= inv_n;
-    acc += plogp * inv_n - pbar * lq;
+    acc += plogp * inv_n - (pbar > 0.0f ? pbar * lq : 0.0f);
     if (grow) grow[s] = __expf(lq) - pbar;
   }
   if (grow)
@@ -342,6 +312,155 @@ void distill_reg_kernel(const float* __restrict__ logits, const float* __restric
   }
 }
 
+// ---- streamed rows: aligned rows the register-held kernel does not take
+// (longer than 32768 keys, or more than four teachers). The same two passes
+// with the logits read twice (the second read, their last, mostly from the
+// last-level cache) and the teachers once; the teacher loads and the second
+// logit read carry the non-temporal hint. Loads go
+// through buffer resources sized to the row's full 4-key groups and are
+// issued unconditionally, four groups deep in pass 1 and two groups (and two
+// teachers) deep in pass 2; the partly valid last group is the owning
+// thread's, as in the register-held kernel.
+constexpr int kStreamThreads = 1024;  // measured faster than 512 with eight teachers
+
+template <int NTHR>
+__global__ __launch_bounds__(NTHR)
+void distill_stream_kernel(const float* __restrict__ logits, const float* __restrict__ teachers,
+                           int n_teachers, int Lq, int Lk, int q_pos0, size_t teacher_stride,
+                           float* __restrict__ row_loss, float* __restrict__ grad) {
+  constexpr int NW = NTHR / kWave;
+  __shared__ float red_m[NW], red_z[NW], red_l[NW];
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  const size_t row = blockIdx.x;
+  const int t = q_pos0 + (int)(row % Lq);
+  const int n = min(t + 1, Lk);
+  const int nvec = n >> 2;
+  const int tail = n & 3;
+  const bool tail_owner = tail != 0 && tid == nvec % NTHR;
+  const float* x = logits + row * Lk;
+  const __amdgpu_buffer_rsrc_t xr = span_rsrc(x, nvec * 16);
+
+  // ---- pass 1: online log-sum-exp over the row's logits
+  float m = -INFINITY, z = 0.0f;
+  auto add4 = [&](const f32x4& v) {
+    const float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+    if (mx > m) {
+      z *= exp_hw(m - mx);  // 0 while m is -inf
+      m = mx;
+    }
+    if (m != -INFINITY) z += exp_hw(v[0] - m) + exp_hw(v[1] - m) + exp_hw(v[2] - m) + exp_hw(v[3] - m);
+  };
+  for (int g0 = tid; g0 < nvec; g0 += 4 * NTHR) {
+    f32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           xr, (g0 + u * NTHR) * 16, 0, 0));
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (g0 + u * NTHR < nvec) add4(v[u]);
+  }
+  f32x4 xt = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  if (tail_owner) {
+    for (int e = 0; e < tail; ++e) xt[e] = x[4 * nvec + e];
+    add4(xt);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off, kWave);
+    const float z2 = __shfl_xor(z, off, kWave);
+    lse_merge_hw(m, z, m2, z2);
+  }
+  if (lane == 0) {
+    red_m[wave] = m;
+    red_z[wave] = z;
+  }
+  __syncthreads();
+  m = red_m[0];
+  z = red_z[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) lse_merge_hw(m, z, red_m[w], red_z[w]);
+  const float lse = m + __builtin_amdgcn_logf(z) * kLn2;
+
+  // ---- pass 2: teachers, gradient and loss terms over every group of the
+  // row (groups past the row's keys get zero gradients)
+  const float inv_n = 1.0f / (float)n_teachers;
+  const float* prow = teachers + row * Lk;
+  float* grow = grad ? grad + row * Lk : nullptr;
+  const __amdgpu_buffer_rsrc_t gr = span_rsrc(grow, grow ? Lk * 4 : 0);
+  const int ngrp = Lk >> 2;
+  float acc = 0.0f, acc_h2 = 0.0f;
+  for (int g0 = tid; g0 < ngrp; g0 += 2 * NTHR) {
+    f32x4 xv[2], pb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      xv[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            xr, (g0 + u * NTHR) * 16, 0, 2));
+      pb[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    float plogp = 0.0f;
+#pragma unroll 2
+    for (int j = 0; j < n_teachers; ++j) {
+      const __amdgpu_buffer_rsrc_t pr = span_rsrc(prow + (size_t)j * teacher_stride, nvec * 16);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const f32x4 p = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      pr, (g0 + u * NTHR) * 16, 0, 2));
+        pb[u] += p;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) plogp += plog2p(p[e]);
+      }
+    }
+    acc_h2 += plogp * inv_n;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int g = g0 + u * NTHR;
+      f32x4 gv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lq = g < nvec ? xv[u][e] - lse : -INFINITY;
+        const float pbe = pb[u][e] * inv_n;
+        acc -= pbe > 0.0f ? pbe * lq : 0.0f;
+        gv[e] = exp_hw(lq) - pbe;
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, gv), gr,
+                                             (tail != 0 && g == nvec) ? Lk * 4 : g * 16, 0, 0);
+    }
+  }
+  if (tail_owner) {
+    f32x4 pb = {0.0f, 0.0f, 0.0f, 0.0f};
+    float plogp = 0.0f;
+    for (int j = 0; j < n_teachers; ++j)
+      for (int e = 0; e < tail; ++e) {
+        const float p = prow[(size_t)j * teacher_stride + 4 * nvec + e];
+        pb[e] += p;
+        plogp += plog2p(p);
+      }
+    f32x4 gv = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int e = 0; e < tail; ++e) {
+      const float lq = xt[e] - lse;
+      const float pbe = pb[e] * inv_n;
+      acc -= pbe > 0.0f ? pbe * lq : 0.0f;
+      gv[e] = exp_hw(lq) - pbe;
+    }
+    acc_h2 += plogp * inv_n;
+    if (grow) *reinterpret_cast<f32x4*>(grow + 4 * nvec) = gv;
+  }
+  acc += acc_h2 * kLn2;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, kWave);
+  if (lane == 0) red_l[wave] = acc;
+  __syncthreads();
+  if (tid == 0 && row_loss) {
+    float l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) l += red_l[w];
+    row_loss[row] = l;
+  }
+}
+
 template <int CH>
 hipError_t launch_reg(const float* logits, const float* teachers, int n_teachers, int rows,
                       int Lq, int Lk, int q_pos0, size_t stride, float* row_loss, float* grad,
@@ -382,10 +501,11 @@ hipError_t launch_distill(const float* logits, const float* teachers, int n_teac
                                        row_loss, grad, st);
   }
   if (Lk % 4 == 0)
-    hipLaunchKernelGGL(distill_kernel<true>, dim3((unsigned)(B * Lq)), dim3(kDistThreads), 0, st,
-                       logits, teachers, n_teachers, Lq, Lk, q_pos0, stride, row_loss, grad);
+    hipLaunchKernelGGL(distill_stream_kernel<kStreamThreads>, dim3((unsigned)rows),
+                       dim3(kStreamThreads), 0, st, logits, teachers, n_teachers, Lq, Lk, q_pos0,
+                       stride, row_loss, grad);
   else
-    hipLaunchKernelGGL(distill_kernel<false>, dim3((unsigned)(B * Lq)), dim3(kDistThreads), 0, st,
+    hipLaunchKernelGGL(distill_scalar_kernel, dim3((unsigned)rows), dim3(kDistThreads), 0, st,
                        logits, teachers, n_teachers, Lq, Lk, q_pos0, stride, row_loss, grad);
   return hipGetLastError();
 }

@@ -664,6 +664,7 @@ def test_distill_loss_matches_oracle(n, B, Lq, Lk, q_pos0):
     (2, 1, 9, 4100, 2040),     # tails 1, 2, 3 and none at one register width
     (5, 1, 6, 600, 590),       # more teachers than the register path takes
     (2, 1, 3, 33000, 32990),   # rows longer than the register path takes
+    (2, 1, 3, 70000, 69990),   # long rows: 1024-thread workgroups
 ])
 def test_distill_loss_row_layouts(n, B, Lq, Lk, q_pos0):
     g = torch.Generator().manual_seed(Lk + n)
