@@ -350,6 +350,26 @@ def distill_rate(Lq=2048, Lk=32768, n_teachers=4, seed=0):
             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
+def overlap_rate(Lq=32768, Lk=32768, k=2048, seed=0):
+    """idxc_overlap on two [1, Lq, k] index tensors of one prefill layer's
+    shape (row t holds k causal positions drawn from [0, t], repeats
+    allowed); algorithmic bytes = both tensors read once (4 B per entry each)
+    + the three per-row outputs (12 B per row)."""
+    import torch
+    import dsa_lightning_indexer_score_amd as idxc
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    t = (torch.arange(Lq, device="cuda") + (Lk - Lq)).view(1, Lq, 1).float()
+    a = (torch.rand((1, Lq, k), generator=g, device="cuda") * (t + 1)).int()
+    b = (torch.rand((1, Lq, k), generator=g, device="cuda") * (t + 1)).int()
+    ms = events_ms(lambda: idxc.idxc_overlap(a, b, Lk), 5)
+    nbytes = 2 * Lq * k * 4 + Lq * 12
+    del a, b
+    torch.cuda.empty_cache()
+    return {"Lq": Lq, "Lk": Lk, "k": k, "ms": ms, "algorithmic_bytes": nbytes,
+            "GBs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
 def standalone_topk(B, Lq, Lk, q_pos0, k, seed=0, order="score"):
     """idxc_topk on materialised fp32 scores, in score order (sorted output)
     or position order (the index cache's order, no sort); algorithmic bytes =
@@ -991,6 +1011,10 @@ def main():
         log("distillation loss (4 teachers, 512 x 131072 chunk, streamed rows): %.3f ms, %.0f GB/s"
             % (dll["ms"], dll["GBs"]))
         extra["distill_loss_long_rows"] = dll
+        ov = overlap_rate()
+        log("cross-layer overlap (two 32768 x 2048 index tensors): %.3f ms, %.0f GB/s"
+            % (ov["ms"], ov["GBs"]))
+        extra["overlap_rate"] = ov
         tk = {"decode_rows": standalone_topk(64, 1, 65536, 65535, 2048),
               "prefill_rows": standalone_topk(1, 8192, 8192, 0, 2048),
               "decode_rows_position_order": standalone_topk(64, 1, 65536, 65535, 2048,

@@ -15,8 +15,9 @@
 // One workgroup per row. Each list is turned into a bitmap over [0, Lk) in
 // LDS with atomic ORs (the returned old word tells whether a position is new,
 // so duplicates count once), then the second list's new positions are tested
-// against the first bitmap. The lists are read once, coalesced: the kernel is
-// bound by HBM reads of the two index tensors.
+// against the first bitmap. The lists are read once, coalesced, with each
+// thread's entries loaded before its bitmap updates: the kernel is bound by
+// HBM reads of the two index tensors.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -25,6 +26,7 @@ namespace idxc {
 namespace {
 
 constexpr int kOvThreads = 256;
+constexpr int kOvBatch = 8;  // list entries per thread in flight
 
 __global__ __launch_bounds__(kOvThreads)
 void overlap_kernel(const int32_t* __restrict__ a, const int32_t* __restrict__ b, int k, int Lk,
@@ -36,28 +38,50 @@ void overlap_kernel(const int32_t* __restrict__ a, const int32_t* __restrict__ b
   uint32_t* bits_b = bits + words;
   const int tid = threadIdx.x;
   const size_t row = blockIdx.x;
-  for (int w = tid; w < 2 * words; w += kOvThreads) bits[w] = 0u;
-  __syncthreads();
-
   const int32_t* ar = a + row * k;
   const int32_t* br = b + row * k;
+  // Entries are loaded kOvBatch per thread at a time, all issued before the
+  // bitmap updates use them; lists of up to kOvThreads * kOvBatch entries
+  // (k <= 2048) also have B's entries loaded before A's bitmap is built.
+  auto load_batch = [&](const int32_t* r, int base, int (&p)[kOvBatch]) {
+#pragma unroll
+    for (int u = 0; u < kOvBatch; ++u) {
+      const int e = base + u * kOvThreads + tid;
+      p[u] = e < k ? __builtin_nontemporal_load(r + e) : -1;
+    }
+  };
+  const bool one_batch = k <= kOvThreads * kOvBatch;
+  int pa[kOvBatch], pb[kOvBatch];
+  load_batch(ar, 0, pa);
+  if (one_batch) load_batch(br, 0, pb);
+  // the bitmaps are cleared while the first loads are in flight
+  for (int w = tid; w < 2 * words; w += kOvThreads) bits[w] = 0u;
+  __syncthreads();
   int na = 0;
-  for (int e = tid; e < k; e += kOvThreads) {
-    const int p = ar[e];
-    if (p >= 0 && p < Lk) {
-      const uint32_t m = 1u << (p & 31);
-      na += (atomicOr(&bits_a[p >> 5], m) & m) ? 0 : 1;
+  for (int base = 0; base < k; base += kOvThreads * kOvBatch) {
+    if (base > 0) load_batch(ar, base, pa);
+#pragma unroll
+    for (int u = 0; u < kOvBatch; ++u) {
+      const int p = pa[u];
+      if (p >= 0 && p < Lk) {
+        const uint32_t m = 1u << (p & 31);
+        na += (atomicOr(&bits_a[p >> 5], m) & m) ? 0 : 1;
+      }
     }
   }
   __syncthreads();
   int nb = 0, ni = 0;
-  for (int e = tid; e < k; e += kOvThreads) {
-    const int p = br[e];
-    if (p >= 0 && p < Lk) {
-      const uint32_t m = 1u << (p & 31);
-      if (!(atomicOr(&bits_b[p >> 5], m) & m)) {
-        ++nb;
-        ni += (bits_a[p >> 5] & m) ? 1 : 0;
+  for (int base = 0; base < k; base += kOvThreads * kOvBatch) {
+    if (!one_batch) load_batch(br, base, pb);
+#pragma unroll
+    for (int u = 0; u < kOvBatch; ++u) {
+      const int p = pb[u];
+      if (p >= 0 && p < Lk) {
+        const uint32_t m = 1u << (p & 31);
+        if (!(atomicOr(&bits_b[p >> 5], m) & m)) {
+          ++nb;
+          ni += (bits_a[p >> 5] & m) ? 1 : 0;
+        }
       }
     }
   }
