@@ -897,10 +897,18 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.cand) {
     if (a.nseg == 1) {
       // one position-ordered list per row (the fused indexer's candidates)
+      // the fewest registers that hold the list: fewer registers, more waves
+      // per SIMD (20 pairs per thread: 82 VGPRs, five waves; 32: 110, four;
+      // 239 vs 315 us on the 32768-row prefill layer's lists of up to 5120)
+      if (a.stage_cap <= kRowThreads * 20) return launch_pairs_final<kSrcCand1, kRowThreads, 20>(a, 1, st);
+      if (a.stage_cap <= kRowThreads * 28) return launch_pairs_final<kSrcCand1, kRowThreads, 28>(a, 1, st);
       if (a.stage_cap <= kTopkChunk) return launch_pairs_final<kSrcCand1, kRowThreads, kRowR>(a, 1, st);
       return launch_pairs_final<kSrcCand1, kWideThreads, kWideR>(a, 1, st);
     }
     const int groups = topk_segment_groups(a.nseg, a.k);
+    // (up to four 2048-entry segments, a 65536-key decode row: 8 pairs per
+    // thread, half the per-thread work of 16; 13.2 vs 14.2 us)
+    if (groups <= 1 && a.stage_cap <= kWideThreads * 8) return launch_pairs_final<kSrcCandSeg, kWideThreads, 8>(a, 1, st);
     if (groups <= 1) return launch_pairs_final<kSrcCandSeg, kWideThreads, kWideR>(a, 1, st);
     // too many segments for one workgroup: the exact top-k of each group of
     // consecutive segments (into a.part), then of the groups' winners (every
