@@ -328,18 +328,23 @@ __device__ int rdx_emit_regs(const uint32_t (&key)[R], int n, Valid valid, const
 // buckets linear in the score value between the least and greatest winner:
 // bucket(x) = clamp(floor((x - lo) * 2048 / (hi - lo))), a non-decreasing
 // function of the key, so rank = winners in higher buckets + larger words in
-// the own bucket. The positions go to out[0..kk) in rank order through LDS
-// (coalesced stores), then -1 up to k. Returns false, having written no
-// output, when a bucket holds more than kMaxRankBucket winners (the caller
-// then sorts). `slots` takes kk 16-bit entries; the histogram is zero on
-// return either way (for the caller's sort, which does not use it).
+// the own bucket. Each thread reads its winners' words and buckets once; the
+// words are then scattered into bucket order over the same array (buckets
+// descending), and a winner's rank is its bucket's start plus the bucket's
+// members with larger words, read four at a time. The positions go to
+// out[0..kk) in rank order through LDS (coalesced stores), then -1 up to k.
+// Returns false, having written no output and left the words in place, when
+// a bucket holds more than kMaxRankBucket winners (the caller then sorts).
+// The histogram is zero on return either way (for the caller's sort, which
+// does not use it).
 // ---------------------------------------------------------------------------
 constexpr int kMaxRankBucket = 48;
 
 template <int NT, int NGRP>
 __device__ bool rdx_rank_output(uint64_t* words, int kk, int k, uint32_t wlo, uint32_t whi,
-                                uint16_t* slots, RdxSmem<NT, NGRP>& sm, int32_t* orow) {
+                                RdxSmem<NT, NGRP>& sm, int32_t* orow) {
   constexpr int BPT = kSelBins / NT;
+  constexpr int EPT = (kMaxK + NT - 1) / NT;
   const int tid = threadIdx.x;
   uint32_t* cur = sm.hist;  // packed 16-bit bucket counts, then cursors
   const float vlo = key_to_float(wlo), vhi = key_to_float(whi);
@@ -349,8 +354,17 @@ __device__ bool rdx_rank_output(uint64_t* words, int kk, int k, uint32_t wlo, ui
     const float x = (key_to_float((uint32_t)(w >> 32)) - vlo) * sc;  // NaN only for 0 * inf
     return (uint32_t)fminf(fmaxf(x, 0.0f), (float)(kSelBins - 1));
   };
-  // the histogram is zero here (rdx_resolve cleared it, or it was never used)
-  for (int sl = tid; sl < kk; sl += NT) hist16_add(cur, bucket_of(words[sl]));
+  // this thread's winners (slots tid + i * NT): words and buckets; the
+  // histogram is zero here (rdx_resolve cleared it, or it was never used)
+  uint64_t wv[EPT];
+  uint32_t bk[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int sl = tid + i * NT;
+    wv[i] = sl < kk ? words[sl] : 0ull;
+    bk[i] = bucket_of(wv[i]);
+    if (sl < kk) hist16_add(cur, bk[i]);
+  }
   __syncthreads();
   const int top = kSelBins - 1 - BPT * tid;
   int cnts[BPT];
@@ -386,35 +400,42 @@ __device__ bool rdx_rank_output(uint64_t* words, int kk, int k, uint32_t wlo, ui
     cur[(top - q) >> 1] = (start_hi << 16) | (uint32_t)acc;
     acc += cnts[q + 1];
   }
-  __syncthreads();
-  for (int sl = tid; sl < kk; sl += NT) {
-    const uint32_t b = bucket_of(words[sl]);
-    const uint32_t sh = (b & 1u) << 4;
-    const uint32_t old = atomicAdd(&cur[b >> 1], 1u << sh);
-    slots[(old >> sh) & 0xFFFFu] = (uint16_t)sl;
+  __syncthreads();  // also: every thread holds its words, so the array can be rewritten
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    if (tid + i * NT < kk) {
+      const uint32_t b = bk[i];
+      const uint32_t sh = (b & 1u) << 4;
+      const uint32_t old = atomicAdd(&cur[b >> 1], 1u << sh);
+      words[(old >> sh) & 0xFFFFu] = wv[i];
+    }
   }
   __syncthreads();
   // each cursor now holds its bucket's end; bucket b starts where bucket b+1 ends
   auto end_of = [&](uint32_t b) { return (cur[b >> 1] >> ((b & 1u) << 4)) & 0xFFFFu; };
-  constexpr int EPT = (kMaxK + NT - 1) / NT;
   uint32_t rk[EPT], pv[EPT];
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
-    const int sl = tid + i * NT;
     rk[i] = 0u;
     pv[i] = 0u;
-    if (sl < kk) {
-      const uint64_t w = words[sl];
-      const uint32_t b = bucket_of(w);
+    if (tid + i * NT < kk) {
+      const uint64_t w = wv[i];
+      const uint32_t b = bk[i];
       const uint32_t e = end_of(b);
       const uint32_t st = b + 1 < (uint32_t)kSelBins ? end_of(b + 1) : 0u;
       uint32_t rank = st;
-      for (uint32_t j = st; j < e; ++j) rank += words[slots[j]] > w ? 1u : 0u;
+      for (uint32_t j = st; j < e; j += 4) {
+        uint64_t m[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) m[u] = words[min(j + u, e - 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) rank += (j + u < e && m[u] > w) ? 1u : 0u;
+      }
       rk[i] = rank;
       pv[i] = ~(uint32_t)(w & 0xFFFFFFFFull);
     }
   }
-  __syncthreads();  // every word and slot read: reuse the words' LDS for the output
+  __syncthreads();  // every word read: reuse the words' LDS for the output
   uint32_t* obuf = reinterpret_cast<uint32_t*>(words);
 #pragma unroll
   for (int i = 0; i < EPT; ++i)

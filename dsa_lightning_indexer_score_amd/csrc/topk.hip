@@ -272,7 +272,7 @@ __device__ __forceinline__ void load_pair_list(const u32x2* src, int n, uint32_t
 // Score-order finish: the kk winners' words are in `words`, their key range
 // in [wmin, wmax] per thread. Ranks them (or sorts them) into orow.
 template <int NT, int NGRP>
-__device__ void score_order_output(uint64_t* words, uint16_t* slots, int kk, int k,
+__device__ void score_order_output(uint64_t* words, int kk, int k,
                                    uint32_t wmin, uint32_t wmax, RdxSmem<NT, NGRP>& sm,
                                    int32_t* orow) {
   const int tid = threadIdx.x;
@@ -289,7 +289,7 @@ __device__ void score_order_output(uint64_t* words, uint16_t* slots, int kk, int
     whi = max(whi, sm.red[NT / kWave + w]);
   }
   __syncthreads();  // red is reused below
-  if (rdx_rank_output<NT, NGRP>(words, kk, k, wlo, whi, slots, sm, orow)) return;
+  if (rdx_rank_output<NT, NGRP>(words, kk, k, wlo, whi, sm, orow)) return;
   // bitonic sort of the kk winners padded with zero words (every winner's word
   // is nonzero, so they sort last); the first 256 threads hold the words
   static_assert(kMaxK == 8 * 256 && NT % 256 == 0, "register sort layout");
@@ -325,7 +325,6 @@ void topk_rows_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, i
   constexpr int NT = kRowThreads, R = kRowR, NGRP = R / 4;
   __shared__ RdxSmem<NT, NGRP> sm;
   __shared__ uint64_t words[OUT == kOutScore ? kMaxK : 2];
-  __shared__ uint16_t slots[OUT == kOutScore ? kMaxK : 2];
   const int tid = threadIdx.x;
   const int i = Lq - 1 - (int)(blockIdx.x / (unsigned)B);
   const int b = (int)(blockIdx.x % (unsigned)B);
@@ -361,7 +360,7 @@ void topk_rows_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, i
                                                    wmin = min(wmin, kv);
                                                    wmax = max(wmax, kv);
                                                  });
-    score_order_output<NT, NGRP>(words, slots, kk, k, wmin, wmax, sm, orow);
+    score_order_output<NT, NGRP>(words, kk, k, wmin, wmax, sm, orow);
   }
 }
 
@@ -528,7 +527,7 @@ __device__ void stream_level(const float* src, int n, RdxSmem<NT, NGRP>& sm, Rdx
 // fully resolved key: the keys above it and the first `rem` equal to it) into
 // LDS in position order, and the selection finishes on them in registers.
 // Dynamic LDS: RdxSmem, then kLongCap keys and kLongCap positions (the
-// score-order words and rank slots reuse the keys' area).
+// score-order words reuse the keys' area).
 // ---------------------------------------------------------------------------
 template <int OUT>
 __global__ __launch_bounds__(kWideThreads)
@@ -543,7 +542,6 @@ void topk_long_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, i
   uint32_t* ckey = reinterpret_cast<uint32_t*>(dyn + kOffKeys);
   uint32_t* cpos = ckey + kLongCap;
   uint64_t* words = reinterpret_cast<uint64_t*>(ckey);  // score order, after the keys are read
-  uint16_t* slots = reinterpret_cast<uint16_t*>(words + kMaxK);
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
@@ -729,7 +727,7 @@ void topk_long_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, i
           wmin = min(wmin, kv);
           wmax = max(wmax, kv);
         });
-    score_order_output<NT, NGRP>(words, slots, kk, k, wmin, wmax, sm, orow);
+    score_order_output<NT, NGRP>(words, kk, k, wmin, wmax, sm, orow);
   }
 }
 
@@ -749,7 +747,6 @@ void topk_pairs_kernel(TopkArgs a, int ngroups) {
   constexpr int NGRP = R / 4;
   __shared__ RdxSmem<NT, NGRP> sm;
   __shared__ uint64_t words[OUT == kOutScore ? kMaxK : 2];
-  __shared__ uint16_t slots[OUT == kOutScore ? kMaxK : 2];
   __shared__ int seg_off[kMaxSegments + 1];
   const int tid = threadIdx.x;
   const int row = (int)(blockIdx.x / (unsigned)ngroups);
@@ -825,7 +822,7 @@ void topk_pairs_kernel(TopkArgs a, int ngroups) {
           wmin = min(wmin, kv);
           wmax = max(wmax, kv);
         });
-    score_order_output<NT, NGRP>(words, slots, kk, k, wmin, wmax, sm, orow);
+    score_order_output<NT, NGRP>(words, kk, k, wmin, wmax, sm, orow);
   }
 }
 
