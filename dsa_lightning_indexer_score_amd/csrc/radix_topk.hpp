@@ -254,15 +254,15 @@ __device__ void rdx_search_regs(const uint32_t (&rel)[R], int n, RdxSmem<NT, NGR
   }
 }
 
-// Position-ordered emit of the winners held in registers (rel values, final
-// state st; valid(r) marks the row's elements and is only consulted when
-// every element is kept): emit(slot, rel, r) for every winner, slot = its
-// rank in position order. One block scan over all NGRP groups (one barrier;
-// wtot slot `buf`). Returns the number of winners, min(k, n).
-template <int NT, int NGRP, int G, int R, typename Valid, typename Emit>
-__device__ int rdx_emit_regs(const uint32_t (&key)[R], int n, Valid valid, const RdxState& st,
-                             RdxSmem<NT, NGRP>& sm, int buf, Emit emit) {
-  static_assert(R == NGRP * G && G == 4, "groups of four");
+// Position-ordered emit of the winners held in registers, by class: cls(r)
+// is 1 for a winner, 2 for an element tied with the threshold (the first
+// rem_eq of them in position order win), 0 otherwise; emit(slot, r) is called
+// for every winner, slot = its rank in position order. One block scan over
+// all NGRP groups (one barrier; wtot slot `buf`). Returns the number of
+// winners.
+template <int NT, int NGRP, int G, typename Cls, typename Emit>
+__device__ int rdx_emit_by(int n, Cls cls, int rem_eq, RdxSmem<NT, NGRP>& sm, int buf, Emit emit) {
+  static_assert(G == 4, "groups of four");
   constexpr int NW = NT / kWave;
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
@@ -278,14 +278,9 @@ __device__ int rdx_emit_regs(const uint32_t (&key)[R], int n, Valid valid, const
     if (v >= nvg) continue;  // workgroup-uniform
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      const int r = v * G + j;
-      if (st.all) {
-        if (valid(r)) kept[v] |= 1u << j;
-      } else {
-        const int c = rdx_class(key[r], st);
-        if (c == 1) kept[v] |= 1u << j;
-        else if (c == 2) eqm[v] |= 1u << j;
-      }
+      const int c = cls(v * G + j);
+      if (c == 1) kept[v] |= 1u << j;
+      else if (c == 2) eqm[v] |= 1u << j;
     }
     cnt[v] = __popc(kept[v]) | (__popc(eqm[v]) << 16);
     inc[v] = wave_incl_scan(cnt[v]);
@@ -293,7 +288,6 @@ __device__ int rdx_emit_regs(const uint32_t (&key)[R], int n, Valid valid, const
   }
   __syncthreads();
   int base = 0;  // packed (above, equal) counts of all earlier groups
-  const int rem = st.rem;
 #pragma unroll
   for (int v = 0; v < NGRP; ++v) {
     if (v >= nvg) continue;  // workgroup-uniform
@@ -307,19 +301,32 @@ __device__ int rdx_emit_regs(const uint32_t (&key)[R], int n, Valid valid, const
     base += tot;
     const int excl = before + inc[v] - cnt[v];
     int eq_before = excl >> 16;
-    int slot = (excl & 0xFFFF) + min(eq_before, rem);
+    int slot = (excl & 0xFFFF) + min(eq_before, rem_eq);
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       const int r = v * G + j;
       if ((kept[v] >> j) & 1u) {
-        emit(slot++, key[r], r);
+        emit(slot++, r);
       } else if ((eqm[v] >> j) & 1u) {
-        if (eq_before < rem) emit(slot++, key[r], r);
+        if (eq_before < rem_eq) emit(slot++, r);
         ++eq_before;
       }
     }
   }
-  return (base & 0xFFFF) + min(base >> 16, st.all || st.done ? 0 : rem);
+  return (base & 0xFFFF) + min(base >> 16, rem_eq);
+}
+
+// The same under a digit-search outcome (rel values, final state st; valid(r)
+// marks the row's elements and is only consulted when every element is
+// kept): emit(slot, rel, r). Returns the number of winners, min(k, n).
+template <int NT, int NGRP, int G, int R, typename Valid, typename Emit>
+__device__ int rdx_emit_regs(const uint32_t (&key)[R], int n, Valid valid, const RdxState& st,
+                             RdxSmem<NT, NGRP>& sm, int buf, Emit emit) {
+  static_assert(R == NGRP * G, "groups of four");
+  const bool all = st.all;
+  auto cls = [&](int r) { return all ? (valid(r) ? 1 : 0) : rdx_class(key[r], st); };
+  return rdx_emit_by<NT, NGRP, G>(n, cls, all || st.done ? 0 : st.rem, sm, buf,
+                                  [&](int slot, int r) { emit(slot, key[r], r); });
 }
 
 // ---------------------------------------------------------------------------

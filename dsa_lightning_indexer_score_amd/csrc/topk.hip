@@ -5,12 +5,17 @@
 // lower position, with -0.0 == +0.0, and rows shorter than k return all of
 // their t+1 positions followed by -1.
 //
-// Scores become order-preserving 32-bit keys held in registers (32 per thread
-// in 256-thread workgroups, one row each, for rows of up to 8192 scores; 16
-// per thread in 1024-thread workgroups for candidate lists of up to 16384
-// pairs). radix_topk.hpp finds the k-th best key digit by digit and emits the
-// winners in position order; score order then ranks the winners by value
-// buckets (a bitonic sort when scores bunch on few values).
+// A materialised row of up to 8192 scores is held in registers (32 per
+// thread, one 256-thread workgroup per row). Its threshold comes from 2048
+// buckets linear in the score over a sample of the row's range: the bucket
+// holding the k-th best score (typically a few dozen scores) is gathered and
+// ranked by one wave. Rows whose threshold bucket holds more than 64 scores
+// (ties, outliers) take the digit search below instead. Candidate lists
+// become order-preserving 32-bit keys held in registers (16 per thread in
+// 1024-thread workgroups for up to 16384 pairs), and radix_topk.hpp finds
+// the k-th best key digit by digit. Either way the winners leave in position
+// order; score order then ranks them by value buckets (a bitonic sort when
+// scores bunch on few values).
 //
 // Longer rows take two or three launches: one workgroup per (row,
 // 8192-score chunk) counts the top 11 bits of its keys into a global
@@ -220,9 +225,279 @@ __device__ __forceinline__ void load_row_keys(const float* src, int n, uint32_t 
   }
 }
 
+
+// One score row (n scores) as floats in registers, group v of this thread
+// being row group tid + NT*v; elements past the row become -inf.
+template <int NT, int R>
+__device__ __forceinline__ void load_row_floats(const float* src, int n, float (&x)[R]) {
+  const RowSrc rs = row_src(src, n);
+  const int tid = threadIdx.x;
+  const int nvg = rdx_live_groups<NT>(n);
+  u32x4 raw[R / 4];
+#pragma unroll
+  for (int v = 0; v < R / 4; ++v)
+    raw[v] = v < nvg ? row_load4(rs, tid + NT * v) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int v = 0; v < R / 4; ++v) {
+    if (v >= nvg) continue;  // workgroup-uniform
+    const int g = tid + NT * v;
+    row_fix_tail(rs, g, raw[v]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[4 * v + j] = __uint_as_float(raw[v][j]);
+    if (4 * g + 3 >= n) {  // the row's last group (or past the row)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * g + j >= n) x[4 * v + j] = -INFINITY;
+    }
+  }
+}
+
+// Least and greatest of this thread's row elements in its first and last
+// live groups (+inf / -inf if none): a sample of the row's range that takes
+// in both of its ends.
+template <int NT, int R>
+__device__ __forceinline__ void sample_range(const float (&x)[R], int n, float& mn, float& mx) {
+  const int tid = threadIdx.x;
+  const int nvg = rdx_live_groups<NT>(n);
+  mn = INFINITY;
+  mx = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < R / 4; ++v) {
+    if (v != 0 && v != nvg - 1) continue;  // workgroup-uniform
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (4 * (tid + NT * v) + j < n) {
+        mn = fminf(mn, x[4 * v + j]);
+        mx = fmaxf(mx, x[4 * v + j]);
+      }
+    }
+  }
+}
+
 template <int NT>
 __device__ __forceinline__ int elem_of(int r) {
   return 4 * ((int)threadIdx.x + NT * (r >> 2)) + (r & 3);
+}
+
+// orow[0..k) = obuf[0..kk), then -1: 16-byte stores when the row allows.
+template <int NT>
+__device__ __forceinline__ void store_row_positions(const int* obuf, int kk, int k, int32_t* orow) {
+  const int tid = threadIdx.x;
+  if ((k & 3) == 0 && (reinterpret_cast<uintptr_t>(orow) & 15) == 0) {
+    for (int j = 4 * tid; j < k; j += 4 * NT) {
+      int4 v = *reinterpret_cast<const int4*>(obuf + j);
+      if (j + 3 >= kk) {
+        v.x = j < kk ? v.x : -1;
+        v.y = j + 1 < kk ? v.y : -1;
+        v.z = j + 2 < kk ? v.z : -1;
+        v.w = -1;
+      }
+      *reinterpret_cast<int4*>(orow + j) = v;
+    }
+  } else {
+    for (int j = tid; j < k; j += NT) orow[j] = j < kk ? obuf[j] : -1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Threshold of a materialised score row by value buckets. The row's scores
+// (floats in registers, n > k of them, spanning [lo, hi], lo < hi finite) are
+// counted into kSelBins buckets linear in the value,
+//   bucket(x) = trunc(clamp(fma(x, sc, c), 0, kSelBins - 1)),
+//   sc = kSelBins / (hi - lo), c = -lo * sc,
+// a non-decreasing function of x (each step rounds monotonically), so the
+// k-th best score lies in the bucket b* where the count from the top first
+// reaches k, and every score in a higher bucket is a winner. Linear buckets
+// spread a row's scores evenly where the digits of their bit patterns would
+// pile them onto the few bins of a handful of exponents, so b* typically
+// holds a few dozen scores. Those are gathered into LDS and one wave ranks
+// them by value: the threshold T is the score of rank rem = k - (scores in
+// higher buckets) among them, and the winners are the scores above T and the
+// first rem_eq of the scores equal to T in position order. Returns false
+// (block-uniform; nothing written but LDS, and the histogram clear again)
+// when b* holds more than kVbCap scores.
+// ---------------------------------------------------------------------------
+constexpr int kVbCap = 64;
+
+constexpr int kVbGroups = kRowR / 4;            // element groups per thread
+constexpr int kVbWaves = kRowThreads / kWave;
+struct VbSmem {
+  float cv[kVbCap];  // b*'s scores and positions
+  int cp[kVbCap];
+  int cnt;
+  float thr;
+  int rem_eq;
+  int ok;
+  // the scores equal to T that win, as a bitmap over the row's positions,
+  // and per (element group, wave) whether it holds any of them
+  uint32_t eqbits[kTopkChunk / 32];
+  int eqflag[kVbGroups * kVbWaves];
+  int trash[kWave];  // targets of the stores of elements that lose
+  uint64_t trash64[kWave];
+};
+
+// Clears the tie bitmap and flags (needs a barrier before vb_threshold).
+__device__ __forceinline__ void vb_clear(VbSmem& vs) {
+  static_assert(kTopkChunk / 32 == kRowThreads && kVbGroups * kVbWaves <= kRowThreads,
+                "one word per thread");
+  vs.eqbits[threadIdx.x] = 0u;
+  if (threadIdx.x < kVbGroups * kVbWaves) vs.eqflag[threadIdx.x] = 0;
+}
+
+__device__ __forceinline__ float vb_y(float x, float sc, float c) { return fmaf(x, sc, c); }
+
+__device__ __forceinline__ uint32_t vb_bucket(float x, float sc, float c) {
+  return (uint32_t)__builtin_amdgcn_fmed3f(vb_y(x, sc, c), 0.0f, (float)(kSelBins - 1));
+}
+
+// sc and c for the row range [lo, hi], or false when value buckets do not
+// apply (block-uniform inputs).
+__device__ __forceinline__ bool vb_scale(float lo, float hi, float& sc, float& c) {
+  const float span = hi - lo;
+  if (!(span > 0.0f) || !(span <= 3.4028234663852886e38f)) return false;  // also NaN
+  sc = (float)kSelBins / span;
+  c = -lo * sc;
+  return sc <= 3.4028234663852886e38f && fabsf(c) <= 3.4028234663852886e38f;
+}
+
+template <int NT, int NGRP, int R>
+__device__ bool vb_threshold(const float (&x)[R], int n, int k, float sc, float c,
+                             RdxSmem<NT, NGRP>& sm, VbSmem& vs, float& thr, int& rem_eq) {
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int nvg = rdx_live_groups<NT>(n);
+  if (tid == 0) vs.cnt = 0;  // read after the barriers of the resolve below
+  // the groups holding row elements (the padding, -inf, lands in bucket 0,
+  // below every row element's rank while the row has more than k)
+#pragma unroll
+  for (int v = 0; v < NGRP; ++v) {
+    if (v < nvg && 4 * (tid + NT * v) < n) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) atomicAdd(&sm.hist[vb_bucket(x[4 * v + j], sc, c)], 1u);
+    }
+  }
+  __syncthreads();
+  RdxState st;
+  st.lo = 0u;
+  st.prefix = 0u;
+  st.sh0 = 0;
+  st.sh1 = 0;
+  st.rem = k;
+  st.level = 0;
+  st.done = false;
+  st.all = false;
+  const int cnt = rdx_resolve<NT, NGRP, false>(sm, st, 0);  // clears the histogram
+  if (cnt > kVbCap) return false;                           // block-uniform
+  const uint32_t bs = st.prefix;                            // b*
+  const int rem = st.rem;
+  // bucket(x) == b*  <=>  ylo <= fma(x, sc, c) < yhi
+  // (the top bucket has no upper bound: there y may overflow to +inf)
+  const float ylo = bs == 0u ? -INFINITY : (float)bs;
+  const bool top = bs == (uint32_t)(kSelBins - 1);
+  const float yhi = (float)(bs + 1u);
+#pragma unroll
+  for (int v = 0; v < NGRP; ++v) {
+    if (v < nvg && 4 * (tid + NT * v) < n) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float y = vb_y(x[4 * v + j], sc, c);
+        if (y >= ylo && (top || y < yhi)) {
+          const int s = atomicAdd(&vs.cnt, 1);
+          if (s < kVbCap) {
+            vs.cv[s] = x[4 * v + j];
+            vs.cp[s] = 4 * (tid + NT * v) + j;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    const int m = min(vs.cnt, kVbCap);
+    const float mine = lane < m ? vs.cv[lane] : -INFINITY;
+    int gt = 0, ge = 0;
+    for (int j = 0; j < m; ++j) {
+      const float u = vs.cv[j];
+      gt += u > mine ? 1 : 0;
+      ge += u >= mine ? 1 : 0;
+    }
+    const uint64_t hit = ballot(lane < m && gt < rem && rem <= ge);
+    const int src = hit ? __ffsll((unsigned long long)hit) - 1 : 0;
+    if (lane == 0) vs.ok = (hit && vs.cnt == cnt) ? 1 : 0;  // the gathered scores are b*'s
+    const float t = __shfl(mine, src, kWave);
+    const int req = rem - __shfl(gt, src, kWave);
+    if (lane == 0) {
+      vs.thr = t;
+      vs.rem_eq = req;
+    }
+    // the scores equal to T rank by position: the first req of them win
+    const int mp = lane < m ? vs.cp[lane] : 0x7FFFFFFF;
+    int rp = 0;
+    for (int j = 0; j < m; ++j) rp += (vs.cv[j] == t && vs.cp[j] < mp) ? 1 : 0;
+    if (hit && lane < m && mine == t && rp < req) {
+      const int g = mp >> 2;  // element group tid + NT*v of the row
+      atomicOr(&vs.eqbits[mp >> 5], 1u << (mp & 31));
+      vs.eqflag[(g / NT) * (NT / kWave) + (g % NT) / kWave] = 1;
+    }
+  }
+  __syncthreads();
+  thr = vs.thr;
+  rem_eq = vs.rem_eq;
+  return vs.ok != 0;
+}
+
+// Position-ordered winners after vb_threshold: the scores above T, and the
+// scores equal to T marked in the tie bitmap. Each thread keeps a 4-bit mask
+// of winners per element group; one block scan of the group counts gives the
+// groups' first slots, then emit(win, slot, r) runs for every element r of
+// the thread, slot being its rank among the winners in position order when
+// win (the callback stores without a branch per element: a loser's store
+// goes to a trash word). Returns the number of winners (k).
+template <int NT, int NGRP, int R, typename Emit>
+__device__ int vb_emit(const float (&x)[R], int n, float thr, RdxSmem<NT, NGRP>& sm, VbSmem& vs,
+                       Emit emit) {
+  constexpr int NW = NT / kWave;
+  static_assert(NGRP == kVbGroups && NT == kRowThreads, "tie flags per (group, wave)");
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  const int nvg = rdx_live_groups<NT>(n);
+  uint32_t msk[NGRP];
+  int inc[NGRP];
+#pragma unroll
+  for (int v = 0; v < NGRP; ++v) {
+    msk[v] = 0u;
+    inc[v] = 0;
+    if (v >= nvg) continue;  // workgroup-uniform
+    const int g = tid + NT * v;
+    uint32_t m = (x[4 * v] > thr ? 1u : 0u) | (x[4 * v + 1] > thr ? 2u : 0u) |
+                 (x[4 * v + 2] > thr ? 4u : 0u) | (x[4 * v + 3] > thr ? 8u : 0u);
+    if (vs.eqflag[v * NW + wave])  // wave-uniform: this group holds winning ties
+      m |= (vs.eqbits[g >> 3] >> (4 * (g & 7))) & 15u;
+    msk[v] = m;
+    inc[v] = wave_incl_scan(__popc(m));
+    if (lane == kWave - 1) sm.wtot[0][v * NW + wave] = inc[v];
+  }
+  __syncthreads();
+  int base = 0;  // winners of all earlier groups
+#pragma unroll
+  for (int v = 0; v < NGRP; ++v) {
+    if (v >= nvg) continue;  // workgroup-uniform
+    int before = base, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int y = sm.wtot[0][v * NW + w];
+      if (w < wave) before += y;
+      tot += y;
+    }
+    base += tot;
+    const uint32_t m = msk[v];
+    const int slot0 = before + inc[v] - __popc(m);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      emit(((m >> j) & 1u) != 0u, slot0 + __popc(m & ((1u << j) - 1u)), 4 * v + j);
+  }
+  return base;
 }
 
 // A position-ordered list of n (key, position) pairs into registers (element
@@ -315,11 +590,10 @@ __device__ void score_order_output(uint64_t* words, int kk, int k,
 // row, longest rows first. Row r = b*Lq + i holds candidates 0..t, t =
 // q_pos0 + i (never more than Lk).
 // ---------------------------------------------------------------------------
-// (position order fits six waves per SIMD in 80 registers: 58.8 vs 63.7 us
-// on 8192 causal rows of 8192; score order, asked for six, takes more
-// registers and runs at four, so it keeps the compiler's choice of five)
+// (position order fits six waves per SIMD in 80 registers; score order runs
+// at five: 134 vs 149 us at the four its register count would give)
 template <int OUT>
-__global__ __launch_bounds__(kRowThreads, OUT == kOutPos ? 6 : 1)
+__global__ __launch_bounds__(kRowThreads, OUT == kOutPos ? 6 : 5)
 void topk_rows_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, int q_pos0, int k,
                       int32_t* __restrict__ out) {
   constexpr int NT = kRowThreads, R = kRowR, NGRP = R / 4;
@@ -335,13 +609,77 @@ void topk_rows_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, i
     for (int j = tid; j < k; j += NT) orow[j] = j < n ? j : -1;
     return;
   }
-  rdx_clear(sm, kHistWords);
-  // A full score row spans most of the key space, so the digits are taken of
-  // the keys themselves (base 0): no key range to find. Elements past the row
-  // get key 0, below the key of every finite score.
+  rdx_clear(sm, kSelBins);  // 32-bit bucket counts (the digit search uses the first half)
+  __shared__ VbSmem vs;
+  vb_clear(vs);
+  float x[R];
+  load_row_floats<NT, R>(scores + row * Lk, n, x);
+  // A sample of the row's range sets the buckets (scores outside it fall
+  // into the end buckets, which keeps the bucket function monotonic): one
+  // barrier, which also orders the histogram clear.
+  {
+    float fmn, fmx;
+    sample_range<NT, R>(x, n, fmn, fmx);
+    uint32_t kmn = fmn <= fmx ? order_key(fmn) : 0xFFFFFFFFu;
+    uint32_t kmx = fmn <= fmx ? order_key(fmx) : 0u;
+    wave_minmax(kmn, kmx);
+    if (lane_id() == 0) {
+      sm.red[tid / kWave] = kmn;
+      sm.red[NT / kWave + tid / kWave] = kmx;
+    }
+  }
+  __syncthreads();
+  uint32_t klo = sm.red[0], khi = sm.red[NT / kWave];
+#pragma unroll
+  for (int w = 1; w < NT / kWave; ++w) {
+    klo = min(klo, sm.red[w]);
+    khi = max(khi, sm.red[NT / kWave + w]);
+  }
+  float sc = 0.0f, c = 0.0f, thr = 0.0f;
+  int rem_eq = 0;
+  if (n > k && vb_scale(key_to_float(klo), key_to_float(khi), sc, c) &&
+      vb_threshold<NT, NGRP, R>(x, n, k, sc, c, sm, vs, thr, rem_eq)) {  // block-uniform
+    const int lane = lane_id();
+    if (OUT == kOutPos) {
+      // the winners' positions gather in LDS by slot (over the histogram, not
+      // read after vb_emit's barrier), then leave in 16-byte stores
+      static_assert(kSelBins >= kMaxK, "positions staged over the histogram");
+      int* obuf = reinterpret_cast<int*>(sm.hist);
+      const int kk = vb_emit<NT, NGRP, R>(x, n, thr, sm, vs, [&](bool win, int slot, int r) {
+        *(win ? obuf + slot : vs.trash + lane) = elem_of<NT>(r);
+      });
+      __syncthreads();
+      store_row_positions<NT>(obuf, kk, k, orow);
+    } else {
+      // the least winner is T; the greatest is the row's greatest score
+      const uint32_t wmin = order_key(thr);
+      uint32_t wmax = 0u;
+      const int kk = vb_emit<NT, NGRP, R>(x, n, thr, sm, vs, [&](bool win, int slot, int r) {
+        const uint32_t kv = order_key(x[r]);
+        *(win ? words + slot : vs.trash64 + lane) =
+            ((uint64_t)kv << 32) | (uint64_t)(~(uint32_t)elem_of<NT>(r));
+        wmax = max(wmax, win ? kv : 0u);
+      });
+      score_order_output<NT, NGRP>(words, kk, k, wmin, wmax, sm, orow);
+    }
+    return;
+  }
+  // Digit search over the keys (rows of at most k scores, or whose scores
+  // bunch in one value bucket). A full score row spans most of the key
+  // space, so the digits are taken of the keys themselves (base 0): no key
+  // range to find. Elements past the row get key 0, below the key of every
+  // finite score. The histogram is clear here.
   uint32_t key[R];
-  load_row_keys<NT, R>(scores + row * Lk, n, key);
-  __syncthreads();  // the histogram is clear
+  {
+    const int nvg = rdx_live_groups<NT>(n);
+#pragma unroll
+    for (int v = 0; v < NGRP; ++v) {
+      if (v >= nvg) continue;  // workgroup-uniform
+      const int g = tid + NT * v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) key[4 * v + j] = 4 * g + j < n ? order_key(x[4 * v + j]) : 0u;
+    }
+  }
   auto valid = [&](int r) { return elem_of<NT>(r) < n; };
   constexpr uint32_t lo = 0u;
   RdxState st = rdx_start(n, k, 0u, 0xFFFFFFFFu);

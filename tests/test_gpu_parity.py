@@ -1112,6 +1112,45 @@ def test_topk_random_shapes_exact(seed):
         assert np.array_equal(got.cpu().numpy(), exp)
 
 
+def _bucket_edge_rows(case, Lk, seed=21):
+    """Score rows whose k-th best score sits where the value-bucket selection
+    of materialised rows has its edges: in the top bucket, made of scores
+    above the sampled range (positions away from each thread's first and last
+    groups), in the bottom bucket below it, and tied with other scores of its
+    bucket."""
+    rng = np.random.default_rng(seed)
+    s = rng.standard_normal(Lk).astype(np.float32)
+    mid = np.arange(1200, min(Lk, 6000))
+    if case == "top":  # 30 scores far above the rest, with ties, k below 30
+        s[mid[:30]] = np.float32(50.0) + rng.integers(0, 4, 30).astype(np.float32)
+    elif case == "bottom":  # 60 scores far below the rest, with ties, n just above k
+        s[mid[:60]] = np.float32(-50.0) - rng.integers(0, 4, 60).astype(np.float32)
+    elif case == "tied":  # many copies of values near the k-th best
+        s[mid[::7]] = np.float32(0.6875)
+        s[mid[3::11]] = np.float32(0.671875)
+    else:  # "outliers": one huge score puts everything else in one bucket
+        s[mid[0]] = np.float32(1e30)
+    return torch.from_numpy(np.tile(s, (1, 1, 1)))
+
+
+@pytest.mark.parametrize("case,Lk,k", [
+    ("top", 8192, 16), ("top", 8192, 30), ("top", 4000, 29),
+    ("bottom", 2100, 2048), ("bottom", 2100, 2045),
+    ("tied", 8192, 2048), ("tied", 5000, 1500), ("tied", 3000, 2048),
+    ("outliers", 8192, 2048),
+])
+def test_topk_value_bucket_edges_exact(case, Lk, k):
+    _say("topk bucket edges %s Lk=%d k=%d" % (case, Lk, k))
+    s = _bucket_edge_rows(case, Lk)
+    q0 = Lk - 1
+    want = oracle.topk(s.numpy(), k, q0)
+    for order in ("score", "position"):
+        got = idxc.idxc_topk(cu(s), k, q_pos0=q0, order=order)
+        torch.cuda.synchronize()
+        exp = want if order == "score" else oracle.position_order(want)
+        assert np.array_equal(got.cpu().numpy(), exp)
+
+
 @pytest.mark.parametrize("seed", range(16))
 def test_sparse_attn_random_shapes(seed):
     # head counts off the 32-head blocks, both head dims, list lengths off the
