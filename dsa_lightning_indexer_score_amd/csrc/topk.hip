@@ -314,10 +314,19 @@ __device__ __forceinline__ void store_row_positions(const int* obuf, int kk, int
 // them by value: the threshold T is the score of rank rem = k - (scores in
 // higher buckets) among them, and the winners are the scores above T and the
 // first rem_eq of the scores equal to T in position order. Returns false
-// (block-uniform; nothing written but LDS, and the histogram clear again)
-// when b* holds more than kVbCap scores.
+// (block-uniform; nothing written but LDS) when b* holds more than kVbCap
+// scores. The histogram is left as counted.
 // ---------------------------------------------------------------------------
 constexpr int kVbCap = 64;
+
+// threadIdx.x as a value the compiler cannot tie to earlier uses: the group
+// indices derived from it are recomputed (one add) in each phase instead of
+// being kept live, or spilled, across the phases.
+__device__ __forceinline__ int fresh_tid() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
 
 constexpr int kVbGroups = kRowR / 4;            // element groups per thread
 constexpr int kVbWaves = kRowThreads / kWave;
@@ -377,27 +386,51 @@ __device__ bool vb_threshold(const float (&x)[R], int n, int k, float sc, float 
     }
   }
   __syncthreads();
-  RdxState st;
-  st.lo = 0u;
-  st.prefix = 0u;
-  st.sh0 = 0;
-  st.sh1 = 0;
-  st.rem = k;
-  st.level = 0;
-  st.done = false;
-  st.all = false;
-  const int cnt = rdx_resolve<NT, NGRP, false>(sm, st, 0);  // clears the histogram
-  if (cnt > kVbCap) return false;                           // block-uniform
-  const uint32_t bs = st.prefix;                            // b*
-  const int rem = st.rem;
+  // b*: the bucket where the count from the top first reaches k (a block
+  // scan of the 32-bit counts, bins in descending order; the thread whose
+  // range holds it reads its bins again)
+  {
+    constexpr int BPT = kSelBins / NT;
+    static_assert(BPT == 8, "two 16-byte histogram reads per thread");
+    const int wave = tid / kWave;
+    const int top = kSelBins - 1 - BPT * tid;
+    const u32x4* hp = reinterpret_cast<const u32x4*>(sm.hist + top - (BPT - 1));
+    const u32x4 a = hp[0], b = hp[1];
+    const int local = (int)(a.x + a.y + a.z + a.w + b.x + b.y + b.z + b.w);
+    const int incl = wave_incl_scan(local);
+    if (lane == kWave - 1) sm.scan[0][wave] = incl;
+    __syncthreads();
+    int excl = incl - local;
+#pragma unroll
+    for (int w = 0; w < NT / kWave; ++w)
+      if (w < wave) excl += sm.scan[0][w];
+    if (excl < k && excl + local >= k) {
+      int acc = excl;
+      for (int q = 0; q < BPT; ++q) {
+        const int c = (int)sm.hist[top - q];
+        if (acc < k && acc + c >= k) {
+          sm.bc[0][0] = top - q;
+          sm.bc[0][1] = acc;
+          sm.bc[0][2] = c;
+        }
+        acc += c;
+      }
+    }
+    __syncthreads();
+  }
+  const int cnt = sm.bc[0][2];
+  if (cnt > kVbCap) return false;  // block-uniform
+  const uint32_t bs = (uint32_t)sm.bc[0][0];  // b*
+  const int rem = k - sm.bc[0][1];
   // bucket(x) == b*  <=>  ylo <= fma(x, sc, c) < yhi
   // (the top bucket has no upper bound: there y may overflow to +inf)
   const float ylo = bs == 0u ? -INFINITY : (float)bs;
   const bool top = bs == (uint32_t)(kSelBins - 1);
   const float yhi = (float)(bs + 1u);
+  const int ftid = fresh_tid();
 #pragma unroll
   for (int v = 0; v < NGRP; ++v) {
-    if (v < nvg && 4 * (tid + NT * v) < n) {
+    if (v < nvg && 4 * (ftid + NT * v) < n) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float y = vb_y(x[4 * v + j], sc, c);
@@ -405,7 +438,7 @@ __device__ bool vb_threshold(const float (&x)[R], int n, int k, float sc, float 
           const int s = atomicAdd(&vs.cnt, 1);
           if (s < kVbCap) {
             vs.cv[s] = x[4 * v + j];
-            vs.cp[s] = 4 * (tid + NT * v) + j;
+            vs.cp[s] = 4 * (ftid + NT * v) + j;
           }
         }
       }
@@ -449,16 +482,16 @@ __device__ bool vb_threshold(const float (&x)[R], int n, int k, float sc, float 
 // Position-ordered winners after vb_threshold: the scores above T, and the
 // scores equal to T marked in the tie bitmap. Each thread keeps a 4-bit mask
 // of winners per element group; one block scan of the group counts gives the
-// groups' first slots, then emit(win, slot, r) runs for every element r of
-// the thread, slot being its rank among the winners in position order when
-// win (the callback stores without a branch per element: a loser's store
+// groups' first slots, then emit(win, slot, r, pos) runs for every element r
+// (row position pos) of the thread, slot being its rank among the winners in
+// position order when win (the callback stores without a branch per element: a loser's store
 // goes to a trash word). Returns the number of winners (k).
 template <int NT, int NGRP, int R, typename Emit>
 __device__ int vb_emit(const float (&x)[R], int n, float thr, RdxSmem<NT, NGRP>& sm, VbSmem& vs,
                        Emit emit) {
   constexpr int NW = NT / kWave;
   static_assert(NGRP == kVbGroups && NT == kRowThreads, "tie flags per (group, wave)");
-  const int tid = threadIdx.x;
+  const int tid = fresh_tid();
   const int lane = lane_id();
   const int wave = tid / kWave;
   const int nvg = rdx_live_groups<NT>(n);
@@ -495,7 +528,8 @@ __device__ int vb_emit(const float (&x)[R], int n, float thr, RdxSmem<NT, NGRP>&
     const int slot0 = before + inc[v] - __popc(m);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      emit(((m >> j) & 1u) != 0u, slot0 + __popc(m & ((1u << j) - 1u)), 4 * v + j);
+      emit(((m >> j) & 1u) != 0u, slot0 + __popc(m & ((1u << j) - 1u)), 4 * v + j,
+           4 * (tid + NT * v) + j);
   }
   return base;
 }
@@ -645,19 +679,20 @@ void topk_rows_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, i
       // read after vb_emit's barrier), then leave in 16-byte stores
       static_assert(kSelBins >= kMaxK, "positions staged over the histogram");
       int* obuf = reinterpret_cast<int*>(sm.hist);
-      const int kk = vb_emit<NT, NGRP, R>(x, n, thr, sm, vs, [&](bool win, int slot, int r) {
-        *(win ? obuf + slot : vs.trash + lane) = elem_of<NT>(r);
+      const int kk = vb_emit<NT, NGRP, R>(x, n, thr, sm, vs, [&](bool win, int slot, int, int p) {
+        *(win ? obuf + slot : vs.trash + lane) = p;
       });
       __syncthreads();
       store_row_positions<NT>(obuf, kk, k, orow);
     } else {
-      // the least winner is T; the greatest is the row's greatest score
+      // the least winner is T; the greatest is the row's greatest score.
+      // The bucket ranks need a clear histogram (ordered by vb_emit's barrier).
+      rdx_clear(sm, kSelBins / 2);
       const uint32_t wmin = order_key(thr);
       uint32_t wmax = 0u;
-      const int kk = vb_emit<NT, NGRP, R>(x, n, thr, sm, vs, [&](bool win, int slot, int r) {
+      const int kk = vb_emit<NT, NGRP, R>(x, n, thr, sm, vs, [&](bool win, int slot, int r, int p) {
         const uint32_t kv = order_key(x[r]);
-        *(win ? words + slot : vs.trash64 + lane) =
-            ((uint64_t)kv << 32) | (uint64_t)(~(uint32_t)elem_of<NT>(r));
+        *(win ? words + slot : vs.trash64 + lane) = ((uint64_t)kv << 32) | (uint64_t)(~(uint32_t)p);
         wmax = max(wmax, win ? kv : 0u);
       });
       score_order_output<NT, NGRP>(words, kk, k, wmin, wmax, sm, orow);
@@ -668,7 +703,9 @@ void topk_rows_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, i
   // bunch in one value bucket). A full score row spans most of the key
   // space, so the digits are taken of the keys themselves (base 0): no key
   // range to find. Elements past the row get key 0, below the key of every
-  // finite score. The histogram is clear here.
+  // finite score. The histogram may hold the value-bucket counts.
+  rdx_clear(sm, kHistWords);
+  __syncthreads();
   uint32_t key[R];
   {
     const int nvg = rdx_live_groups<NT>(n);
