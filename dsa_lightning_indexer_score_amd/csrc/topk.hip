@@ -341,6 +341,8 @@ struct VbSmem {
   // and per (element group, wave) whether it holds any of them
   uint32_t eqbits[kTopkChunk / 32];
   int eqflag[kVbGroups * kVbWaves];
+  int bstar;         // the bucket of the k-th best score
+  int bmax;          // most scores in one bucket above b* (score order)
   int trash[kWave];  // targets of the stores of elements that lose
   uint64_t trash64[kWave];
 };
@@ -392,7 +394,7 @@ __device__ bool vb_threshold(const float (&x)[R], int n, int k, float sc, float 
   {
     constexpr int BPT = kSelBins / NT;
     static_assert(BPT == 8, "two 16-byte histogram reads per thread");
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int top = kSelBins - 1 - BPT * tid;
     const u32x4* hp = reinterpret_cast<const u32x4*>(sm.hist + top - (BPT - 1));
     const u32x4 a = hp[0], b = hp[1];
@@ -421,6 +423,7 @@ __device__ bool vb_threshold(const float (&x)[R], int n, int k, float sc, float 
   const int cnt = sm.bc[0][2];
   if (cnt > kVbCap) return false;  // block-uniform
   const uint32_t bs = (uint32_t)sm.bc[0][0];  // b*
+  if (tid == 0) vs.bstar = (int)bs;           // read after the barriers below
   const int rem = k - sm.bc[0][1];
   // bucket(x) == b*  <=>  ylo <= fma(x, sc, c) < yhi
   // (the top bucket has no upper bound: there y may overflow to +inf)
@@ -463,11 +466,15 @@ __device__ bool vb_threshold(const float (&x)[R], int n, int k, float sc, float 
       vs.thr = t;
       vs.rem_eq = req;
     }
-    // the scores equal to T rank by position: the first req of them win
+    // the scores equal to T rank by position: the first req of them win (a
+    // lone T wins without the ranking)
     const int mp = lane < m ? vs.cp[lane] : 0x7FFFFFFF;
+    const bool is_t = lane < m && mine == t;
     int rp = 0;
-    for (int j = 0; j < m; ++j) rp += (vs.cv[j] == t && vs.cp[j] < mp) ? 1 : 0;
-    if (hit && lane < m && mine == t && rp < req) {
+    if (popc64(ballot(is_t)) > 1) {
+      for (int j = 0; j < m; ++j) rp += (vs.cv[j] == t && vs.cp[j] < mp) ? 1 : 0;
+    }
+    if (hit && is_t && rp < req) {
       const int g = mp >> 2;  // element group tid + NT*v of the row
       atomicOr(&vs.eqbits[mp >> 5], 1u << (mp & 31));
       vs.eqflag[(g / NT) * (NT / kWave) + (g % NT) / kWave] = 1;
@@ -493,7 +500,7 @@ __device__ int vb_emit(const float (&x)[R], int n, float thr, RdxSmem<NT, NGRP>&
   static_assert(NGRP == kVbGroups && NT == kRowThreads, "tie flags per (group, wave)");
   const int tid = fresh_tid();
   const int lane = lane_id();
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int nvg = rdx_live_groups<NT>(n);
   uint32_t msk[NGRP];
   int inc[NGRP];
@@ -532,6 +539,122 @@ __device__ int vb_emit(const float (&x)[R], int n, float thr, RdxSmem<NT, NGRP>&
            4 * (tid + NT * v) + j);
   }
   return base;
+}
+
+// Score order after vb_threshold, from the row's own bucket counts (still in
+// the histogram): buckets above b* hold winners only, so a winner's rank is
+// the number of scores in higher buckets plus the larger (key, ~position)
+// words in its own bucket. The counts become per-bucket cursors starting at
+// the scores above each bucket (a block scan), every winner takes a slot of
+// its bucket's range with an LDS atomic and stores its word there, and each
+// slot then ranks its word within its bucket (its members lie between the
+// next bucket's cursor and its own). The positions leave in rank order
+// through LDS. Returns false (block-uniform, nothing written but LDS) when a
+// bucket above b* holds more than kMaxRankBucket scores: the caller then
+// ranks by the position-order emit and score_order_output.
+template <int NT, int NGRP, int R>
+__device__ bool vb_score_order(const float (&x)[R], int n, int k, float thr, float sc, float c,
+                               RdxSmem<NT, NGRP>& sm, VbSmem& vs, uint64_t* words,
+                               int32_t* orow) {
+  constexpr int NW = NT / kWave;
+  constexpr int BPT = kSelBins / NT;
+  static_assert(BPT == 8 && NGRP == kVbGroups && NT == kRowThreads, "layout as vb_threshold");
+  const int tid = fresh_tid();
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int bs = vs.bstar;
+  // ---- cursors: bin b <- scores in bins above b (thread t holds bins
+  // top-7 .. top, top = kSelBins-1-8t, in descending order by thread)
+  {
+    const int top = kSelBins - 1 - BPT * tid;
+    u32x4* hp = reinterpret_cast<u32x4*>(sm.hist + top - (BPT - 1));
+    const u32x4 a = hp[0], b = hp[1];  // bins top-7..top-4, top-3..top
+    const int local = (int)(a.x + a.y + a.z + a.w + b.x + b.y + b.z + b.w);
+    uint32_t most = 0u;  // greatest count of a bin above b*
+    const uint32_t cb[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (top - (BPT - 1) + q > bs) most = max(most, cb[q]);
+    const int incl = wave_incl_scan(local);
+    uint32_t unused = 0xFFFFFFFFu;
+    wave_minmax(unused, most);
+    if (lane == kWave - 1) sm.scan[1][wave] = incl;
+    if (lane == 0) sm.red[wave] = most;
+    __syncthreads();  // every bin is read
+    int excl = incl - local;
+    uint32_t bmax = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (w < wave) excl += sm.scan[1][w];
+      bmax = max(bmax, sm.red[w]);
+    }
+    u32x4 hi, lo;
+    hi.w = (uint32_t)excl;
+    hi.z = hi.w + b.w;
+    hi.y = hi.z + b.z;
+    hi.x = hi.y + b.y;
+    lo.w = hi.x + b.x;
+    lo.z = lo.w + a.w;
+    lo.y = lo.z + a.z;
+    lo.x = lo.y + a.y;
+    if (bmax > (uint32_t)kMaxRankBucket) return false;  // block-uniform; the counts stay
+    hp[0] = lo;
+    hp[1] = hi;
+  }
+  __syncthreads();  // cursors written
+  // ---- every winner takes a slot of its bucket's range
+  const int nvg = rdx_live_groups<NT>(n);
+#pragma unroll
+  for (int v = 0; v < NGRP; ++v) {
+    if (v >= nvg) continue;  // workgroup-uniform
+    const int g = tid + NT * v;
+    uint32_t m = (x[4 * v] > thr ? 1u : 0u) | (x[4 * v + 1] > thr ? 2u : 0u) |
+                 (x[4 * v + 2] > thr ? 4u : 0u) | (x[4 * v + 3] > thr ? 8u : 0u);
+    if (vs.eqflag[v * NW + wave])  // wave-uniform: this group holds winning ties
+      m |= (vs.eqbits[g >> 3] >> (4 * (g & 7))) & 15u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if ((m >> j) & 1u) {
+        const uint32_t bk = vb_bucket(x[4 * v + j], sc, c);
+        const uint32_t slot = atomicAdd(&sm.hist[bk], 1u);
+        words[slot] = ((uint64_t)order_key(x[4 * v + j]) << 32) | (uint64_t)(~(uint32_t)(4 * g + j));
+      }
+    }
+  }
+  __syncthreads();
+  // ---- rank of each bucket-ordered slot; bucket b spans [cursor(b+1), cursor(b))
+  constexpr int EPT = kMaxK / NT;
+  uint32_t rk[EPT], pv[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int sl = tid + i * NT;
+    rk[i] = 0u;
+    pv[i] = 0u;
+    if (sl < k) {
+      const uint64_t w = words[sl];
+      const uint32_t bk = vb_bucket(key_to_float((uint32_t)(w >> 32)), sc, c);
+      const uint32_t e = sm.hist[bk];
+      const uint32_t st = bk + 1 < (uint32_t)kSelBins ? sm.hist[bk + 1] : 0u;
+      uint32_t rank = st;
+      for (uint32_t j = st; j < e; j += 4) {
+        uint64_t mm[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mm[u] = words[min(j + u, e - 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) rank += (j + u < e && mm[u] > w) ? 1u : 0u;
+      }
+      rk[i] = rank;
+      pv[i] = ~(uint32_t)(w & 0xFFFFFFFFull);
+    }
+  }
+  __syncthreads();  // every word read: the positions go over them
+  uint32_t* obuf = reinterpret_cast<uint32_t*>(words);
+#pragma unroll
+  for (int i = 0; i < EPT; ++i)
+    if (tid + i * NT < k) obuf[rk[i]] = pv[i];
+  __syncthreads();
+  store_row_positions<NT>(reinterpret_cast<const int*>(obuf), k, k, orow);
+  return true;
 }
 
 // A position-ordered list of n (key, position) pairs into registers (element
@@ -685,6 +808,7 @@ void topk_rows_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, i
       __syncthreads();
       store_row_positions<NT>(obuf, kk, k, orow);
     } else {
+      if (vb_score_order<NT, NGRP, R>(x, n, k, thr, sc, c, sm, vs, words, orow)) return;
       // the least winner is T; the greatest is the row's greatest score.
       // The bucket ranks need a clear histogram (ordered by vb_emit's barrier).
       rdx_clear(sm, kSelBins / 2);
