@@ -149,7 +149,7 @@ __device__ __forceinline__ void rdx_key_range(uint32_t kmin, uint32_t kmax,
 // needed before counting into it again. par: the slot parity of this level
 // (alternate between consecutive levels). Returns the bin's count.
 template <int NT, int NGRP, bool PACKED>
-__device__ int rdx_resolve(RdxSmem<NT, NGRP>& sm, RdxState& st, int par) {
+__device__ __forceinline__ int rdx_resolve(RdxSmem<NT, NGRP>& sm, RdxState& st, int par) {
   constexpr int BPT = kSelBins / NT;  // bins per thread, >= 2
   constexpr int NW = NT / kWave;
   static_assert(BPT >= 2 && BPT % 2 == 0, "whole histogram words per thread");
@@ -216,7 +216,7 @@ __device__ __forceinline__ int rdx_live_groups(int n) {
 }
 
 template <int NT, int NGRP, int R>
-__device__ void rdx_search_regs(const uint32_t (&rel)[R], int n, RdxSmem<NT, NGRP>& sm,
+__device__ __forceinline__ void rdx_search_regs(const uint32_t (&rel)[R], int n, RdxSmem<NT, NGRP>& sm,
                                 RdxState& st) {
   static_assert(R == 4 * NGRP, "groups of four");
   if (st.all) return;  // block-uniform
@@ -261,7 +261,7 @@ __device__ void rdx_search_regs(const uint32_t (&rel)[R], int n, RdxSmem<NT, NGR
 // all NGRP groups (one barrier; wtot slot `buf`). Returns the number of
 // winners.
 template <int NT, int NGRP, int G, typename Cls, typename Emit>
-__device__ int rdx_emit_by(int n, Cls cls, int rem_eq, RdxSmem<NT, NGRP>& sm, int buf, Emit emit) {
+__device__ __forceinline__ int rdx_emit_by(int n, Cls cls, int rem_eq, RdxSmem<NT, NGRP>& sm, int buf, Emit emit) {
   static_assert(G == 4, "groups of four");
   constexpr int NW = NT / kWave;
   const int lane = lane_id();
@@ -320,7 +320,7 @@ __device__ int rdx_emit_by(int n, Cls cls, int rem_eq, RdxSmem<NT, NGRP>& sm, in
 // marks the row's elements and is only consulted when every element is
 // kept): emit(slot, rel, r). Returns the number of winners, min(k, n).
 template <int NT, int NGRP, int G, int R, typename Valid, typename Emit>
-__device__ int rdx_emit_regs(const uint32_t (&key)[R], int n, Valid valid, const RdxState& st,
+__device__ __forceinline__ int rdx_emit_regs(const uint32_t (&key)[R], int n, Valid valid, const RdxState& st,
                              RdxSmem<NT, NGRP>& sm, int buf, Emit emit) {
   static_assert(R == NGRP * G, "groups of four");
   const bool all = st.all;
@@ -351,7 +351,7 @@ __device__ int rdx_emit_regs(const uint32_t (&key)[R], int n, Valid valid, const
 constexpr int kMaxRankBucket = 48;
 
 template <int NT, int NGRP>
-__device__ bool rdx_rank_output(uint64_t* words, int kk, int k, uint32_t wlo, uint32_t whi,
+__device__ __forceinline__ bool rdx_rank_output(uint64_t* words, int kk, int k, uint32_t wlo, uint32_t whi,
                                 RdxSmem<NT, NGRP>& sm, int32_t* orow) {
   constexpr int BPT = kSelBins / NT;
   constexpr int EPT = (kMaxK + NT - 1) / NT;

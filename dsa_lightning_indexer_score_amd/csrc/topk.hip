@@ -372,7 +372,7 @@ __device__ __forceinline__ bool vb_scale(float lo, float hi, float& sc, float& c
 }
 
 template <int NT, int NGRP, int R>
-__device__ bool vb_threshold(const float (&x)[R], int n, int k, float sc, float c,
+__device__ __forceinline__ bool vb_threshold(const float (&x)[R], int n, int k, float sc, float c,
                              RdxSmem<NT, NGRP>& sm, VbSmem& vs, float& thr, int& rem_eq) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -494,7 +494,7 @@ __device__ bool vb_threshold(const float (&x)[R], int n, int k, float sc, float 
 // position order when win (the callback stores without a branch per element: a loser's store
 // goes to a trash word). Returns the number of winners (k).
 template <int NT, int NGRP, int R, typename Emit>
-__device__ int vb_emit(const float (&x)[R], int n, float thr, RdxSmem<NT, NGRP>& sm, VbSmem& vs,
+__device__ __forceinline__ int vb_emit(const float (&x)[R], int n, float thr, RdxSmem<NT, NGRP>& sm, VbSmem& vs,
                        Emit emit) {
   constexpr int NW = NT / kWave;
   static_assert(NGRP == kVbGroups && NT == kRowThreads, "tie flags per (group, wave)");
@@ -553,7 +553,7 @@ __device__ int vb_emit(const float (&x)[R], int n, float thr, RdxSmem<NT, NGRP>&
 // bucket above b* holds more than kMaxRankBucket scores: the caller then
 // ranks by the position-order emit and score_order_output.
 template <int NT, int NGRP, int R>
-__device__ bool vb_score_order(const float (&x)[R], int n, int k, float thr, float sc, float c,
+__device__ __forceinline__ bool vb_score_order(const float (&x)[R], int n, int k, float thr, float sc, float c,
                                RdxSmem<NT, NGRP>& sm, VbSmem& vs, uint64_t* words,
                                int32_t* orow) {
   constexpr int NW = NT / kWave;
@@ -704,7 +704,7 @@ __device__ __forceinline__ void load_pair_list(const u32x2* src, int n, uint32_t
 // Score-order finish: the kk winners' words are in `words`, their key range
 // in [wmin, wmax] per thread. Ranks them (or sorts them) into orow.
 template <int NT, int NGRP>
-__device__ void score_order_output(uint64_t* words, int kk, int k,
+__device__ __forceinline__ void score_order_output(uint64_t* words, int kk, int k,
                                    uint32_t wmin, uint32_t wmax, RdxSmem<NT, NGRP>& sm,
                                    int32_t* orow) {
   const int tid = threadIdx.x;
