@@ -371,15 +371,14 @@ __device__ __forceinline__ bool vb_scale(float lo, float hi, float& sc, float& c
   return sc <= 3.4028234663852886e38f && fabsf(c) <= 3.4028234663852886e38f;
 }
 
+// Counts the row's scores into the 32-bit bucket bins (clear on entry), then
+// a barrier. Only groups holding row elements are counted; the padding in
+// the row's last group, -inf, lands in bucket 0 and never takes a slot.
 template <int NT, int NGRP, int R>
-__device__ __forceinline__ bool vb_threshold(const float (&x)[R], int n, int k, float sc, float c,
-                             RdxSmem<NT, NGRP>& sm, VbSmem& vs, float& thr, int& rem_eq) {
+__device__ __forceinline__ void vb_histogram(const float (&x)[R], int n, float sc, float c,
+                                             RdxSmem<NT, NGRP>& sm) {
   const int tid = threadIdx.x;
-  const int lane = lane_id();
   const int nvg = rdx_live_groups<NT>(n);
-  if (tid == 0) vs.cnt = 0;  // read after the barriers of the resolve below
-  // the groups holding row elements (the padding, -inf, lands in bucket 0,
-  // below every row element's rank while the row has more than k)
 #pragma unroll
   for (int v = 0; v < NGRP; ++v) {
     if (v < nvg && 4 * (tid + NT * v) < n) {
@@ -388,6 +387,16 @@ __device__ __forceinline__ bool vb_threshold(const float (&x)[R], int n, int k, 
     }
   }
   __syncthreads();
+}
+
+template <int NT, int NGRP, int R>
+__device__ __forceinline__ bool vb_threshold(const float (&x)[R], int n, int k, float sc, float c,
+                             RdxSmem<NT, NGRP>& sm, VbSmem& vs, float& thr, int& rem_eq) {
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int nvg = rdx_live_groups<NT>(n);
+  if (tid == 0) vs.cnt = 0;  // read after the barriers of the resolve below
+  vb_histogram<NT, NGRP, R>(x, n, sc, c, sm);
   // b*: the bucket where the count from the top first reaches k (a block
   // scan of the 32-bit counts, bins in descending order; the thread whose
   // range holds it reads its bins again)
@@ -549,13 +558,14 @@ __device__ __forceinline__ int vb_emit(const float (&x)[R], int n, float thr, Rd
 // its bucket's range with an LDS atomic and stores its word there, and each
 // slot then ranks its word within its bucket (its members lie between the
 // next bucket's cursor and its own). The positions leave in rank order
-// through LDS. Returns false (block-uniform, nothing written but LDS) when a
-// bucket above b* holds more than kMaxRankBucket scores: the caller then
-// ranks by the position-order emit and score_order_output.
+// through LDS. kk = the number of winners (k, or n for a row of at most k
+// scores, which takes every score: thr = -inf, vs.bstar = -1). Returns false
+// (block-uniform, nothing written but LDS) when a bucket above b* holds more
+// than kMaxRankBucket scores: the caller then takes another path.
 template <int NT, int NGRP, int R>
-__device__ __forceinline__ bool vb_score_order(const float (&x)[R], int n, int k, float thr, float sc, float c,
-                               RdxSmem<NT, NGRP>& sm, VbSmem& vs, uint64_t* words,
-                               int32_t* orow) {
+__device__ __forceinline__ bool vb_score_order(const float (&x)[R], int n, int k, int kk, float thr,
+                                               float sc, float c, RdxSmem<NT, NGRP>& sm,
+                                               VbSmem& vs, uint64_t* words, int32_t* orow) {
   constexpr int NW = NT / kWave;
   constexpr int BPT = kSelBins / NT;
   static_assert(BPT == 8 && NGRP == kVbGroups && NT == kRowThreads, "layout as vb_threshold");
@@ -630,7 +640,7 @@ __device__ __forceinline__ bool vb_score_order(const float (&x)[R], int n, int k
     const int sl = tid + i * NT;
     rk[i] = 0u;
     pv[i] = 0u;
-    if (sl < k) {
+    if (sl < kk) {
       const uint64_t w = words[sl];
       const uint32_t bk = vb_bucket(key_to_float((uint32_t)(w >> 32)), sc, c);
       const uint32_t e = sm.hist[bk];
@@ -651,9 +661,9 @@ __device__ __forceinline__ bool vb_score_order(const float (&x)[R], int n, int k
   uint32_t* obuf = reinterpret_cast<uint32_t*>(words);
 #pragma unroll
   for (int i = 0; i < EPT; ++i)
-    if (tid + i * NT < k) obuf[rk[i]] = pv[i];
+    if (tid + i * NT < kk) obuf[rk[i]] = pv[i];
   __syncthreads();
-  store_row_positions<NT>(reinterpret_cast<const int*>(obuf), k, k, orow);
+  store_row_positions<NT>(reinterpret_cast<const int*>(obuf), kk, k, orow);
   return true;
 }
 
@@ -808,7 +818,7 @@ void topk_rows_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, i
       __syncthreads();
       store_row_positions<NT>(obuf, kk, k, orow);
     } else {
-      if (vb_score_order<NT, NGRP, R>(x, n, k, thr, sc, c, sm, vs, words, orow)) return;
+      if (vb_score_order<NT, NGRP, R>(x, n, k, k, thr, sc, c, sm, vs, words, orow)) return;
       // the least winner is T; the greatest is the row's greatest score.
       // The bucket ranks need a clear histogram (ordered by vb_emit's barrier).
       rdx_clear(sm, kSelBins / 2);
@@ -822,6 +832,15 @@ void topk_rows_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, i
       score_order_output<NT, NGRP>(words, kk, k, wmin, wmax, sm, orow);
     }
     return;
+  }
+  // Score order of a row of at most k scores: every score wins, ranked from
+  // the row's bucket counts (the histogram is clear: vb_threshold never ran).
+  if (OUT == kOutScore && n <= k && vb_scale(key_to_float(klo), key_to_float(khi), sc, c)) {
+    if (tid == 0) vs.bstar = -1;  // every bucket's size is bounded; read after vb_histogram's barrier
+    vb_histogram<NT, NGRP, R>(x, n, sc, c, sm);
+    if (vb_score_order<NT, NGRP, R>(x, n, k, n, -INFINITY, sc, c, sm, vs, words, orow)) return;
+    rdx_clear(sm, kSelBins);  // the counts stay on that return
+    __syncthreads();
   }
   // Digit search over the keys (rows of at most k scores, or whose scores
   // bunch in one value bucket). A full score row spans most of the key
