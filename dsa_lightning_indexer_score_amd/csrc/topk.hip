@@ -611,6 +611,7 @@ __device__ __forceinline__ bool vb_score_order(const float (&x)[R], int n, int k
     hp[0] = lo;
     hp[1] = hi;
   }
+  if (tid < 3) words[kk + tid] = 0ull;  // padding read by the ranks below
   __syncthreads();  // cursors written
   // ---- every winner takes a slot of its bucket's range
   const int nvg = rdx_live_groups<NT>(n);
@@ -645,13 +646,16 @@ __device__ __forceinline__ bool vb_score_order(const float (&x)[R], int n, int k
       const uint32_t bk = vb_bucket(key_to_float((uint32_t)(w >> 32)), sc, c);
       const uint32_t e = sm.hist[bk];
       const uint32_t st = bk + 1 < (uint32_t)kSelBins ? sm.hist[bk + 1] : 0u;
+      // the slots past the bucket's end hold smaller words (lower buckets,
+      // then the zero padding past the winners), so reading them counts
+      // nothing: no bounds check per member
       uint32_t rank = st;
       for (uint32_t j = st; j < e; j += 4) {
         uint64_t mm[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) mm[u] = words[min(j + u, e - 1)];
+        for (int u = 0; u < 4; ++u) mm[u] = words[j + u];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) rank += (j + u < e && mm[u] > w) ? 1u : 0u;
+        for (int u = 0; u < 4; ++u) rank += mm[u] > w ? 1u : 0u;
       }
       rk[i] = rank;
       pv[i] = ~(uint32_t)(w & 0xFFFFFFFFull);
@@ -765,7 +769,7 @@ void topk_rows_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, i
                       int32_t* __restrict__ out) {
   constexpr int NT = kRowThreads, R = kRowR, NGRP = R / 4;
   __shared__ RdxSmem<NT, NGRP> sm;
-  __shared__ uint64_t words[OUT == kOutScore ? kMaxK : 2];
+  __shared__ uint64_t words[OUT == kOutScore ? kMaxK + 3 : 2];  // + padding of the bucket ranks
   const int tid = threadIdx.x;
   const int i = Lq - 1 - (int)(blockIdx.x / (unsigned)B);
   const int b = (int)(blockIdx.x % (unsigned)B);
