@@ -331,7 +331,8 @@ __device__ __forceinline__ int rdx_emit_regs(const uint32_t (&key)[R], int n, Va
 
 // ---------------------------------------------------------------------------
 // Score order: the kk winners' 64-bit words (key << 32 | ~position, all
-// distinct) in words[0..kk) are ranked into descending order through 2048
+// distinct) in words[0..kk) (the array holds kk + 3 words: the ranks read
+// three words of padding past the winners) are ranked into descending order through 2048
 // buckets linear in the score value between the least and greatest winner:
 // bucket(x) = clamp(floor((x - lo) * 2048 / (hi - lo))), a non-decreasing
 // function of the key, so rank = winners in higher buckets + larger words in
@@ -419,6 +420,7 @@ __device__ __forceinline__ bool rdx_rank_output(uint64_t* words, int kk, int k, 
       words[(old >> sh) & 0xFFFFu] = wv[i];
     }
   }
+  if (tid < 3) words[kk + tid] = 0ull;  // padding read by the ranks below
   __syncthreads();
   // each cursor now holds its bucket's end; bucket b starts where bucket b+1 ends
   auto end_of = [&](uint32_t b) { return (cur[b >> 1] >> ((b & 1u) << 4)) & 0xFFFFu; };
@@ -434,13 +436,15 @@ __device__ __forceinline__ bool rdx_rank_output(uint64_t* words, int kk, int k, 
       const uint32_t b = bucket_of(w);
       const uint32_t e = end_of(b);
       const uint32_t st = b + 1 < (uint32_t)kSelBins ? end_of(b + 1) : 0u;
+      // the slots past the bucket's end hold smaller words (lower buckets,
+      // then the zero padding past the winners): read without bounds checks
       uint32_t rank = st;
       for (uint32_t j = st; j < e; j += 4) {
         uint64_t m[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) m[u] = words[min(j + u, e - 1)];
+        for (int u = 0; u < 4; ++u) m[u] = words[j + u];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) rank += (j + u < e && m[u] > w) ? 1u : 0u;
+        for (int u = 0; u < 4; ++u) rank += m[u] > w ? 1u : 0u;
       }
       rk[i] = rank;
       pv[i] = ~(uint32_t)(w & 0xFFFFFFFFull);

@@ -1268,7 +1268,7 @@ __global__ __launch_bounds__(NT, (OUT == kOutPos && NT == kRowThreads && R <= 20
 void topk_pairs_kernel(TopkArgs a, int ngroups) {
   constexpr int NGRP = R / 4;
   __shared__ RdxSmem<NT, NGRP> sm;
-  __shared__ uint64_t words[OUT == kOutScore ? kMaxK : 2];
+  __shared__ uint64_t words[OUT == kOutScore ? kMaxK + 3 : 2];  // + padding of the bucket ranks
   __shared__ int seg_off[kMaxSegments + 1];
   const int tid = threadIdx.x;
   const int row = (int)(blockIdx.x / (unsigned)ngroups);
