@@ -761,10 +761,11 @@ __device__ __forceinline__ void score_order_output(uint64_t* words, int kk, int 
 // row, longest rows first. Row r = b*Lq + i holds candidates 0..t, t =
 // q_pos0 + i (never more than Lk).
 // ---------------------------------------------------------------------------
-// (position order fits six waves per SIMD in 80 registers; score order runs
-// at five: 134 vs 149 us at the four its register count would give)
+// (position order runs seven waves per SIMD in 72 registers: 46 vs 48 us at
+// six, its few spills outside the value-bucket path; score order runs at
+// five: six measured 119 vs 89 us)
 template <int OUT>
-__global__ __launch_bounds__(kRowThreads, OUT == kOutPos ? 6 : 5)
+__global__ __launch_bounds__(kRowThreads, OUT == kOutPos ? 7 : 5)
 void topk_rows_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, int q_pos0, int k,
                       int32_t* __restrict__ out) {
   constexpr int NT = kRowThreads, R = kRowR, NGRP = R / 4;
