@@ -592,8 +592,8 @@ void indexer_split_kernel(const uint16_t* __restrict__ q_idx,
 
 // ---------------------------------------------------------------------------
 // Split-key kernel with chunk-local top-k (few query rows, e.g. decode): a
-// workgroup of 8 waves owns one query row and a 16384-key chunk (2048 keys
-// per wave, three 32-key blocks in flight per wave), keeps the chunk's order
+// workgroup of 8 waves owns one query row and a 16384-key chunk (every eighth
+// 32-key block per wave, three blocks in flight per wave), keeps the chunk's order
 // keys in LDS and writes the chunk's exact top-k, in position order, as one
 // candidate segment; a selection launch over the row's segments finishes the
 // row. Every key of the row's top-k is in its chunk's top-k. (16384-key
@@ -602,7 +602,6 @@ void indexer_split_kernel(const uint16_t* __restrict__ q_idx,
 constexpr int kDecChunk = 16384;
 static_assert(kDecChunk <= kSelMaxKeys, "selection histogram counts fit 16 bits");
 constexpr int kDecWaves = 8;
-constexpr int kDecKeysPerWave = kDecChunk / kDecWaves;
 
 template <int DI, int HB>
 __global__ __launch_bounds__(kDecWaves * kWave, 2)
@@ -654,9 +653,12 @@ void indexer_split_topk_kernel(const uint16_t* __restrict__ q_idx,
   }
 
   const uint16_t* kbase = k_idx + (size_t)b * Lk * DI;
-  const int e_begin = wave * kDecKeysPerWave;  // chunk-local
-  const int e_end = min(e_begin + kDecKeysPerWave, n);
-  const int nb = e_end > e_begin ? (e_end - e_begin + 31) / 32 : 0;
+  // The waves take the chunk's 32-key blocks in turn (block j of wave w is
+  // block j * kDecWaves + w), so that a workgroup streams one contiguous
+  // range at a time rather than eight.
+  const int nblk = (n + 31) / 32;
+  const int nb = nblk > wave ? (nblk - wave + kDecWaves - 1) / kDecWaves : 0;
+  auto blk_key = [&](int j) { return (j * kDecWaves + wave) * 32; };  // chunk-local
 
   // A block's k_I rows are read in row layout (NCH lanes cover one row, so
   // each load instruction covers whole 128-byte lines) with non-temporal
@@ -671,7 +673,7 @@ void indexer_split_topk_kernel(const uint16_t* __restrict__ q_idx,
   auto load_b = [&](int j, bf16x8* dst) {
 #pragma unroll
     for (int q = 0; q < KS; ++q) {
-      const int s = min(c0 + e_begin + j * 32 + q * RPI + lane / NCH, Lk - 1);
+      const int s = min(c0 + blk_key(j) + q * RPI + lane / NCH, Lk - 1);
       dst[q] = __builtin_nontemporal_load(
           reinterpret_cast<const bf16x8*>(kbase + (size_t)s * DI + (lane % NCH) * 8));
     }
@@ -705,8 +707,8 @@ void indexer_split_topk_kernel(const uint16_t* __restrict__ q_idx,
       }
     }
     const float val = pair_sum(part0 + part1) + 0.0f;
-    const int e = e_begin + j * 32 + lane;
-    if (lane < 32 && e < e_end) {
+    const int e = blk_key(j) + lane;
+    if (lane < 32 && e < n) {
       const uint32_t key = order_key(val);
       skey[e] = key;
       kmin = min(kmin, key);
