@@ -342,7 +342,6 @@ struct VbSmem {
   uint32_t eqbits[kTopkChunk / 32];
   int eqflag[kVbGroups * kVbWaves];
   int bstar;         // the bucket of the k-th best score
-  int bmax;          // most scores in one bucket above b* (score order)
   int trash[kWave];  // targets of the stores of elements that lose
   uint64_t trash64[kWave];
 };
