@@ -17,15 +17,20 @@
 // order; score order then ranks them by value buckets (a bitonic sort when
 // scores bunch on few values).
 //
-// Longer rows take two or three launches: one workgroup per (row,
-// 8192-score chunk) counts the top 11 bits of its keys into a global
-// histogram slice; past 16384 scores, one workgroup per (row, chunk) then
-// resolves the row's top digit from the slices and writes its chunk's keys
-// at or above it into the row's candidate list (position order, slots from
-// the earlier chunks' counts); last, one 1024-thread workgroup per row
-// selects from that list, or from the row itself when it holds at most
-// 16384 scores, or, when the list would not fit, refines the digit in passes
-// over the row and gathers the survivors into LDS itself.
+// Rows of up to 65536 scores are held in registers by one 1024-thread
+// workgroup each (64 per thread), threshold again by value buckets; the
+// winners gather in an LDS bitmap and leave by one scan over it. Rows the
+// buckets do not settle take the digit search of the longer rows, its top
+// digit counted over the row.
+//
+// Longer rows take three launches: one workgroup per (row, 8192-score
+// chunk) counts the top 11 bits of its keys into a global histogram slice;
+// one workgroup per (row, chunk) then resolves the row's top digit from the
+// slices and writes its chunk's keys at or above it into the row's
+// candidate list (position order, slots from the earlier chunks' counts);
+// last, one 1024-thread workgroup per row selects from that list or, when the
+// list would not fit, refines the digit in passes over the row and gathers
+// the survivors into LDS itself.
 //
 // Candidate lists of (order key, position) pairs, in increasing position
 // order, come from the fused indexer (one list per row) or from the per-chunk
@@ -328,9 +333,9 @@ __device__ __forceinline__ int fresh_tid() {
   return t;
 }
 
-constexpr int kVbGroups = kRowR / 4;            // element groups per thread
-constexpr int kVbWaves = kRowThreads / kWave;
-struct VbSmem {
+// LDS of the selection of a row held by NT threads, NGRP element groups each.
+template <int NT, int NGRP>
+struct VbSmemT {
   float cv[kVbCap];  // b*'s scores and positions
   int cp[kVbCap];
   int cnt;
@@ -339,19 +344,23 @@ struct VbSmem {
   int ok;
   // the scores equal to T that win, as a bitmap over the row's positions,
   // and per (element group, wave) whether it holds any of them
-  uint32_t eqbits[kTopkChunk / 32];
-  int eqflag[kVbGroups * kVbWaves];
+  uint32_t eqbits[NT * NGRP * 4 / 32];
+  int eqflag[NGRP * (NT / kWave)];
   int bstar;         // the bucket of the k-th best score
   int trash[kWave];  // targets of the stores of elements that lose
   uint64_t trash64[kWave];
 };
 
+using VbSmem = VbSmemT<kRowThreads, kRowR / 4>;
+
 // Clears the tie bitmap and flags (needs a barrier before vb_threshold).
-__device__ __forceinline__ void vb_clear(VbSmem& vs) {
-  static_assert(kTopkChunk / 32 == kRowThreads && kVbGroups * kVbWaves <= kRowThreads,
-                "one word per thread");
-  vs.eqbits[threadIdx.x] = 0u;
-  if (threadIdx.x < kVbGroups * kVbWaves) vs.eqflag[threadIdx.x] = 0;
+template <int NT, int NGRP>
+__device__ __forceinline__ void vb_clear(VbSmemT<NT, NGRP>& vs) {
+  constexpr int kBits = NT * NGRP / 8, kFlags = NGRP * (NT / kWave);
+  static_assert(kBits % NT == 0 && kFlags <= NT, "whole bitmap words per thread");
+#pragma unroll
+  for (int w = 0; w < kBits / NT; ++w) vs.eqbits[(int)threadIdx.x + w * NT] = 0u;
+  if (threadIdx.x < kFlags) vs.eqflag[threadIdx.x] = 0;
 }
 
 __device__ __forceinline__ float vb_y(float x, float sc, float c) { return fmaf(x, sc, c); }
@@ -368,6 +377,37 @@ __device__ __forceinline__ bool vb_scale(float lo, float hi, float& sc, float& c
   sc = (float)kSelBins / span;
   c = -lo * sc;
   return sc <= 3.4028234663852886e38f && fabsf(c) <= 3.4028234663852886e38f;
+}
+
+// Bins p[0 .. BPT) of a 32-bit histogram, in 16- or 8-byte LDS reads
+// (p aligned to them), and their store.
+template <int BPT>
+__device__ __forceinline__ void vb_bins(const uint32_t* p, uint32_t (&cb)[BPT]) {
+  static_assert(BPT % 4 == 0 || BPT == 2, "whole 16- or 8-byte reads");
+  if constexpr (BPT == 2) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    cb[0] = v[0];
+    cb[1] = v[1];
+  } else {
+#pragma unroll
+    for (int q = 0; q < BPT; q += 4) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(p + q);
+      cb[q] = v.x;
+      cb[q + 1] = v.y;
+      cb[q + 2] = v.z;
+      cb[q + 3] = v.w;
+    }
+  }
+}
+template <int BPT>
+__device__ __forceinline__ void vb_store_bins(uint32_t* p, const uint32_t (&cb)[BPT]) {
+  if constexpr (BPT == 2) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{cb[0], cb[1]};
+  } else {
+#pragma unroll
+    for (int q = 0; q < BPT; q += 4)
+      *reinterpret_cast<u32x4*>(p + q) = u32x4{cb[q], cb[q + 1], cb[q + 2], cb[q + 3]};
+  }
 }
 
 // Counts the row's scores into the 32-bit bucket bins (clear on entry), then
@@ -390,7 +430,7 @@ __device__ __forceinline__ void vb_histogram(const float (&x)[R], int n, float s
 
 template <int NT, int NGRP, int R>
 __device__ __forceinline__ bool vb_threshold(const float (&x)[R], int n, int k, float sc, float c,
-                             RdxSmem<NT, NGRP>& sm, VbSmem& vs, float& thr, int& rem_eq) {
+                             RdxSmem<NT, NGRP>& sm, VbSmemT<NT, NGRP>& vs, float& thr, int& rem_eq) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int nvg = rdx_live_groups<NT>(n);
@@ -401,12 +441,13 @@ __device__ __forceinline__ bool vb_threshold(const float (&x)[R], int n, int k, 
   // range holds it reads its bins again)
   {
     constexpr int BPT = kSelBins / NT;
-    static_assert(BPT == 8, "two 16-byte histogram reads per thread");
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int top = kSelBins - 1 - BPT * tid;
-    const u32x4* hp = reinterpret_cast<const u32x4*>(sm.hist + top - (BPT - 1));
-    const u32x4 a = hp[0], b = hp[1];
-    const int local = (int)(a.x + a.y + a.z + a.w + b.x + b.y + b.z + b.w);
+    uint32_t cb[BPT];
+    vb_bins<BPT>(sm.hist + top - (BPT - 1), cb);
+    int local = 0;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) local += (int)cb[q];
     const int incl = wave_incl_scan(local);
     if (lane == kWave - 1) sm.scan[0][wave] = incl;
     __syncthreads();
@@ -502,10 +543,10 @@ __device__ __forceinline__ bool vb_threshold(const float (&x)[R], int n, int k, 
 // position order when win (the callback stores without a branch per element: a loser's store
 // goes to a trash word). Returns the number of winners (k).
 template <int NT, int NGRP, int R, typename Emit>
-__device__ __forceinline__ int vb_emit(const float (&x)[R], int n, float thr, RdxSmem<NT, NGRP>& sm, VbSmem& vs,
+__device__ __forceinline__ int vb_emit(const float (&x)[R], int n, float thr, RdxSmem<NT, NGRP>& sm,
+                                       VbSmemT<NT, NGRP>& vs,
                        Emit emit) {
   constexpr int NW = NT / kWave;
-  static_assert(NGRP == kVbGroups && NT == kRowThreads, "tie flags per (group, wave)");
   const int tid = fresh_tid();
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -564,10 +605,9 @@ __device__ __forceinline__ int vb_emit(const float (&x)[R], int n, float thr, Rd
 template <int NT, int NGRP, int R>
 __device__ __forceinline__ bool vb_score_order(const float (&x)[R], int n, int k, int kk, float thr,
                                                float sc, float c, RdxSmem<NT, NGRP>& sm,
-                                               VbSmem& vs, uint64_t* words, int32_t* orow) {
+                                               VbSmemT<NT, NGRP>& vs, uint64_t* words, int32_t* orow) {
   constexpr int NW = NT / kWave;
   constexpr int BPT = kSelBins / NT;
-  static_assert(BPT == 8 && NGRP == kVbGroups && NT == kRowThreads, "layout as vb_threshold");
   const int tid = fresh_tid();
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -576,14 +616,16 @@ __device__ __forceinline__ bool vb_score_order(const float (&x)[R], int n, int k
   // top-7 .. top, top = kSelBins-1-8t, in descending order by thread)
   {
     const int top = kSelBins - 1 - BPT * tid;
-    u32x4* hp = reinterpret_cast<u32x4*>(sm.hist + top - (BPT - 1));
-    const u32x4 a = hp[0], b = hp[1];  // bins top-7..top-4, top-3..top
-    const int local = (int)(a.x + a.y + a.z + a.w + b.x + b.y + b.z + b.w);
+    uint32_t* hb = sm.hist + top - (BPT - 1);
+    uint32_t cb[BPT];  // bins top-BPT+1 .. top
+    vb_bins<BPT>(hb, cb);
+    int local = 0;
     uint32_t most = 0u;  // greatest count of a bin above b*
-    const uint32_t cb[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+    for (int q = 0; q < BPT; ++q) {
+      local += (int)cb[q];
       if (top - (BPT - 1) + q > bs) most = max(most, cb[q]);
+    }
     const int incl = wave_incl_scan(local);
     uint32_t unused = 0xFFFFFFFFu;
     wave_minmax(unused, most);
@@ -597,18 +639,15 @@ __device__ __forceinline__ bool vb_score_order(const float (&x)[R], int n, int k
       if (w < wave) excl += sm.scan[1][w];
       bmax = max(bmax, sm.red[w]);
     }
-    u32x4 hi, lo;
-    hi.w = (uint32_t)excl;
-    hi.z = hi.w + b.w;
-    hi.y = hi.z + b.z;
-    hi.x = hi.y + b.y;
-    lo.w = hi.x + b.x;
-    lo.z = lo.w + a.w;
-    lo.y = lo.z + a.z;
-    lo.x = lo.y + a.y;
+    uint32_t cur[BPT];  // bin top starts at excl, each lower one after the bins above it
+    uint32_t run = (uint32_t)excl;
+#pragma unroll
+    for (int q = BPT - 1; q >= 0; --q) {
+      cur[q] = run;
+      run += cb[q];
+    }
     if (bmax > (uint32_t)kMaxRankBucket) return false;  // block-uniform; the counts stay
-    hp[0] = lo;
-    hp[1] = hi;
+    vb_store_bins<BPT>(hb, cur);
   }
   if (tid < 3) words[kk + tid] = 0ull;  // padding read by the ranks below
   __syncthreads();  // cursors written
@@ -1041,17 +1080,141 @@ __device__ void stream_level(const float* src, int n, RdxSmem<NT, NGRP>& sm, Rdx
 
 // ---------------------------------------------------------------------------
 // Long rows, last launch: one 1024-thread workgroup per row (longest rows
-// first). Rows of at most kLongCap scores are loaded straight into registers;
-// longer ones take the candidate list of the chunk-gather launch when it fit.
-// Otherwise: the row's chunk histograms give the top digit; while the keys
+// first). VB (rows of at most kWideRowCap scores, the only launch): the row
+// is selected by value buckets as a whole, 64 scores per thread in registers;
+// rows the buckets do not settle continue below, the top digit then counted
+// over the row itself. Rows of at most kLongCap scores are loaded straight
+// into registers; longer ones take the candidate list of the chunk-gather
+// launch when it fit. Otherwise: the row's chunk histograms give the top digit; while the keys
 // at or above the digits found so far exceed kLongCap, one more digit is
 // resolved by a pass over the row; then a pass gathers those keys (for a
 // fully resolved key: the keys above it and the first `rem` equal to it) into
 // LDS in position order, and the selection finishes on them in registers.
 // Dynamic LDS: RdxSmem, then kLongCap keys and kLongCap positions (the
-// score-order words reuse the keys' area).
+// score-order words reuse the keys' area); the value buckets' scratch
+// overlays them.
 // ---------------------------------------------------------------------------
+constexpr int kWideRowCap = 65536;  // scores a 1024-thread workgroup holds in registers
+constexpr int kWideRowR = kWideRowCap / kWideThreads;
+using WideVbSmem = RdxSmem<kWideThreads, kWideRowR / 4>;
+using WideVbTies = VbSmemT<kWideThreads, kWideRowR / 4>;
+constexpr size_t kWideOffTies = (sizeof(WideVbSmem) + 15) / 16 * 16;
+constexpr size_t kWideOffWords = (kWideOffTies + sizeof(WideVbTies) + 15) / 16 * 16;
+constexpr size_t kWideVbBytes = kWideOffWords + (size_t)(kMaxK + 3) * 8;
+
+// Value-bucket selection of a row of n scores (at most kWideRowCap) by a
+// 1024-thread workgroup, its LDS at dyn: true when done, false
+// (block-uniform, LDS left dirty) when the buckets do not settle the row. The
+// threshold is found as for the shorter rows; the winners then gather in the
+// tie bitmap (each thread ORs in the bits of its scores above T, eight lanes'
+// groups to a word), and leave by one block scan over its words in position
+// order. Score order reads the winners back from the row and ranks them.
 template <int OUT>
+__device__ __forceinline__ bool wide_vb_select(const float* src, int n, int k, uint8_t* dyn,
+                                               int32_t* orow) {
+  constexpr int NT = kWideThreads, R = kWideRowR, NGRP = R / 4, NW = NT / kWave;
+  constexpr int kWords = NT * NGRP / 8;  // bitmap words: 32 positions each
+  static_assert(kWords == 2 * NT, "two bitmap words per thread");
+  WideVbSmem& sm = *reinterpret_cast<WideVbSmem*>(dyn);
+  WideVbTies& vs = *reinterpret_cast<WideVbTies*>(dyn + kWideOffTies);
+  uint64_t* words = reinterpret_cast<uint64_t*>(dyn + kWideOffWords);
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  if (OUT == kOutScore && n <= k) {  // every score wins (the packed histogram is cleared)
+    rdx_clear(sm, kSelBins / 2);
+    uint32_t wmin = 0xFFFFFFFFu, wmax = 0u;
+    for (int p = tid; p < n; p += NT) {
+      const uint32_t kv = order_key(src[p]);
+      words[p] = ((uint64_t)kv << 32) | (uint64_t)(~(uint32_t)p);
+      wmin = min(wmin, kv);
+      wmax = max(wmax, kv);
+    }
+    score_order_output<NT, NGRP>(words, n, k, wmin, wmax, sm, orow);
+    return true;
+  }
+  rdx_clear(sm, kSelBins);
+  vb_clear(vs);
+  float x[R];
+  load_row_floats<NT, R>(src, n, x);
+  {
+    float fmn, fmx;
+    sample_range<NT, R>(x, n, fmn, fmx);
+    uint32_t kmn = fmn <= fmx ? order_key(fmn) : 0xFFFFFFFFu;
+    uint32_t kmx = fmn <= fmx ? order_key(fmx) : 0u;
+    wave_minmax(kmn, kmx);
+    if (lane == 0) {
+      sm.red[wave] = kmn;
+      sm.red[NW + wave] = kmx;
+    }
+  }
+  __syncthreads();  // also orders the clears
+  uint32_t klo = sm.red[0], khi = sm.red[NW];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    klo = min(klo, sm.red[w]);
+    khi = max(khi, sm.red[NW + w]);
+  }
+  float sc = 0.0f, c = 0.0f, thr = 0.0f;
+  int rem_eq = 0;
+  if (!(vb_scale(key_to_float(klo), key_to_float(khi), sc, c) &&
+        vb_threshold<NT, NGRP, R>(x, n, k, sc, c, sm, vs, thr, rem_eq)))
+    return false;  // block-uniform
+  // the scores above T join the winning ties in the bitmap: group g's four
+  // bits go to bits 4 (g % 8) .. of word g / 8, the eight lanes of a word
+  // combined by lane exchanges
+  const int nvg = rdx_live_groups<NT>(n);
+#pragma unroll
+  for (int v = 0; v < NGRP; ++v) {
+    if (v >= nvg) continue;  // workgroup-uniform
+    const uint32_t m = (x[4 * v] > thr ? 1u : 0u) | (x[4 * v + 1] > thr ? 2u : 0u) |
+                       (x[4 * v + 2] > thr ? 4u : 0u) | (x[4 * v + 3] > thr ? 8u : 0u);
+    uint32_t w = m << (4 * (lane & 7));
+    w |= lane_xor<1>(w);
+    w |= lane_xor<2>(w);
+    w |= lane_xor<4>(w);
+    if ((lane & 7) == 0 && w != 0u) atomicOr(&vs.eqbits[(tid + NT * v) >> 3], w);
+  }
+  if (OUT == kOutScore) rdx_clear(sm, kSelBins / 2);  // for the ranks (the histogram is free)
+  __syncthreads();
+  // winners in position order: words 2 tid, 2 tid + 1, slots from a block scan
+  const u32x2 bw = *reinterpret_cast<const u32x2*>(vs.eqbits + 2 * tid);
+  const int cnt = __popc(bw[0]) + __popc(bw[1]);
+  const int incl = wave_incl_scan(cnt);
+  if (lane == kWave - 1) sm.scan[0][wave] = incl;
+  __syncthreads();
+  int slot = incl - cnt;
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+    if (w < wave) slot += sm.scan[0][w];
+  uint32_t wmax = 0u;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    uint32_t bits = bw[j];
+    while (bits != 0u) {
+      const int p = 32 * (2 * tid + j) + __ffs((int)bits) - 1;
+      bits &= bits - 1u;
+      if (OUT == kOutPos) {
+        reinterpret_cast<int*>(sm.hist)[slot] = p;
+      } else {
+        const uint32_t kv = order_key(src[p]);
+        words[slot] = ((uint64_t)kv << 32) | (uint64_t)(~(uint32_t)p);
+        wmax = max(wmax, kv);
+      }
+      ++slot;
+    }
+  }
+  if (OUT == kOutPos) {
+    __syncthreads();
+    store_row_positions<NT>(reinterpret_cast<const int*>(sm.hist), k, k, orow);
+  } else {
+    // the least winner is T
+    score_order_output<NT, NGRP>(words, k, k, order_key(thr), wmax, sm, orow);
+  }
+  return true;
+}
+
+template <int OUT, bool VB>
 __global__ __launch_bounds__(kWideThreads)
 void topk_long_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, int q_pos0, int k,
                       int nch, const uint32_t* __restrict__ ghist,
@@ -1077,6 +1240,10 @@ void topk_long_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, i
     for (int j = tid; j < k; j += NT) orow[j] = j < n ? j : -1;
     return;
   }
+  if constexpr (VB) {
+    if (wide_vb_select<OUT>(src, n, k, dyn, orow)) return;  // block-uniform
+    __syncthreads();  // the buckets' scratch is free
+  }
   uint32_t key[R], pos[R], kmin, kmax;
   int m;  // elements held in registers
   if (n <= kLongCap) {
@@ -1085,7 +1252,7 @@ void topk_long_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, i
 #pragma unroll
     for (int r = 0; r < R; ++r) pos[r] = (uint32_t)elem_of<NT>(r);
     m = n;
-  } else if (lcnt[row] >= 0) {
+  } else if (!VB && lcnt[row] >= 0) {
     // the row's candidate list from the previous launch (position-ordered,
     // a superset of the top-k holding every key equal to its least member)
     m = lcnt[row];
@@ -1102,11 +1269,18 @@ void topk_long_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, i
     }
   } else {
     // level 0 (the top 11 bits) from the chunk histograms, as 32-bit sums
+    // (VB: counted over the row)
     RdxState st = rdx_start(n, k, 0u, 0xFFFFFFFFu);
-    const int nc = (n + kTopkChunk - 1) / kTopkChunk;
     static_assert(kHistWords == NT, "one histogram word per thread");
-    {
+    int par = 0, cnt;
+    if constexpr (VB) {
+      rdx_clear(sm, kSelBins);
+      __syncthreads();
+      stream_level<NT, NGRP>(src, n, sm, st, par);
+      cnt = sm.bc[par][2];
+    } else {
       // the chunks' words, kSumBatch loads in flight per thread
+      const int nc = (n + kTopkChunk - 1) / kTopkChunk;
       constexpr int kSumBatch = 8;
       const uint32_t* gw = ghist + row * nch * kHistWords + tid;
       uint32_t lo = 0u, hi = 0u;
@@ -1123,10 +1297,9 @@ void topk_long_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, i
       }
       sm.hist[2 * tid] = lo;
       sm.hist[2 * tid + 1] = hi;
+      __syncthreads();
+      cnt = rdx_resolve<NT, NGRP, false>(sm, st, par);
     }
-    __syncthreads();
-    int par = 0;
-    int cnt = rdx_resolve<NT, NGRP, false>(sm, st, par);
     // refine over the row while the keys at or above the digits found do
     // not fit in LDS
     while (!st.done && st.level < 3 && (k - st.rem) + cnt > kLongCap) {
@@ -1371,23 +1544,22 @@ int* topk_lcnt(const TopkArgs& a, int nch) {
   return reinterpret_cast<int*>(topk_lcand(a, nch) + (size_t)a.rows * kLongCap);
 }
 
-size_t long_lds_bytes() {
-  constexpr size_t off =
-      (sizeof(RdxSmem<kWideThreads, kWideR / 4>) + 15) / 16 * 16;
-  return off + (size_t)kLongCap * 8;
-}
+constexpr size_t kLongLdsBytes =
+    (sizeof(RdxSmem<kWideThreads, kWideR / 4>) + 15) / 16 * 16 + (size_t)kLongCap * 8;
+static_assert(kWideVbBytes <= kLongLdsBytes, "the value buckets' scratch overlays the long rows'");
 
-template <int OUT>
+// VB: rows of at most kWideRowCap scores in this launch alone (no scratch).
+template <int OUT, bool VB>
 hipError_t launch_long(const TopkArgs& a, int nch, hipStream_t st) {
-  const size_t shmem = long_lds_bytes();
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_long_kernel<OUT>),
+  const size_t shmem = kLongLdsBytes;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_long_kernel<OUT, VB>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
   if (e != hipSuccess) return e;
   const int B = a.rows / a.Lq;
-  hipLaunchKernelGGL((topk_long_kernel<OUT>), dim3((unsigned)a.rows), dim3(kWideThreads), shmem,
-                     st, a.scores, B, a.Lq, a.Lk, a.q_pos0, a.k, nch,
-                     reinterpret_cast<const uint32_t*>(a.ghist), topk_lcand(a, nch),
-                     topk_lcnt(a, nch), a.out);
+  hipLaunchKernelGGL((topk_long_kernel<OUT, VB>), dim3((unsigned)a.rows), dim3(kWideThreads),
+                     shmem, st, a.scores, B, a.Lq, a.Lk, a.q_pos0, a.k, nch,
+                     VB ? nullptr : reinterpret_cast<const uint32_t*>(a.ghist),
+                     VB ? nullptr : topk_lcand(a, nch), VB ? nullptr : topk_lcnt(a, nch), a.out);
   return hipGetLastError();
 }
 
@@ -1398,7 +1570,7 @@ int topk_row_chunks(int Lk) { return (Lk + kTopkChunk - 1) / kTopkChunk; }
 size_t topk_part_bytes(int rows, int Lk, int k) {
   (void)k;
   const int nch = topk_row_chunks(Lk);
-  if (nch <= 1) return 0;
+  if (nch <= 1 || Lk <= kWideRowCap) return 0;  // one launch, no scratch
   size_t b = hist_bytes(rows, nch);
   if (Lk > kLongCap) b += (size_t)rows * kLongCap * 8 + (size_t)rows * 4;
   return b;
@@ -1457,7 +1629,11 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
                          dim3(kRowThreads), 0, st, a.scores, B, a.Lq, a.Lk, a.q_pos0, a.k, a.out);
     return hipGetLastError();
   }
-  // long rows: per-chunk histograms of the top digit, then one workgroup per row
+  // rows of up to kWideRowCap scores: one 1024-thread workgroup per row
+  if (a.Lk <= kWideRowCap)
+    return a.pos_order ? launch_long<kOutPos, true>(a, nch, st)
+                       : launch_long<kOutScore, true>(a, nch, st);
+  // longer rows: per-chunk histograms of the top digit, then one workgroup per row
   hipLaunchKernelGGL(topk_chunk_hist_kernel, dim3((unsigned)((size_t)a.rows * nch)),
                      dim3(kRowThreads), 0, st, a.scores, a.Lq, a.Lk, a.q_pos0, nch,
                      reinterpret_cast<uint32_t*>(a.ghist));
@@ -1473,7 +1649,8 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return a.pos_order ? launch_long<kOutPos>(a, nch, st) : launch_long<kOutScore>(a, nch, st);
+  return a.pos_order ? launch_long<kOutPos, false>(a, nch, st)
+                     : launch_long<kOutScore, false>(a, nch, st);
 }
 
 }  // namespace idxc

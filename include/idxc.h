@@ -128,17 +128,16 @@ enum { IDXC_ORDER_SCORE = 0, IDXC_ORDER_POSITION = 1 };
  * reads scores[b,i,0..t] only (t = q_pos0 + i) and writes indices[b,i,0..k-1]:
  * the min(k, t+1) best positions in the given order (IDXC_ORDER_*, anything
  * else is IDXC_ERR_INVALID_ARG), then -1. Uses B, Lq, Lk, q_pos0, k.
- * Bit-exact and deterministic. Rows longer than 8192 scores are selected
- * in two launches (three past 16384 scores) through a device workspace of
- * at least idxc_topk_workspace_bytes() bytes (per-chunk histograms and, past
- * 16384 scores, a per-row candidate list; NULL/0 is fine when that is 0);
+ * Bit-exact and deterministic. With Lk <= 65536 this is one launch and
+ * needs no workspace; longer rows are selected in three launches through a
+ * device workspace of at least idxc_topk_workspace_bytes() bytes (per-chunk
+ * histograms and a per-row candidate list; NULL/0 is fine when that is 0);
  * any Lk up to 2^24 is supported. */
 int idxc_topk(const float* scores, const idxc_dims* dims, int32_t order, void* workspace,
               size_t workspace_bytes, int32_t* indices, void* hip_stream);
 
-/* Workspace bytes idxc_topk needs for these sizes: 0 when Lk <= 8192, else
- * B * Lq * ceil(Lk / 8192) * 4096, plus B * Lq * (16384 * 8 + 4) when
- * Lk > 16384. Host-only. */
+/* Workspace bytes idxc_topk needs for these sizes: 0 when Lk <= 65536, else
+ * B * Lq * (ceil(Lk / 8192) * 4096 + 16384 * 8 + 4). Host-only. */
 int idxc_topk_workspace_bytes(const idxc_dims* dims, size_t* bytes);
 
 /* Bytes of device workspace for these sizes (written to *bytes), host-only:

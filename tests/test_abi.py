@@ -103,22 +103,24 @@ def test_topk_argument_errors(lib):
     for bad in (-1, 2, 7):
         assert f(P(), ctypes.byref(_dims()), None, 0, P(), None, bad) == _lib.IDXC_ERR_INVALID_ARG
         assert "order" in lib.idxc_last_error().decode()
-    # long rows need the two-stage workspace; too long rows are unsupported
-    long_rows = _dims(Lq=1, Lk=65536, q_pos0=65535, k=2048)
+    # rows of up to 65536 scores take one launch and no workspace; longer
+    # ones need the chunked selection's
     n = ctypes.c_size_t(0)
+    for Lk in (8193, 16384, 65536):
+        fits = _dims(Lq=1, Lk=Lk, q_pos0=Lk - 1, k=2048)
+        assert lib.idxc_topk_workspace_bytes(ctypes.byref(fits), ctypes.byref(n)) == 0
+        assert n.value == 0
+    long_rows = _dims(Lq=1, Lk=65537, q_pos0=65536, k=2048)
     assert lib.idxc_topk_workspace_bytes(ctypes.byref(long_rows), ctypes.byref(n)) == 0
-    # one 2048-bin histogram of 16-bit counts per 8192-score chunk, and for
-    # rows past 16384 scores a list of 16384 (key, position) pairs and a count
-    assert n.value == 8 * 4096 + 16384 * 8 + 4
+    # one 2048-bin histogram of 16-bit counts per 8192-score chunk, and a
+    # list of 16384 (key, position) pairs and a count per row
+    assert n.value == 9 * 4096 + 16384 * 8 + 4
     assert f(P(), ctypes.byref(long_rows), None, 0, P(), None) == _lib.IDXC_ERR_INVALID_ARG
     assert f(P(), ctypes.byref(long_rows), P(), n.value - 1, P(), None) == _lib.IDXC_ERR_INVALID_ARG
     # rows of any length up to Lk = 2^24 are supported given the workspace
     longest = _dims(B=2, Lq=3, Lk=1 << 24, q_pos0=(1 << 24) - 3, k=2048)
     assert lib.idxc_topk_workspace_bytes(ctypes.byref(longest), ctypes.byref(n)) == 0
     assert n.value == 6 * 2048 * 4096 + 6 * (16384 * 8 + 4)
-    two_chunks = _dims(Lq=1, Lk=16384, q_pos0=16383, k=2048)
-    assert lib.idxc_topk_workspace_bytes(ctypes.byref(two_chunks), ctypes.byref(n)) == 0
-    assert n.value == 2 * 4096
     assert f(P(), ctypes.byref(longest), P(), n.value - 16, P(), None) == _lib.IDXC_ERR_INVALID_ARG
     short = _dims(Lq=1, Lk=8192, q_pos0=8191, k=2048)
     assert lib.idxc_topk_workspace_bytes(ctypes.byref(short), ctypes.byref(n)) == 0

@@ -1112,15 +1112,19 @@ def test_topk_random_shapes_exact(seed):
         assert np.array_equal(got.cpu().numpy(), exp)
 
 
-def _bucket_edge_rows(case, Lk, seed=21):
+def _bucket_edge_rows(case, Lk, seed=21, n=None):
     """Score rows whose k-th best score sits where the value-bucket selection
     of materialised rows has its edges: in the top bucket, made of scores
     above the sampled range (positions away from each thread's first and last
-    groups), in the bottom bucket below it, and tied with other scores of its
-    bucket."""
+    groups: 256 threads of four-score groups for rows of up to 8192 scores,
+    1024 threads past that), in the bottom bucket below it, and tied with
+    other scores of its bucket. The edits fall in the first n scores."""
     rng = np.random.default_rng(seed)
     s = rng.standard_normal(Lk).astype(np.float32)
-    mid = np.arange(1200, min(Lk, 6000))
+    n = Lk if n is None else n
+    mid = np.arange(1200, min(n, 6000)) if Lk <= 8192 else np.arange(5000, min(n, 20000))
+    if mid.size < 60:
+        mid = np.arange(1200, n)
     if case == "top":  # 30 scores far above the rest, with ties, k below 30
         s[mid[:30]] = np.float32(50.0) + rng.integers(0, 4, 30).astype(np.float32)
     elif case == "bottom":  # 60 scores far below the rest, with ties, n just above k
@@ -1146,6 +1150,26 @@ def test_topk_value_bucket_edges_exact(case, Lk, k):
     want = oracle.topk(s.numpy(), k, q0)
     for order in ("score", "position"):
         got = idxc.idxc_topk(cu(s), k, q_pos0=q0, order=order)
+        torch.cuda.synchronize()
+        exp = want if order == "score" else oracle.position_order(want)
+        assert np.array_equal(got.cpu().numpy(), exp)
+
+
+@pytest.mark.parametrize("case,Lk,n,k", [
+    ("top", 40000, 40000, 16), ("top", 65536, 65536, 30),
+    ("bottom", 20000, 2100, 2048),
+    ("tied", 65536, 65536, 2048), ("tied", 40000, 30000, 1500),
+    ("outliers", 65536, 65536, 2048),  # buckets fail: the top digit counted over the row
+    ("outliers", 20000, 12000, 2048),  # buckets fail on a row the digit search holds whole
+])
+def test_topk_value_bucket_edges_wide_rows_exact(case, Lk, n, k):
+    """The same edges in rows of up to 65536 scores (one 1024-thread
+    workgroup per row), a row of n scores out of Lk."""
+    _say("topk bucket edges wide %s Lk=%d n=%d k=%d" % (case, Lk, n, k))
+    s = _bucket_edge_rows(case, Lk, n=n)
+    want = oracle.topk(s.numpy(), k, n - 1)
+    for order in ("score", "position"):
+        got = idxc.idxc_topk(cu(s), k, q_pos0=n - 1, order=order)
         torch.cuda.synchronize()
         exp = want if order == "score" else oracle.position_order(want)
         assert np.array_equal(got.cpu().numpy(), exp)
