@@ -1100,7 +1100,8 @@ using WideVbSmem = RdxSmem<kWideThreads, kWideRowR / 4>;
 using WideVbTies = VbSmemT<kWideThreads, kWideRowR / 4>;
 constexpr size_t kWideOffTies = (sizeof(WideVbSmem) + 15) / 16 * 16;
 constexpr size_t kWideOffWords = (kWideOffTies + sizeof(WideVbTies) + 15) / 16 * 16;
-constexpr size_t kWideVbBytes = kWideOffWords + (size_t)(kMaxK + 3) * 8;
+constexpr size_t kWideOffPos = kWideOffWords + (size_t)(kMaxK + 3 + 1) / 2 * 16;
+constexpr size_t kWideVbBytes = kWideOffPos + (size_t)kMaxK * 4;
 
 // Value-bucket selection of a row of n scores (at most kWideRowCap) by a
 // 1024-thread workgroup, its LDS at dyn: true when done, false
@@ -1108,7 +1109,8 @@ constexpr size_t kWideVbBytes = kWideOffWords + (size_t)(kMaxK + 3) * 8;
 // threshold is found as for the shorter rows; the winners then gather in the
 // tie bitmap (each thread ORs in the bits of its scores above T, eight lanes'
 // groups to a word), and leave by one block scan over its words in position
-// order. Score order reads the winners back from the row and ranks them.
+// order. Score order then reads the winners' scores back from the row (two
+// per thread, both loads in flight) and ranks them.
 template <int OUT>
 __device__ __forceinline__ bool wide_vb_select(const float* src, int n, int k, uint8_t* dyn,
                                                int32_t* orow) {
@@ -1187,27 +1189,41 @@ __device__ __forceinline__ bool wide_vb_select(const float* src, int n, int k, u
 #pragma unroll
   for (int w = 0; w < NW; ++w)
     if (w < wave) slot += sm.scan[0][w];
-  uint32_t wmax = 0u;
+  // positions by slot: over the histogram (position order) or in an area of
+  // their own (score order, whose ranks need the histogram clear)
+  int* pbuf = OUT == kOutPos ? reinterpret_cast<int*>(sm.hist)
+                             : reinterpret_cast<int*>(dyn + kWideOffPos);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     uint32_t bits = bw[j];
     while (bits != 0u) {
-      const int p = 32 * (2 * tid + j) + __ffs((int)bits) - 1;
+      pbuf[slot++] = 32 * (2 * tid + j) + __ffs((int)bits) - 1;
       bits &= bits - 1u;
-      if (OUT == kOutPos) {
-        reinterpret_cast<int*>(sm.hist)[slot] = p;
-      } else {
-        const uint32_t kv = order_key(src[p]);
-        words[slot] = ((uint64_t)kv << 32) | (uint64_t)(~(uint32_t)p);
-        wmax = max(wmax, kv);
-      }
-      ++slot;
     }
   }
+  __syncthreads();
   if (OUT == kOutPos) {
-    __syncthreads();
-    store_row_positions<NT>(reinterpret_cast<const int*>(sm.hist), k, k, orow);
+    store_row_positions<NT>(pbuf, k, k, orow);
   } else {
+    constexpr int EPT = (kMaxK + NT - 1) / NT;
+    int pv[EPT];
+    float sv[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int i = tid + e * NT;
+      pv[e] = i < k ? pbuf[i] : 0;
+      sv[e] = i < k ? src[pv[e]] : 0.0f;
+    }
+    uint32_t wmax = 0u;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int i = tid + e * NT;
+      if (i < k) {
+        const uint32_t kv = order_key(sv[e]);
+        words[i] = ((uint64_t)kv << 32) | (uint64_t)(~(uint32_t)pv[e]);
+        wmax = max(wmax, kv);
+      }
+    }
     // the least winner is T
     score_order_output<NT, NGRP>(words, k, k, order_key(thr), wmax, sm, orow);
   }
