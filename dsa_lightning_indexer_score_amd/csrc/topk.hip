@@ -590,6 +590,68 @@ __device__ __forceinline__ int vb_emit(const float (&x)[R], int n, float thr, Rd
   return base;
 }
 
+// Position-ordered winners after vb_threshold through the tie bitmap: each
+// thread ORs in the bits of its scores above T (group g's four bits at bits
+// 4 (g % 8) .. of word g / 8, the eight lanes of a word combined by lane
+// exchanges), then one block scan over the bitmap's words (one or two per
+// thread) gives every winner its slot: pbuf[slot] = its position. Returns
+// the number of winners; a barrier must come before pbuf is read.
+template <int NT, int NGRP, int R>
+__device__ __forceinline__ int vb_bitmap_emit(const float (&x)[R], int n, float thr,
+                                              RdxSmem<NT, NGRP>& sm, VbSmemT<NT, NGRP>& vs,
+                                              int* pbuf) {
+  constexpr int NW = NT / kWave;
+  constexpr int kWords = NT * NGRP / 8;
+  constexpr int WPT = kWords / NT;
+  static_assert(WPT * NT == kWords && (WPT == 1 || WPT == 2), "whole bitmap words per thread");
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  const int nvg = rdx_live_groups<NT>(n);
+#pragma unroll
+  for (int v = 0; v < NGRP; ++v) {
+    if (v >= nvg) continue;  // workgroup-uniform
+    const uint32_t m = (x[4 * v] > thr ? 1u : 0u) | (x[4 * v + 1] > thr ? 2u : 0u) |
+                       (x[4 * v + 2] > thr ? 4u : 0u) | (x[4 * v + 3] > thr ? 8u : 0u);
+    uint32_t w = m << (4 * (lane & 7));
+    w |= lane_xor<1>(w);
+    w |= lane_xor<2>(w);
+    w |= lane_xor<4>(w);
+    if ((lane & 7) == 0 && w != 0u) atomicOr(&vs.eqbits[(tid + NT * v) >> 3], w);
+  }
+  __syncthreads();
+  uint32_t bw[WPT];
+  if constexpr (WPT == 2) {
+    const u32x2 b2 = *reinterpret_cast<const u32x2*>(vs.eqbits + 2 * tid);
+    bw[0] = b2[0];
+    bw[1] = b2[1];
+  } else {
+    bw[0] = vs.eqbits[tid];
+  }
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) cnt += __popc(bw[j]);
+  const int incl = wave_incl_scan(cnt);
+  if (lane == kWave - 1) sm.scan[0][wave] = incl;
+  __syncthreads();
+  int slot = incl - cnt, total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int y = sm.scan[0][w];
+    if (w < wave) slot += y;
+    total += y;
+  }
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    uint32_t bits = bw[j];
+    while (bits != 0u) {
+      pbuf[slot++] = 32 * (WPT * tid + j) + __ffs((int)bits) - 1;
+      bits &= bits - 1u;
+    }
+  }
+  return total;
+}
+
 // Score order after vb_threshold, from the row's own bucket counts (still in
 // the histogram): buckets above b* hold winners only, so a winner's rank is
 // the number of scores in higher buckets plus the larger (key, ~position)
@@ -799,11 +861,11 @@ __device__ __forceinline__ void score_order_output(uint64_t* words, int kk, int 
 // row, longest rows first. Row r = b*Lq + i holds candidates 0..t, t =
 // q_pos0 + i (never more than Lk).
 // ---------------------------------------------------------------------------
-// (position order runs seven waves per SIMD in 72 registers: 46 vs 48 us at
-// six, its few spills outside the value-bucket path; score order runs at
-// five: six measured 119 vs 89 us)
+// (position order runs eight waves per SIMD in 64 registers: 41 us, against
+// 43 us at seven, its few spills outside the value-bucket path; score order
+// runs at five: six measured 119 vs 89 us)
 template <int OUT>
-__global__ __launch_bounds__(kRowThreads, OUT == kOutPos ? 7 : 5)
+__global__ __launch_bounds__(kRowThreads, OUT == kOutPos ? 8 : 5)
 void topk_rows_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, int q_pos0, int k,
                       int32_t* __restrict__ out) {
   constexpr int NT = kRowThreads, R = kRowR, NGRP = R / 4;
@@ -855,9 +917,7 @@ void topk_rows_kernel(const float* __restrict__ scores, int B, int Lq, int Lk, i
       // read after vb_emit's barrier), then leave in 16-byte stores
       static_assert(kSelBins >= kMaxK, "positions staged over the histogram");
       int* obuf = reinterpret_cast<int*>(sm.hist);
-      const int kk = vb_emit<NT, NGRP, R>(x, n, thr, sm, vs, [&](bool win, int slot, int, int p) {
-        *(win ? obuf + slot : vs.trash + lane) = p;
-      });
+      const int kk = vb_bitmap_emit<NT, NGRP, R>(x, n, thr, sm, vs, obuf);
       __syncthreads();
       store_row_positions<NT>(obuf, kk, k, orow);
     } else {
